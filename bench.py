@@ -1,0 +1,213 @@
+"""Benchmark of the SageSLA attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: pooling +
+Q quantization, head stats, block selection, K/V quantization + linear states, linear
+totals, linear complement (+ W_proj), and the block-sparse INT8/FP8 attention with the
+fused epilogue. The timed region issues the library's stage entry points in the same
+order as sagesla_fwd (the output is checked identical to sagesla_fwd), with HIP events
+on the launch stream between the stages, so that every kernel's average duration is
+measured live.
+
+Prints one JSON line. Default workload: the Wan2.1-14B-720P attention layer shape
+(B=1, H=40, N=75600, d=128, topk=0.1).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+PEAK_INT8_FP8_TOPS = 5000.0  # MI355X dense INT8 / FP8 MFMA peak, TOP/s
+PEAK_HBM_GBS = 8000.0
+STAGES = ["pool", "head_stats", "select", "quant_kv", "linear_total", "linear_complement", "sparse_attn"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="wan14b-720p")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=12, help="query blocks in the oracle sample")
+    return ap.parse_args()
+
+
+def src_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the SageSLA forward here has no multi-GPU path "
+              "(heads would shard across GPUs with no exchange; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import sparse_attention_sagesla_amd as S
+    from sparse_attention_sagesla_amd import synth
+
+    cfg = synth.CONFIGS[args.config]
+    B, H, N, d, topk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.topk
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = synth.make_inputs(cfg, device=dev)
+    q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
+    linear = proj is not None
+    Nb = (N + 63) // 64
+    ks = S.ksel(N, topk)
+    use_lin = linear and ks < Nb
+    ws = S.alloc_workspace(q, topk, linear)
+    out = torch.empty_like(q)
+    lay = S.workspace_layout(B, H, N, topk=topk, linear=linear)
+    P = {n: ws.data_ptr() + o for n, o in lay.items()}
+    L = S.lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def ck(st, what):
+        if st != 0:
+            raise RuntimeError("%s failed: %s" % (what, S.status_string(st)))
+
+    def stage_calls():
+        return [
+            ("pool", lambda: L.sagesla_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, 64, P["qbar"],
+                                            P["kbart"], P["ksum"], P["vamax_blk"], P["q8"], P["sq"], sp)),
+            ("head_stats", lambda: L.sagesla_head_stats(P["ksum"], P["vamax_blk"], B, H, N, d, 64, P["kmean"],
+                                                        P["vamax"], sp)),
+            ("select", lambda: L.sagesla_select(P["qbar"], P["kbart"], B, H, N, d, 64, topk, P["idx"], sp)),
+            ("quant_kv", lambda: L.sagesla_quant_kv(
+                k.data_ptr(), v.data_ptr(), P["kmean"], P["vamax"], B, H, N, d, 64, P["k8"], P["sk"], P["v8"],
+                P["hs"] if use_lin else None, P["zs"] if use_lin else None, P["hpart"] if use_lin else None,
+                P["zpart"] if use_lin else None, sp)),
+        ] + ([
+            ("linear_total", lambda: L.sagesla_linear_total(P["hpart"], P["zpart"], B, H, N, d, 64, P["htot"],
+                                                            P["ztot"], sp)),
+            ("linear_complement", lambda: L.sagesla_linear_complement(
+                q.data_ptr(), P["idx"], P["hs"], P["zs"], P["htot"], P["ztot"], proj.data_ptr(), B, H, N, d, 64,
+                topk, P["y"], sp)),
+        ] if use_lin else []) + [
+            ("sparse_attn", lambda: L.sagesla_sparse_attn(
+                P["q8"], P["sq"], P["k8"], P["sk"], P["v8"], P["vamax"], P["idx"], P["y"] if use_lin else None,
+                B, H, N, d, 64, topk, out.data_ptr(), sp)),
+        ]
+
+    calls = stage_calls()
+    names = [n for n, _ in calls]
+    for _ in range(args.warmup):
+        S.fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, events between stages on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for c, (name, fn) in enumerate(calls):
+            ck(fn(), name)
+            ev[s][c + 1].record(stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+    per_kernel = {n: sum(ev[s][c].elapsed_time(ev[s][c + 1]) for s in range(args.steps)) / args.steps
+                  for c, n in enumerate(names)}
+
+    # the staged pass computes exactly what sagesla_fwd computes
+    staged = out.clone()
+    ref = S.fwd(q, k, v, proj, topk=topk)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(staged, ref))
+
+    # executed MFMA work from the actual selection: sum over kept pairs of 4 * n_i * n_j * d
+    idx = S.workspace_views(ws, B, H, N, topk=topk, linear=linear)["idx"].long()
+    nlen = torch.full((Nb,), 64, dtype=torch.int64, device=dev)
+    nlen[-1] = N - 64 * (Nb - 1)
+    pair_tok = (nlen[idx].sum(-1) * nlen[None, :]).sum().item()
+    exec_ops = 4.0 * d * pair_tok
+    dense_flops = 4.0 * B * H * N * N * d
+    sa_ms = per_kernel["sparse_attn"]
+    achieved = exec_ops / (sa_ms * 1e-3) / 1e12
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "sparse_attn_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            kpath = os.path.join(ROOT, "sparse_attention_sagesla_amd", "csrc", "sparse_attn.hip")
+            if tj.get("source_sha256_16") == src_hash(kpath) and tj.get("workload") == args.config:
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "SageSLA fwd ms/call + dense-equiv TFLOPS & MFMA % peak, Wan-14B-720P shape",
+        "value": round(ms_step, 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8e4m3 (MFMA), fp32 softmax",
+        "data": "synthetic (seeded generator with the layer's shape; no model weights)",
+        "config": {"workload": "%s: B=%d H=%d N=%d d=%d topk=%g block=64%s" % (
+            cfg.name, B, H, N, d, topk, "" if linear else " linear-branch off"),
+            "ksel": ks, "num_blocks": Nb, "seed": cfg.seed},
+        "dense_equiv_tflops": round(dense_flops / (ms_step * 1e-3) / 1e12, 2),
+        "executed_tops_whole_call": round(exec_ops / (ms_step * 1e-3) / 1e12, 2),
+        "sparse_attn_executed_tops": round(achieved, 2),
+        "sparse_attn_frac_of_mfma_peak": round(achieved / PEAK_INT8_FP8_TOPS, 4),
+        "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
+        "staged_equals_fwd": same,
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_FP8_TOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_FP8_TOPS, 4), "traffic": traffic,
+                     "kernel": "sparse_attn_kernel", "work_per_launch_ops": exec_ops},
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, x, nblocks):
+    """The oracle, as it is, on one head: once with no query blocks (the per-head part:
+    pooling, quantization, linear states) and once with `nblocks` query blocks; the call
+    time is extrapolated to all heads and blocks (heads and blocks are independent)."""
+    import oracle as O
+    from sparse_attention_sagesla_amd import synth
+    q, k, v = (synth.bf16_bits(x[n][0, 0]) for n in ("q", "k", "v"))
+    w = synth.bf16_bits(x["proj"]) if x["proj"] is not None else None
+    Nb = (cfg.N + 63) // 64
+    t0 = time.perf_counter()
+    O.sagesla_head(q, k, v, w, cfg.topk, qblocks=[])
+    t_head = time.perf_counter() - t0
+    blocks = list(range(0, Nb, max(1, Nb // nblocks)))[:nblocks]
+    t0 = time.perf_counter()
+    O.sagesla_head(q, k, v, w, cfg.topk, qblocks=blocks)
+    t_blk = max(0.0, (time.perf_counter() - t0 - t_head) / len(blocks))
+    est_ms = (cfg.B * cfg.H) * (t_head + Nb * t_blk) * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+            "sample": "one head of %s: per-head part %.2f s, %d of %d query blocks at %.3f s each; "
+                      "extrapolated to %d heads x %d blocks, single thread" % (
+                          cfg.name, t_head, len(blocks), Nb, t_blk, cfg.B * cfg.H, Nb),
+            "measured_s": round(t_head * 2 + t_blk * len(blocks), 2)}
+
+
+if __name__ == "__main__":
+    main()

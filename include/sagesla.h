@@ -1,0 +1,161 @@
+/*
+ * sagesla.h — C ABI of the SageSLA attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * SageSLA is sparse-linear attention (SLA) combined with SageAttention's low-bit
+ * quantization, swapped in for trained SLA at inference time (TurboDiffusion explainer,
+ * news.qq.com, sections "First key: attention" and "From training to deployment").
+ * SLA scores how strongly pairs of positions are related, computes only the top
+ * fraction exactly (Top-K ratio 0.1; 0.1-0.15 recommended) and hands the rest to a
+ * linear-attention branch; SageAttention runs the exact part on 8-bit data (same page;
+ * bonega.ai blog, SLA paragraph; tiemojia.cn article, sections 2.2.1-2.2.2).
+ *
+ * The pages give no formulas. This library computes, per (batch, head):
+ *   1. pooling + selection: mean-pool Q and K over 64-token blocks, score block pairs
+ *      s_ij = Qbar_i . Kbar_j / sqrt(d), keep the ksel = ceil(topk * Nb) best key blocks
+ *      of every query block (ties: lower index), stored ascending;
+ *   2. quantization: K smoothed by its per-channel mean over all tokens; Q and K to INT8
+ *      per 64-token block (scale amax/127, round half to even); V to FP8 e4m3 per
+ *      channel (scale amax/448);
+ *   3. sparse attention over the kept blocks: INT8 QK^T, online softmax in fp32,
+ *      probabilities as e4m3(p*448), FP8 PV;
+ *   4. linear branch over the other blocks: phi = softmax over the d channels,
+ *      per-key-block states H_j = phi(K_j)^T V_j and z_j = colsum phi(K_j), the
+ *      complement total minus kept, O_l = phi(q) H^c / (phi(q) . z^c);
+ *   5. output O = O_s + O_l W_proj (bf16).
+ *
+ * Conventions (all entry points):
+ *  - Tensors are device pointers to contiguous row-major data. q, k, v, out are bf16
+ *    [B, H, N, d]; proj is bf16 [d, d] applied as (row vector) x W.
+ *  - This version supports d = 128 and block = 64 only (others: SAGESLA_ERR_UNSUPPORTED),
+ *    1 <= N <= 1048576, B*H*ceil(N/64) < 2^31, 0 < topk <= 1.
+ *  - Every pointer must be 16-byte aligned. The caller owns all memory; the library
+ *    allocates nothing and keeps no state other than a per-device architecture check.
+ *  - Arguments are validated on the host before anything is enqueued; on any error
+ *    nothing is launched and the status says why. Launch failures return
+ *    SAGESLA_ERR_HIP. Faults inside kernels surface at the caller's next synchronize.
+ *  - All work is enqueued on `stream` (0 = the null stream); calls never synchronize.
+ *    Inputs must stay alive until the stream has passed the call.
+ *  - Calls on different streams with different workspaces may run concurrently.
+ */
+#ifndef SAGESLA_H
+#define SAGESLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *sagesla_stream_t; /* a hipStream_t */
+
+typedef enum {
+    SAGESLA_OK = 0,
+    SAGESLA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or ratio */
+    SAGESLA_ERR_UNSUPPORTED = 2,      /* d != 128, block != 64, or not a gfx950 device */
+    SAGESLA_ERR_WORKSPACE = 3,        /* workspace smaller than sagesla_workspace_size */
+    SAGESLA_ERR_HIP = 4               /* a HIP runtime call or kernel launch failed */
+} sagesla_status;
+
+/* Workspace regions (indices into the offsets array of sagesla_workspace_layout). */
+enum {
+    SAGESLA_WS_QBAR = 0,  /* fp64 [BH][Nb][d]   block means of Q                          */
+    SAGESLA_WS_KBART,     /* fp64 [BH][d][Nb]   block means of K, channel-major            */
+    SAGESLA_WS_KSUM,      /* fp64 [BH][Nb][d]   block column sums of K                     */
+    SAGESLA_WS_VAMAXB,    /* fp32 [BH][Nb][d]   block column max |V|                       */
+    SAGESLA_WS_KMEAN,     /* fp32 [BH][d]       per-channel mean of K over all N           */
+    SAGESLA_WS_VAMAX,     /* fp32 [BH][d]       per-channel max |V| over all N             */
+    SAGESLA_WS_Q8,        /* int8 [BH][Nb][8192] Q codes, MFMA operand order (see below)   */
+    SAGESLA_WS_SQ,        /* fp32 [BH][Nb]      Q block scales                             */
+    SAGESLA_WS_K8,        /* int8 [BH][Nb][8192] smoothed-K codes, MFMA operand order      */
+    SAGESLA_WS_SK,        /* fp32 [BH][Nb]      K block scales                             */
+    SAGESLA_WS_V8,        /* e4m3 [BH][Nb][8192] V codes, MFMA operand order               */
+    SAGESLA_WS_IDX,       /* int32 [BH][Nb][ksel] kept key blocks, ascending               */
+    SAGESLA_WS_HS,        /* fp32 [BH][Nb][d][d] H_j = phi(K_j)^T V_j       (linear only)  */
+    SAGESLA_WS_ZS,        /* fp32 [BH][Nb][d]    z_j = colsum phi(K_j)      (linear only)  */
+    SAGESLA_WS_HPART,     /* fp32 [BH][Nc][d][d] sums of 16 consecutive H_j (linear only)  */
+    SAGESLA_WS_ZPART,     /* fp32 [BH][Nc][d]    sums of 16 consecutive z_j (linear only)  */
+    SAGESLA_WS_HTOT,      /* fp32 [BH][d][d]     sum of all H_j             (linear only)  */
+    SAGESLA_WS_ZTOT,      /* fp32 [BH][d]        sum of all z_j             (linear only)  */
+    SAGESLA_WS_Y,         /* fp32 [BH][N][d]     O_l W_proj                 (linear only)  */
+    SAGESLA_WS_COUNT
+};
+/*
+ * Code layouts (one 64-token block = 8192 bytes; lane l in 0..63, g = l/32, r = l%32):
+ *  Q8/K8: byte ((t*4 + s)*64 + l)*16 + e holds row 32*t + r, channel 64*g + 16*s + e
+ *         (t in 0..1, s in 0..3, e in 0..15); rows past N are 0.
+ *  V8:    byte (dt*64 + l)*32 + e holds channel 32*dt + r of token
+ *         32*(e/16) + 8*((e%16)/4) + 4*g + e%4 (dt in 0..3, e in 0..31); rows past N are 0.
+ * Nc = ceil(Nb/16).
+ */
+
+int sagesla_version(void);
+const char *sagesla_status_string(sagesla_status s);
+
+/* Number of kept key blocks per query block: clamp(ceil(topk*Nb - 1e-9), 1, Nb). */
+sagesla_status sagesla_ksel(int N, int block, double topk, int *ksel);
+
+/* Bytes of workspace sagesla_fwd needs (linear = 0 when proj will be NULL). Host only. */
+sagesla_status sagesla_workspace_size(int B, int H, int N, int d, int block, double topk,
+                                      int linear, size_t *bytes);
+
+/* Byte offsets of the SAGESLA_WS_* regions inside the workspace (unused regions get the
+ * total size). Host only. */
+sagesla_status sagesla_workspace_layout(int B, int H, int N, int d, int block, double topk,
+                                        int linear, size_t offsets[SAGESLA_WS_COUNT]);
+
+/*
+ * Full forward: out = SageSLA(q, k, v) (+ linear branch through proj when proj != NULL
+ * and ksel < Nb). workspace: device memory of at least sagesla_workspace_size bytes;
+ * its contents on return are the SAGESLA_WS_* intermediates of this call.
+ */
+sagesla_status sagesla_fwd(const void *q, const void *k, const void *v, const void *proj,
+                           int B, int H, int N, int d, double topk, int block, void *out,
+                           void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
+
+/* ---- stages ("friends"): the same conventions; buffers as in the workspace table ---- */
+
+/* Block pooling of Q and K (fp64 sums of the bf16 inputs), K block sums, V block max,
+ * and INT8 quantization of Q per block. */
+sagesla_status sagesla_pool(const void *q, const void *k, const void *v, int B, int H, int N,
+                            int d, int block, void *qbar, void *kbart, void *ksum,
+                            void *vamax_blk, void *q8, void *sq, sagesla_stream_t stream);
+
+/* Per-head reductions: K channel mean (from block sums) and V channel max. */
+sagesla_status sagesla_head_stats(const void *ksum, const void *vamax_blk, int B, int H, int N,
+                                  int d, int block, void *kmean, void *vamax,
+                                  sagesla_stream_t stream);
+
+/* Block scores (fp64) and top-ksel selection per query block. */
+sagesla_status sagesla_select(const void *qbar, const void *kbart, int B, int H, int N, int d,
+                              int block, double topk, void *idx, sagesla_stream_t stream);
+
+/* K smoothing + INT8, V FP8, and (when hs != NULL) the linear-branch states H_j, z_j
+ * and their 16-block partial sums. */
+sagesla_status sagesla_quant_kv(const void *k, const void *v, const void *kmean,
+                                const void *vamax, int B, int H, int N, int d, int block,
+                                void *k8, void *sk, void *v8, void *hs, void *zs, void *hpart,
+                                void *zpart, sagesla_stream_t stream);
+
+/* Totals H = sum_j H_j, z = sum_j z_j from the partial sums. */
+sagesla_status sagesla_linear_total(const void *hpart, const void *zpart, int B, int H, int N,
+                                    int d, int block, void *htot, void *ztot,
+                                    sagesla_stream_t stream);
+
+/* Linear branch: complement = total - kept, O_l = phi(q) H^c / (phi(q).z^c), y = O_l W. */
+sagesla_status sagesla_linear_complement(const void *q, const void *idx, const void *hs,
+                                         const void *zs, const void *htot, const void *ztot,
+                                         const void *proj, int B, int H, int N, int d,
+                                         int block, double topk, void *y,
+                                         sagesla_stream_t stream);
+
+/* Sparse attention over the kept blocks and the epilogue out = O_s (+ y if y != NULL). */
+sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k8,
+                                   const void *sk, const void *v8, const void *vamax,
+                                   const void *idx, const void *y, int B, int H, int N, int d,
+                                   int block, double topk, void *out, sagesla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGESLA_H */

@@ -37,8 +37,8 @@ def lib():
             "oracle_num_blocks": (i32, [i32, i32]),
             "oracle_ksel": (i32, [f64, i32]),
             "oracle_pool": (None, [P, i32, i32, i32, P]),
-            "oracle_scores": (None, [P, P, i32, i32, P]),
-            "oracle_select": (None, [P, i32, i32, P]),
+            "oracle_scores": (None, [P, P, i32, i32, i32, P]),
+            "oracle_select": (None, [P, i32, i32, i32, P]),
             "oracle_k_mean": (None, [P, i32, i32, P]),
             "oracle_quant_blocks": (None, [P, i32, i32, i32, P, P]),
             "oracle_quant_v": (None, [P, i32, i32, P, P]),
@@ -107,18 +107,21 @@ def pool(x_bits, blk=64):
 
 
 def scores(qbar, kbar):
+    """[nq, nk] block scores qbar_i . kbar_j / sqrt(d)."""
     qbar, kbar = _c(qbar, np.float64), _c(kbar, np.float64)
-    Nb, d = qbar.shape
-    out = np.empty((Nb, Nb), np.float64)
-    lib().oracle_scores(_p(qbar), _p(kbar), Nb, d, _p(out))
+    nq, d = qbar.shape
+    nk = kbar.shape[0]
+    out = np.empty((nq, nk), np.float64)
+    lib().oracle_scores(_p(qbar), _p(kbar), nq, nk, d, _p(out))
     return out
 
 
 def select(score_mat, k: int):
+    """Top-k columns of every row (score desc, index asc), ascending. [nq, k] int32."""
     s = _c(score_mat, np.float64)
-    Nb = s.shape[0]
-    idx = np.empty((Nb, k), np.int32)
-    lib().oracle_select(_p(s), Nb, k, _p(idx))
+    nq, nk = s.shape
+    idx = np.empty((nq, k), np.int32)
+    lib().oracle_select(_p(s), nq, nk, k, _p(idx))
     return idx
 
 
@@ -222,6 +225,7 @@ def sagesla_head(q_bits, k_bits, v_bits, w_bits, topk, quant=True, qblocks=None,
     """SageSLA forward of one head. Returns dict(out, out_s, out_l, idx, ksel, qblocks).
 
     out/out_s/out_l are [len(qblocks)*blk, d] fp64; rows past N in the last block are 0.
+    idx is [Nb, ksel]; rows of query blocks not listed in qblocks are -1.
     """
     q = _c(q_bits, np.uint16)
     k = _c(k_bits, np.uint16)

@@ -22,7 +22,7 @@
  * The pages give no formulas. Every step below that they leave open follows one
  * stated reading (block granularity 64, mean pooling, scores qbar.kbar/sqrt(d),
  * ceil(topk*Nb) blocks per query block, K-mean smoothing, per-block INT8 Q/K,
- * per-channel FP8 e4m3 V, e4m3(p*448) probabilities, phi = softmax over channels,
+ * per-channel FP8 e4m3 V, e4m3(448 p) probabilities, phi = softmax over channels,
  * O = O_s + O_l W_proj). Parity of those choices is unpinned by the pages; the
  * implementation of each is pinned by the tests in tests/test_oracle_*.py.
  *
@@ -163,16 +163,16 @@ void oracle_pool(const uint16_t *x, int N, int d, int blk, double *out)
 
 /* ---------------------------------------------------------------- O2, O3: score and select */
 
-/* s_ij = qbar_i . kbar_j / sqrt(d), fp64. scores: [Nb][Nb]. */
-void oracle_scores(const double *qbar, const double *kbar, int Nb, int d, double *scores)
+/* s_ij = qbar_i . kbar_j / sqrt(d), fp64. qbar: [nq][d], kbar: [nk][d], scores: [nq][nk]. */
+void oracle_scores(const double *qbar, const double *kbar, int nq, int nk, int d, double *scores)
 {
     double inv = 1.0 / sqrt((double)d);
-    for (int i = 0; i < Nb; i++)
-        for (int j = 0; j < Nb; j++) {
+    for (int i = 0; i < nq; i++)
+        for (int j = 0; j < nk; j++) {
             double s = 0.0;
             for (int c = 0; c < d; c++)
                 s += qbar[(size_t)i * d + c] * kbar[(size_t)j * d + c];
-            scores[(size_t)i * Nb + j] = s * inv;
+            scores[(size_t)i * nk + j] = s * inv;
         }
 }
 
@@ -180,12 +180,12 @@ void oracle_scores(const double *qbar, const double *kbar, int Nb, int d, double
  * For every query block keep the ksel key blocks with the largest score; equal scores
  * prefer the lower key index. The kept indices are written in ascending order.
  * Plain selection: ksel passes, each picking the best not-yet-taken block.
- * idx: [Nb][ksel].
+ * scores: [nq][Nb], idx: [nq][ksel].
  */
-void oracle_select(const double *scores, int Nb, int ksel, int32_t *idx)
+void oracle_select(const double *scores, int nq, int Nb, int ksel, int32_t *idx)
 {
     char *taken = (char *)malloc((size_t)Nb);
-    for (int i = 0; i < Nb; i++) {
+    for (int i = 0; i < nq; i++) {
         const double *row = scores + (size_t)i * Nb;
         memset(taken, 0, (size_t)Nb);
         for (int r = 0; r < ksel; r++) {
@@ -303,9 +303,12 @@ int32_t oracle_dot_i8(const int8_t *a, const int8_t *b, int d)
  * on the kept blocks): for each kept key block j in ascending order,
  *   S = q8 . k8 (int32), a = (s_q[i]*s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
  *   x = fp32(S)*a, m' = max(m, max x), alpha = exp2f(m - m'),
- *   p = exp2f(x - m'), l = l*alpha + sum p (fp64),
- *   p8 = e4m3(p*448), acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
- * Output row: acc[c] * sv[c] / (448*l). Keys past N are skipped.
+ *   w = exp2f(fmaf(fp32(S), a, L - m')) with L = fp32(log2(448)), i.e. w = 448 p for
+ *     p = 2^(x - m') (the exponent argument is formed in fp32 exactly as the FP8 code
+ *     decision is taken on the GPU),
+ *   l = l*alpha + sum w (fp64), p8 = e4m3(w) (saturating), 
+ *   acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
+ * Output row: acc[c] * sv[c] / l. Keys past N are skipped.
  * out: [blk][d] (rows past N left untouched).
  */
 void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
@@ -314,9 +317,10 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
                          double *out)
 {
     const float c0 = (float)(1.4426950408889634 / sqrt((double)d));
+    const float L = (float)log2(448.0);
     int nq = block_len(qb, N, blk);
     const int32_t *crit = idx + (size_t)qb * ksel;
-    float *x = (float *)malloc(sizeof(float) * blk);
+    float *sf = (float *)malloc(sizeof(float) * blk);
     double *acc = (double *)malloc(sizeof(double) * d);
     for (int r = 0; r < nq; r++) {
         const int8_t *qrow = q8 + (size_t)(qb * blk + r) * d;
@@ -330,32 +334,33 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
             float a = (sq[qb] * sk[j]) * c0;
             float mb = -INFINITY;
             for (int t = 0; t < nk; t++) {
-                int32_t S = oracle_dot_i8(qrow, k8 + (size_t)(j * blk + t) * d, d);
-                x[t] = (float)S * a;
-                if (x[t] > mb)
-                    mb = x[t];
+                sf[t] = (float)oracle_dot_i8(qrow, k8 + (size_t)(j * blk + t) * d, d);
+                float x = sf[t] * a;
+                if (x > mb)
+                    mb = x;
             }
             float mn = m > mb ? m : mb;
             float alpha = exp2f(m - mn);
-            double psum = 0.0;
+            float bias = L - mn;
+            double wsum = 0.0;
             l *= (double)alpha;
             for (int c = 0; c < d; c++)
                 acc[c] *= (double)alpha;
             for (int t = 0; t < nk; t++) {
-                float p = exp2f(x[t] - mn);
-                psum += (double)p;
-                double pq = dec8(oracle_e4m3_encode(p * 448.0f));
+                float w = exp2f(fmaf(sf[t], a, bias));
+                wsum += (double)w;
+                double pq = dec8(oracle_e4m3_encode(w));
                 const uint8_t *vrow = v8 + (size_t)(j * blk + t) * d;
                 for (int c = 0; c < d; c++)
                     acc[c] += pq * dec8(vrow[c]);
             }
-            l += psum;
+            l += wsum;
             m = mn;
         }
         for (int c = 0; c < d; c++)
-            out[(size_t)r * d + c] = acc[c] * (double)sv[c] / (448.0 * l);
+            out[(size_t)r * d + c] = acc[c] * (double)sv[c] / l;
     }
-    free(x);
+    free(sf);
     free(acc);
 }
 
@@ -530,9 +535,10 @@ void oracle_project(const double *ol, const uint16_t *w, int rows, int d, double
  * O_s from the quantized sparse softmax (quant = 1) or its fp64 form (quant = 0),
  * O_l from the linear branch over the blocks that were not kept (skipped when w is
  * NULL). Outputs for listed block b go to rows [b_pos*blk, b_pos*blk + n_b) of out,
- * out_s, out_l (each [nqb*blk][d]; out_s / out_l may be NULL). idx_out (may be NULL)
- * receives the kept blocks of every query block, [Nb][ksel].
- * Returns ksel, or -1 on bad arguments.
+ * out_s, out_l (each [nqb*blk][d]; out_s / out_l may be NULL). idx_out (may be NULL,
+ * [Nb][ksel]) receives the kept blocks of every listed query block in its row; rows of
+ * query blocks that are not listed are set to -1. Scores and selection are evaluated
+ * only for the listed query blocks. Returns ksel, or -1 on bad arguments.
  */
 int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const uint16_t *w, int N, int d, int blk, double topk, int quant,
@@ -544,20 +550,29 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     int Nb = oracle_num_blocks(N, blk);
     int ksel = oracle_ksel(topk, Nb);
 
+    /* O1-O3: pooling, scores and selection for the listed query blocks */
     double *qbar = (double *)malloc(sizeof(double) * (size_t)Nb * d);
     double *kbar = (double *)malloc(sizeof(double) * (size_t)Nb * d);
-    double *scores = (double *)malloc(sizeof(double) * (size_t)Nb * Nb);
+    double *srow = (double *)malloc(sizeof(double) * (size_t)Nb);
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)Nb * ksel);
+    for (size_t e = 0; e < (size_t)Nb * ksel; e++)
+        idx[e] = -1;
     oracle_pool(q, N, d, blk, qbar);
     oracle_pool(k, N, d, blk, kbar);
-    oracle_scores(qbar, kbar, Nb, d, scores);
-    oracle_select(scores, Nb, ksel, idx);
+    for (int b = 0; b < nqb; b++) {
+        int qb = qblocks[b];
+        if (qb < 0 || qb >= Nb)
+            continue;
+        oracle_scores(qbar + (size_t)qb * d, kbar, 1, Nb, d, srow);
+        oracle_select(srow, 1, Nb, ksel, idx + (size_t)qb * ksel);
+    }
     if (idx_out)
         memcpy(idx_out, idx, sizeof(int32_t) * (size_t)Nb * ksel);
     free(qbar);
     free(kbar);
-    free(scores);
+    free(srow);
 
+    /* O4-O6: smoothing and quantization */
     int8_t *q8 = NULL, *k8 = NULL;
     uint8_t *v8 = NULL;
     float *sq = NULL, *sk = NULL, *sv = NULL;
@@ -582,6 +597,7 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         free(mu);
     }
 
+    /* O8 states */
     double *H = NULL, *z = NULL;
     int linear = (w != NULL) && ksel < Nb;
     if (linear) {
@@ -590,6 +606,7 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         oracle_linear_states(k, v, N, d, blk, H, z);
     }
 
+    /* O7-O10 per listed query block */
     double *os = (double *)malloc(sizeof(double) * (size_t)blk * d);
     double *ol = (double *)malloc(sizeof(double) * (size_t)blk * d);
     double *y = (double *)malloc(sizeof(double) * (size_t)blk * d);

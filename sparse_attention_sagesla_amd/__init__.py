@@ -1,9 +1,12 @@
 """SageSLA attention forward for AMD Instinct MI355X (gfx950).
 
 The compute path is the C-ABI library ``libsagesla.so`` built from hand-written HIP
-kernels (``csrc/``); this package only marshals torch tensors into it. The library
-is loaded on first use; there is no CPU fallback.
+kernels (``csrc/``, interface in ``include/sagesla.h``); this package only marshals torch
+tensors into it. The library is loaded on first use; there is no CPU fallback.
 """
 from . import synth  # noqa: F401  (seeded synthetic inputs)
+from ._lib import (SageSLAError, alloc_workspace, fwd, ksel, lib, status_string,  # noqa: F401
+                   workspace_layout, workspace_size, workspace_views)
 
-__all__ = ["synth"]
+__all__ = ["fwd", "ksel", "workspace_size", "workspace_layout", "workspace_views", "alloc_workspace",
+           "SageSLAError", "status_string", "lib", "synth"]

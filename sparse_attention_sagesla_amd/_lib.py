@@ -1,0 +1,169 @@
+"""ctypes binding of libsagesla.so (the C ABI declared in include/sagesla.h).
+
+Argument marshalling only: torch tensors provide device memory and the stream; every
+step of the computation runs in the library's HIP kernels. There is no fallback: if the
+library is missing or the device is not gfx950 the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsagesla.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+
+WS_REGIONS = ["qbar", "kbart", "ksum", "vamax_blk", "kmean", "vamax", "q8", "sq", "k8", "sk", "v8", "idx",
+              "hs", "zs", "hpart", "zpart", "htot", "ztot", "y"]
+WS_COUNT = len(WS_REGIONS)
+
+EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_workspace_size",
+           "sagesla_workspace_layout", "sagesla_fwd", "sagesla_pool", "sagesla_head_stats", "sagesla_select",
+           "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn"]
+
+_lib = None
+
+
+class SageSLAError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, status_string(status), status))
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libsagesla.so is not built (run sparse_attention_sagesla_amd/build.py); "
+                              "there is no fallback path")
+        L = C.CDLL(LIB_PATH)
+        P, i32, f64, sz = C.c_void_p, C.c_int, C.c_double, C.c_size_t
+        dims = [i32, i32, i32, i32]
+        sigs = {
+            "sagesla_version": (i32, []),
+            "sagesla_status_string": (C.c_char_p, [i32]),
+            "sagesla_ksel": (i32, [i32, i32, f64, C.POINTER(i32)]),
+            "sagesla_workspace_size": (i32, dims + [i32, f64, i32, C.POINTER(sz)]),
+            "sagesla_workspace_layout": (i32, dims + [i32, f64, i32, C.POINTER(sz * WS_COUNT)]),
+            "sagesla_fwd": (i32, [P, P, P, P] + dims + [f64, i32, P, P, sz, P]),
+            "sagesla_pool": (i32, [P, P, P] + dims + [i32] + [P] * 6 + [P]),
+            "sagesla_head_stats": (i32, [P, P] + dims + [i32, P, P, P]),
+            "sagesla_select": (i32, [P, P] + dims + [i32, f64, P, P]),
+            "sagesla_quant_kv": (i32, [P, P, P, P] + dims + [i32] + [P] * 7 + [P]),
+            "sagesla_linear_total": (i32, [P, P] + dims + [i32, P, P, P]),
+            "sagesla_linear_complement": (i32, [P] * 7 + dims + [i32, f64, P, P]),
+            "sagesla_sparse_attn": (i32, [P] * 8 + dims + [i32, f64, P, P]),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().sagesla_status_string(int(s)).decode()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, what):
+    if status != OK:
+        raise SageSLAError(status, what)
+
+
+def ksel(N: int, topk: float, block: int = 64) -> int:
+    out = C.c_int()
+    _check(lib().sagesla_ksel(N, block, float(topk), C.byref(out)), "sagesla_ksel")
+    return out.value
+
+
+def workspace_size(B, H, N, d=128, block=64, topk=0.1, linear=True) -> int:
+    out = C.c_size_t()
+    _check(lib().sagesla_workspace_size(B, H, N, d, block, float(topk), int(bool(linear)), C.byref(out)),
+           "sagesla_workspace_size")
+    return out.value
+
+
+def workspace_layout(B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict:
+    arr = (C.c_size_t * WS_COUNT)()
+    _check(lib().sagesla_workspace_layout(B, H, N, d, block, float(topk), int(bool(linear)), C.byref(arr)),
+           "sagesla_workspace_layout")
+    return {name: arr[i] for i, name in enumerate(WS_REGIONS)}
+
+
+def _shape(q):
+    if q.dim() != 4 or q.dtype != torch.bfloat16 or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q/k/v must be contiguous bf16 CUDA tensors of shape [B, H, N, d]")
+    return q.shape
+
+
+def alloc_workspace(q, topk=0.1, linear=True, block=64):
+    B, H, N, d = _shape(q)
+    n = workspace_size(B, H, N, d, block, topk, linear)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def fwd(q, k, v, proj=None, topk=0.1, block=64, out=None, workspace=None, stream=None):
+    """out = SageSLA(q, k, v) [+ linear branch through proj]. Returns out (bf16 [B, H, N, d])."""
+    B, H, N, d = _shape(q)
+    for x in (k, v):
+        if _shape(x) != q.shape:
+            raise ValueError("q, k, v shapes differ")
+    if proj is not None and (proj.shape != (d, d) or proj.dtype != torch.bfloat16 or not proj.is_contiguous()):
+        raise ValueError("proj must be a contiguous bf16 [d, d] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(q, topk, proj is not None, block)
+    st = lib().sagesla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(proj), B, H, N, d, float(topk), block, _ptr(out),
+                           _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sagesla_fwd")
+    return out
+
+
+def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict:
+    """Typed torch views of the intermediates left in a workspace by fwd()."""
+    lay = workspace_layout(B, H, N, d, block, topk, linear)
+    BH, Nb = B * H, (N + block - 1) // block
+    k = ksel(N, topk, block)
+    Nc = (Nb + 15) // 16
+    spec = {
+        "qbar": (torch.float64, (BH, Nb, d)), "kbart": (torch.float64, (BH, d, Nb)),
+        "ksum": (torch.float64, (BH, Nb, d)), "vamax_blk": (torch.float32, (BH, Nb, d)),
+        "kmean": (torch.float32, (BH, d)), "vamax": (torch.float32, (BH, d)),
+        "q8": (torch.int8, (BH, Nb, 8192)), "sq": (torch.float32, (BH, Nb)),
+        "k8": (torch.int8, (BH, Nb, 8192)), "sk": (torch.float32, (BH, Nb)),
+        "v8": (torch.uint8, (BH, Nb, 8192)), "idx": (torch.int32, (BH, Nb, k)),
+        "hs": (torch.float32, (BH, Nb, d, d)), "zs": (torch.float32, (BH, Nb, d)),
+        "hpart": (torch.float32, (BH, Nc, d, d)), "zpart": (torch.float32, (BH, Nc, d)),
+        "htot": (torch.float32, (BH, d, d)), "ztot": (torch.float32, (BH, d)),
+        "y": (torch.float32, (BH, N, d)),
+    }
+    total = ws.numel()
+    out = {}
+    for name, (dt, shape) in spec.items():
+        off = lay[name]
+        nbytes = torch.Size(shape).numel() * torch.empty((), dtype=dt).element_size()
+        if off >= total or off + nbytes > total:
+            continue
+        out[name] = ws[off:off + nbytes].view(dt).view(shape)
+    return out

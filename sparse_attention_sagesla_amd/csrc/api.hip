@@ -1,0 +1,318 @@
+// C ABI of the SageSLA forward: argument validation, workspace layout and the launch
+// sequence pool -> head stats -> select -> quantize K/V (+ linear states) -> linear
+// totals -> linear complement -> sparse attention with the fused epilogue.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/sagesla.h"
+#include "common.h"
+
+namespace sagesla {
+hipError_t launch_pool(const void*, const void*, const void*, int, int, int, void*, void*, void*, void*,
+                       void*, void*, hipStream_t);
+hipError_t launch_head_stats(const void*, const void*, int, int, int, void*, void*, hipStream_t);
+hipError_t launch_select(const void*, const void*, int, int, int, void*, hipStream_t);
+hipError_t launch_quant_kv(const void*, const void*, const void*, const void*, int, int, int, void*, void*,
+                           void*, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_linear_total(const void*, const void*, int, int, void*, void*, hipStream_t);
+hipError_t launch_linear_complement(const void*, const void*, const void*, const void*, const void*,
+                                    const void*, const void*, int, int, int, int, void*, hipStream_t);
+hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
+                              const void*, const void*, int, int, int, int, void*, hipStream_t);
+}  // namespace sagesla
+
+using namespace sagesla;
+
+namespace {
+
+constexpr int kMaxN = 1 << 20;
+
+struct Geom {
+  int BH, N, Nb, ksel, Nc;
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ksel_of(int Nb, double topk) {
+  double x = ceil(topk * (double)Nb - 1e-9);
+  int k = (int)x;
+  if (k < 1) k = 1;
+  if (k > Nb) k = Nb;
+  return k;
+}
+
+// Host-only validation of the sizes shared by every entry point.
+sagesla_status check_sizes(int B, int H, int N, int d, int block, Geom* gm) {
+  if (B < 1 || H < 1 || N < 1 || N > kMaxN) return SAGESLA_ERR_INVALID_ARGUMENT;
+  if (d != kD || block != kBlk) return SAGESLA_ERR_UNSUPPORTED;
+  long long BH = (long long)B * H;
+  int Nb = (N + kBlk - 1) / kBlk;
+  if (BH * Nb >= (1LL << 31) || BH * N >= (1LL << 40)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  gm->BH = (int)BH;
+  gm->N = N;
+  gm->Nb = Nb;
+  gm->Nc = (Nb + kChunk - 1) / kChunk;
+  gm->ksel = Nb;
+  return SAGESLA_OK;
+}
+
+sagesla_status check_topk(double topk, Geom* gm) {
+  if (!(topk > 0.0 && topk <= 1.0)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  gm->ksel = ksel_of(gm->Nb, topk);
+  return SAGESLA_OK;
+}
+
+sagesla_status check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr || !aligned16(p)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  return SAGESLA_OK;
+}
+
+sagesla_status check_opt_ptr(const void* p) {
+  return (p != nullptr && !aligned16(p)) ? SAGESLA_ERR_INVALID_ARGUMENT : SAGESLA_OK;
+}
+
+// The current device must be gfx950 (checked once per device).
+sagesla_status check_device() {
+  static std::mutex mu;
+  static int state[64];  // 0 unknown, 1 ok, 2 unsupported
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGESLA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SAGESLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SAGESLA_ERR_HIP;
+    state[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+  }
+  return state[dev] == 1 ? SAGESLA_OK : SAGESLA_ERR_UNSUPPORTED;
+}
+
+sagesla_status from_hip(hipError_t e) { return e == hipSuccess ? SAGESLA_OK : SAGESLA_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* total) {
+  const size_t BH = gm.BH, Nb = gm.Nb, N = gm.N, D = kD, Nc = gm.Nc, ks = gm.ksel;
+  size_t sz[SAGESLA_WS_COUNT] = {};
+  sz[SAGESLA_WS_QBAR] = BH * Nb * D * 8;
+  sz[SAGESLA_WS_KBART] = BH * Nb * D * 8;
+  sz[SAGESLA_WS_KSUM] = BH * Nb * D * 8;
+  sz[SAGESLA_WS_VAMAXB] = BH * Nb * D * 4;
+  sz[SAGESLA_WS_KMEAN] = BH * D * 4;
+  sz[SAGESLA_WS_VAMAX] = BH * D * 4;
+  sz[SAGESLA_WS_Q8] = BH * Nb * kBlkBytes;
+  sz[SAGESLA_WS_SQ] = BH * Nb * 4;
+  sz[SAGESLA_WS_K8] = BH * Nb * kBlkBytes;
+  sz[SAGESLA_WS_SK] = BH * Nb * 4;
+  sz[SAGESLA_WS_V8] = BH * Nb * kBlkBytes;
+  sz[SAGESLA_WS_IDX] = BH * Nb * ks * 4;
+  if (linear) {
+    sz[SAGESLA_WS_HS] = BH * Nb * D * D * 4;
+    sz[SAGESLA_WS_ZS] = BH * Nb * D * 4;
+    sz[SAGESLA_WS_HPART] = BH * Nc * D * D * 4;
+    sz[SAGESLA_WS_ZPART] = BH * Nc * D * 4;
+    sz[SAGESLA_WS_HTOT] = BH * D * D * 4;
+    sz[SAGESLA_WS_ZTOT] = BH * D * 4;
+    sz[SAGESLA_WS_Y] = BH * N * D * 4;
+  }
+  size_t o = 0;
+  for (int r = 0; r < SAGESLA_WS_COUNT; r++) {
+    if (sz[r] == 0) continue;
+    off[r] = o;
+    o += align256(sz[r]);
+  }
+  for (int r = 0; r < SAGESLA_WS_COUNT; r++)
+    if (sz[r] == 0) off[r] = o;
+  *total = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sagesla_version(void) { return 100; }
+
+const char* sagesla_status_string(sagesla_status s) {
+  switch (s) {
+    case SAGESLA_OK: return "ok";
+    case SAGESLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SAGESLA_ERR_UNSUPPORTED: return "unsupported (d must be 128, block 64, device gfx950)";
+    case SAGESLA_ERR_WORKSPACE: return "workspace too small";
+    case SAGESLA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+sagesla_status sagesla_ksel(int N, int block, double topk, int* ksel) {
+  Geom gm;
+  if (!ksel) return SAGESLA_ERR_INVALID_ARGUMENT;
+  sagesla_status s = check_sizes(1, 1, N, kD, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  *ksel = gm.ksel;
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_workspace_layout(int B, int H, int N, int d, int block, double topk, int linear,
+                                        size_t offsets[SAGESLA_WS_COUNT]) {
+  Geom gm;
+  if (!offsets) return SAGESLA_ERR_INVALID_ARGUMENT;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  size_t total;
+  layout(gm, linear != 0 && gm.ksel < gm.Nb, offsets, &total);
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_workspace_size(int B, int H, int N, int d, int block, double topk, int linear,
+                                      size_t* bytes) {
+  Geom gm;
+  if (!bytes) return SAGESLA_ERR_INVALID_ARGUMENT;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  size_t off[SAGESLA_WS_COUNT];
+  layout(gm, linear != 0 && gm.ksel < gm.Nb, off, bytes);
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
+                           int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
+                           sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, out, workspace})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
+  const bool linear = proj != nullptr && gm.ksel < gm.Nb;
+  size_t off[SAGESLA_WS_COUNT], total;
+  layout(gm, linear, off, &total);
+  if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto P = [&](int r) { return (void*)(ws + off[r]); };
+  hipError_t e;
+  if ((e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART),
+                       P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), st)) !=
+      hipSuccess)
+    return from_hip(e);
+  if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb,
+                             P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_IDX),
+                         st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb,
+                           P(SAGESLA_WS_K8), P(SAGESLA_WS_SK), P(SAGESLA_WS_V8),
+                           linear ? P(SAGESLA_WS_HS) : nullptr, linear ? P(SAGESLA_WS_ZS) : nullptr,
+                           linear ? P(SAGESLA_WS_HPART) : nullptr, linear ? P(SAGESLA_WS_ZPART) : nullptr,
+                           st)) != hipSuccess)
+    return from_hip(e);
+  if (linear) {
+    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), P(SAGESLA_WS_ZPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT),
+                                 P(SAGESLA_WS_ZTOT), st)) != hipSuccess)
+      return from_hip(e);
+    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_ZS),
+                                      P(SAGESLA_WS_HTOT), P(SAGESLA_WS_ZTOT), proj, gm.BH, gm.N, gm.Nb,
+                                      gm.ksel, P(SAGESLA_WS_Y), st)) != hipSuccess)
+      return from_hip(e);
+  }
+  e = launch_sparse_attn(P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), P(SAGESLA_WS_K8), P(SAGESLA_WS_SK),
+                         P(SAGESLA_WS_V8), P(SAGESLA_WS_VAMAX), P(SAGESLA_WS_IDX),
+                         linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH, gm.N, gm.Nb, gm.ksel, out, st);
+  return from_hip(e);
+}
+
+sagesla_status sagesla_pool(const void* q, const void* k, const void* v, int B, int H, int N, int d, int block,
+                            void* qbar, void* kbart, void* ksum, void* vamax_blk, void* q8, void* sq,
+                            sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, qbar, kbart, ksum, vamax_blk, q8, sq})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, qbar, kbart, ksum, vamax_blk, q8, sq,
+                              (hipStream_t)stream));
+}
+
+sagesla_status sagesla_head_stats(const void* ksum, const void* vamax_blk, int B, int H, int N, int d, int block,
+                                  void* kmean, void* vamax, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({ksum, vamax_blk, kmean, vamax})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_head_stats(ksum, vamax_blk, gm.BH, gm.N, gm.Nb, kmean, vamax, (hipStream_t)stream));
+}
+
+sagesla_status sagesla_select(const void* qbar, const void* kbart, int B, int H, int N, int d, int block,
+                              double topk, void* idx, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({qbar, kbart, idx})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_select(qbar, kbart, gm.BH, gm.Nb, gm.ksel, idx, (hipStream_t)stream));
+}
+
+sagesla_status sagesla_quant_kv(const void* k, const void* v, const void* kmean, const void* vamax, int B, int H,
+                                int N, int d, int block, void* k8, void* sk, void* v8, void* hs, void* zs,
+                                void* hpart, void* zpart, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({k, v, kmean, vamax, k8, sk, v8})) != SAGESLA_OK) return s;
+  const bool st = hs != nullptr;
+  if (st && (s = check_ptrs({hs, zs, hpart, zpart})) != SAGESLA_OK) return s;
+  if (!st && (zs || hpart || zpart)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_quant_kv(k, v, kmean, vamax, gm.BH, gm.N, gm.Nb, k8, sk, v8, hs, zs, hpart, zpart,
+                                  (hipStream_t)stream));
+}
+
+sagesla_status sagesla_linear_total(const void* hpart, const void* zpart, int B, int H, int N, int d, int block,
+                                    void* htot, void* ztot, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({hpart, zpart, htot, ztot})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_linear_total(hpart, zpart, gm.BH, gm.Nb, htot, ztot, (hipStream_t)stream));
+}
+
+sagesla_status sagesla_linear_complement(const void* q, const void* idx, const void* hs, const void* zs,
+                                         const void* htot, const void* ztot, const void* proj, int B, int H, int N,
+                                         int d, int block, double topk, void* y, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, idx, hs, zs, htot, ztot, proj, y})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_linear_complement(q, idx, hs, zs, htot, ztot, proj, gm.BH, gm.N, gm.Nb, gm.ksel, y,
+                                           (hipStream_t)stream));
+}
+
+sagesla_status sagesla_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk, const void* v8,
+                                   const void* vamax, const void* idx, const void* y, int B, int H, int N, int d,
+                                   int block, double topk, void* out, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q8, sq, k8, sk, v8, vamax, idx, out})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(y)) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_sparse_attn(q8, sq, k8, sk, v8, vamax, idx, y, gm.BH, gm.N, gm.Nb, gm.ksel, out,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

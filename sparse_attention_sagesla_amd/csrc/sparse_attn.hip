@@ -1,0 +1,177 @@
+// Block-sparse quantized attention over the kept key blocks, with the fused epilogue
+// out = O_s + y (y = O_l W_proj from the linear branch, optional).
+//
+// SLA computes only the top ~10 % of block pairs exactly and skips about 90 % of the
+// work (TurboDiffusion explainer, news.qq.com, "First key: attention"); SageAttention
+// runs that exact part on 8-bit data at the matrix cores' 8-bit peak (same section).
+// Here QK^T is INT8 MFMA (v_mfma_i32_32x32x32_i8) and PV is FP8 e4m3 MFMA
+// (v_mfma_f32_32x32x64_f8f6f4), with the online softmax in fp32 registers.
+//
+// Per query block i (64 rows) and kept key block j (ascending), for each row:
+//   S = q8 . k8 (int32), a = (s_q[i] * s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
+//   m' = max(m, max float(S)*a), alpha = 2^(m - m'),
+//   w = 2^fma(float(S), a, log2(448) - m')  (= 448 p with p = 2^(x - m')),
+//   l = l*alpha + sum w, P8 = e4m3(w), acc = acc*alpha + P8 . V8.
+// Epilogue: O = acc * s_v / l (+ y), rounded to bf16.
+//
+// Work split: one workgroup of 2 waves per (bh, i); wave w owns query rows 32w..32w+31.
+// S^T = K8 Q8^T is computed so that each lane holds one query and 32 of the 64 keys:
+// the row max and row sum stay in registers plus one exchange with lane l^32, and the
+// probabilities are already in the B-operand layout of O^T = V8^T P8^T (the V8 code
+// block is stored in the matching key order).
+#include <math.h>
+
+#include "common.h"
+
+namespace sagesla {
+
+constexpr float kLog2_448 = 8.807354922057604f;  // fp32(log2(448))
+
+// c0 = fp32(log2(e) / sqrt(d)), rounded once from double
+static float log2e_over_sqrt_d() { return (float)(1.4426950408889634 / sqrt((double)kD)); }
+
+__device__ __forceinline__ int key_of_slot(int g, int t, int v) { return 32 * t + 8 * (v >> 2) + 4 * g + (v & 3); }
+
+__global__ __launch_bounds__(128) void sparse_attn_kernel(
+    const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
+    const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
+    const int32_t* __restrict__ idx, const float* __restrict__ y, int N, int Nb, int ksel, int tiles,
+    int per_xcd, float c0, uint16_t* __restrict__ out) {
+  const int tile = xcd_tile(blockIdx.x, per_xcd);
+  if (tile >= tiles) return;
+  const int bh = tile / Nb, i = tile % Nb;
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, r = l & 31;
+  const size_t hb = (size_t)bh * Nb;
+
+  // Q8 B-operand for query tile w: 4 steps of 16 bytes
+  v4i qb[4];
+  {
+    const int8_t* qsrc = q8 + (hb + i) * kBlkBytes;
+#pragma unroll
+    for (int s = 0; s < 4; s++) qb[s] = *(const v4i*)(qsrc + ((w * 4 + s) * 64 + l) * 16);
+  }
+  const float sqi = sq[hb + i];
+  const int nlast = block_len(Nb - 1, N);  // valid keys in the last block
+
+  float m = -INFINITY, lsum = 0.f;
+  v16f acc[4];
+#pragma unroll
+  for (int d = 0; d < 4; d++) acc[d] = (v16f){};
+
+  const int32_t* crit = idx + (hb + i) * ksel;
+  for (int u = 0; u < ksel; u++) {
+    const int j = crit[u];
+    const int8_t* kb = k8 + (hb + j) * kBlkBytes;
+    const uint8_t* vb = v8 + (hb + j) * kBlkBytes;
+    v4i ka[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int s = 0; s < 4; s++) ka[tt][s] = *(const v4i*)(kb + ((tt * 4 + s) * 64 + l) * 16);
+    v8i va[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) va[d] = *(const v8i*)(vb + (d * 64 + l) * 32);
+
+    v16i S[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++) {
+      S[tt] = (v16i){};
+#pragma unroll
+      for (int s = 0; s < 4; s++) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[tt][s], qb[s], S[tt], 0, 0, 0);
+    }
+    // keys past N in a partial last block do not take part
+    if (j == Nb - 1 && nlast < kBlk) {
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          if (key_of_slot(g, tt, v) >= nlast) S[tt][v] = INT_MIN;
+    }
+    int mx = INT_MIN;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) mx = max(mx, S[tt][v]);
+    {
+      // the builtin returns unsigned lanes: compare as signed
+      auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+      mx = max((int)sw[0], (int)sw[1]);
+    }
+    const float a = (sqi * sk[hb + j]) * c0;
+    const float mn = fmaxf(m, (float)mx * a);
+    // rescale only when some row's running max moved (alpha == 1 otherwise)
+    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < 4; d++) acc[d] *= alpha;
+    }
+    m = mn;
+    // 448 p = 2^fma(S, a, log2(448) - m'). For the row maximum the fused product may land
+    // a few ulps above log2(448); the FP8 conversion saturates (448, 464] to 448.
+    const float bias = kLog2_448 - mn;
+    v8i pb;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++) {
+        float p[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int sv = S[tt][4 * v4 + e];
+          p[e] = sv == INT_MIN ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, a, bias));
+          lsum += p[e];
+        }
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+        pb[4 * tt + v4] = wd;
+      }
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+      acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[d], pb, acc[d], 0, 0, 0, 0, 0, 0);
+  }
+
+  // epilogue: lsum (the sum of w = 448 p) is split over lanes l and l^32
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum), false, false);
+    lsum = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  }
+  const float inv_l = 1.0f / lsum;
+  const int qrow = i * kBlk + 32 * w + r;
+  if (qrow < N) {
+    uint16_t* orow = out + ((size_t)bh * N + qrow) * kD;
+    const float* yrow = y ? y + ((size_t)bh * N + qrow) * kD : nullptr;
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++) {
+        const int c = 32 * d + 8 * v4 + 4 * g;
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) o[e] = acc[d][4 * v4 + e] * ((vamax[(size_t)bh * kD + c + e] / 448.0f) * inv_l);
+        if (yrow) {
+          v4f yv = *(const v4f*)(yrow + c);
+#pragma unroll
+          for (int e = 0; e < 4; e++) o[e] += yv[e];
+        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+        *(uint2*)(orow + c) = pk;
+      }
+  }
+}
+
+hipError_t launch_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk,
+                              const void* v8, const void* vamax, const void* idx, const void* y, int BH,
+                              int N, int Nb, int ksel, void* out, hipStream_t st) {
+  const int tiles = BH * Nb;
+  const int per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL(sparse_attn_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const int8_t*)q8,
+                     (const float*)sq, (const int8_t*)k8, (const float*)sk, (const uint8_t*)v8,
+                     (const float*)vamax, (const int32_t*)idx, (const float*)y, N, Nb, ksel, tiles,
+                     per_xcd, log2e_over_sqrt_d(), (uint16_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace sagesla

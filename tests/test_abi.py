@@ -1,0 +1,127 @@
+"""The C-ABI library loads without a GPU, exports every declared entry point, and rejects
+bad arguments on the host before anything is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+import torch
+
+import sparse_attention_sagesla_amd as S
+from sparse_attention_sagesla_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sagesla.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sagesla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(_lib.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert S.lib().sagesla_version() >= 100
+    for s in range(5):
+        assert len(S.status_string(s)) > 0
+
+
+def test_ksel_matches_rule():
+    assert S.ksel(2048, 0.1) == 4
+    assert S.ksel(32760, 0.1) == 52
+    assert S.ksel(75600, 0.1) == 119
+    assert S.ksel(75600, 0.15) == 178
+    assert S.ksel(75600, 1.0) == 1182
+    assert S.ksel(1920, 0.1) == 3
+    assert S.ksel(37, 0.1) == 1
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(N=0), _lib.ERR_INVALID_ARGUMENT),
+    (dict(N=(1 << 20) + 1), _lib.ERR_INVALID_ARGUMENT),
+    (dict(d=64), _lib.ERR_UNSUPPORTED),
+    (dict(block=128), _lib.ERR_UNSUPPORTED),
+    (dict(topk=0.0), _lib.ERR_INVALID_ARGUMENT),
+    (dict(topk=1.5), _lib.ERR_INVALID_ARGUMENT),
+    (dict(topk=float("nan")), _lib.ERR_INVALID_ARGUMENT),
+    (dict(B=0), _lib.ERR_INVALID_ARGUMENT),
+])
+def test_workspace_size_rejects(args, status):
+    kw = dict(B=1, H=2, N=2048, d=128, block=64, topk=0.1)
+    kw.update(args)
+    out = C.c_size_t()
+    st = S.lib().sagesla_workspace_size(kw["B"], kw["H"], kw["N"], kw["d"], kw["block"], kw["topk"], 1,
+                                        C.byref(out))
+    assert st == status
+
+
+def test_workspace_layout_regions():
+    lay = S.workspace_layout(1, 4, 1000, topk=0.2, linear=True)
+    total = S.workspace_size(1, 4, 1000, topk=0.2, linear=True)
+    offs = sorted(lay.values())
+    assert all(o % 256 == 0 for o in offs)
+    assert len(set(offs)) == len(offs)  # every region present and distinct
+    assert max(offs) < total
+    no_lin = S.workspace_size(1, 4, 1000, topk=0.2, linear=False)
+    assert no_lin < total
+    lay0 = S.workspace_layout(1, 4, 1000, topk=0.2, linear=False)
+    assert lay0["hs"] == no_lin and lay0["y"] == no_lin
+    # topk = 1 keeps every block: the linear branch has nothing to do
+    assert S.workspace_size(1, 4, 1000, topk=1.0, linear=True) == S.workspace_size(1, 4, 1000, topk=1.0,
+                                                                                    linear=False)
+
+
+def _fwd_status(q=0x10000, k=0x20000, v=0x30000, proj=None, B=1, H=2, N=2048, d=128, topk=0.1, block=64,
+                out=0x40000, ws=0x50000, wsbytes=1 << 40):
+    return S.lib().sagesla_fwd(q, k, v, proj, B, H, N, d, topk, block, out, ws, wsbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.ERR_INVALID_ARGUMENT),
+    (dict(ws=None), _lib.ERR_INVALID_ARGUMENT),
+    (dict(k=0x20008), _lib.ERR_INVALID_ARGUMENT),     # misaligned
+    (dict(proj=0x60004), _lib.ERR_INVALID_ARGUMENT),  # misaligned optional pointer
+    (dict(d=96), _lib.ERR_UNSUPPORTED),
+    (dict(block=32), _lib.ERR_UNSUPPORTED),
+    (dict(topk=-0.1), _lib.ERR_INVALID_ARGUMENT),
+    (dict(N=-5), _lib.ERR_INVALID_ARGUMENT),
+    (dict(wsbytes=100), _lib.ERR_WORKSPACE),
+])
+def test_fwd_rejects_before_launch(kw, status):
+    # the pointers are never dereferenced: validation fails on the host first
+    assert _fwd_status(**kw) == status
+
+
+def test_stage_entry_points_reject_bad_arguments():
+    L = S.lib()
+    p = 0x10000
+    assert L.sagesla_pool(None, p, p, 1, 1, 64, 128, 64, p, p, p, p, p, p, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_select(p, p, 1, 1, 64, 128, 64, 2.0, p, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_sparse_attn(p, p, p, p, p, p, p, 0x7, 1, 1, 64, 128, 64, 0.5, p, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_quant_kv(p, p, p, p, 1, 1, 64, 128, 64, p, p, p, None, p, None, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_linear_complement(p, p, p, p, p, p, None, 1, 1, 64, 128, 64, 0.1, p, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is present")
+def test_valid_arguments_without_device_report_hip_error():
+    # all arguments valid: validation passes, the device check fails, nothing is launched
+    assert _fwd_status() in (_lib.ERR_HIP, _lib.ERR_UNSUPPORTED)
+
+
+def test_python_binding_rejects_cpu_tensors():
+    q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.fwd(q, q, q)

@@ -1,0 +1,155 @@
+"""GPU stage parity at sizes the oracle finishes in seconds: every intermediate the
+library leaves in its workspace is compared with the oracle's stage of the same name.
+
+Bars: pooled means, K mean, V max, INT8/FP8 codes and their scales bit-exact (the sums
+are exact in fp64 for these inputs, and both sides take every rounding decision in
+fp32 with the same expressions); kept sets equal except near-ties (pooled-score gap
+< 1e-5); linear states within 1e-5 relative; the sparse part O_s and the projected
+linear part y = O_l W within cos >= 0.9995 and max-abs <= 2e-2 per head, and the
+output within the same bars.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import sparse_attention_sagesla_amd as S
+from sparse_attention_sagesla_amd import synth
+from _helpers import cos, decode_qk_codes, decode_v_codes, mask_mismatch
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (config, overrides)
+    "tiny": (synth.CONFIGS["tiny"], {}),
+    "ragged-field": (synth.CONFIGS["wan1.3b-480p"], dict(H=3, grid=(3, 10, 21), topk=0.3, seed=21)),
+    "tiles-ragged": (synth.CONFIGS["wan14b-720p"], dict(H=2, grid=(4, 20, 33), seed=22)),
+    "longrange": (synth.CONFIGS["i2v-a14b-720p"], dict(H=2, grid=(3, 24, 40), seed=23)),
+    "one-block": (synth.CONFIGS["tiny"], dict(H=2, grid=(1, 1, 37), seed=24)),
+    "ksel-1": (synth.CONFIGS["wan1.3b-480p"], dict(H=2, grid=(2, 16, 40), topk=1e-6, seed=25)),
+}
+
+
+def _run(name):
+    cfg, ov = CASES[name]
+    cfg = synth.scaled(cfg, name=name, **ov) if ov else cfg
+    print("\n[case] %s: H=%d N=%d topk=%g seed=%d" % (name, cfg.H, cfg.N, cfg.topk, cfg.seed), flush=True)
+    x = synth.make_inputs(cfg, device="cuda")
+    ws = S.alloc_workspace(x["q"], cfg.topk, x["proj"] is not None)
+    ws.fill_(0xFF)  # poison: every region the call reads must have been written by it
+    out = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=cfg.topk, workspace=ws)
+    torch.cuda.synchronize()
+    views = S.workspace_views(ws, cfg.B, cfg.H, cfg.N, topk=cfg.topk, linear=x["proj"] is not None)
+    host = {k: v.cpu().numpy() for k, v in views.items()}
+    bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
+    wbits = synth.bf16_bits(x["proj"]) if x["proj"] is not None else None
+    return cfg, x, ws, out, host, bits, wbits
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_stage_parity(name):
+    cfg, x, ws, out, g, bits, wbits = _run(name)
+    N, Nb = cfg.N, O.num_blocks(cfg.N)
+    ksel = O.ksel(cfg.topk, Nb)
+    linear = wbits is not None and ksel < Nb
+    out_h = out.float().cpu().numpy()
+    for bh in range(cfg.B * cfg.H):
+        b, h = divmod(bh, cfg.H)
+        q, k, v = bits["q"][b, h], bits["k"][b, h], bits["v"][b, h]
+        # pooling
+        qbar, kbar = O.pool(q), O.pool(k)
+        assert np.array_equal(g["qbar"][bh], qbar)
+        assert np.array_equal(g["kbart"][bh].T, kbar)
+        # K mean and V max
+        qz = O.quantize_head(q, k, v)
+        assert np.array_equal(g["kmean"][bh], qz["kmean"])
+        assert np.array_equal(g["vamax"][bh] / np.float32(448.0), qz["sv"])
+        # codes and scales
+        assert np.array_equal(g["sq"][bh], qz["sq"])
+        assert np.array_equal(decode_qk_codes(g["q8"][bh]), qz["q8"])
+        assert np.array_equal(g["sk"][bh], qz["sk"])
+        assert np.array_equal(decode_qk_codes(g["k8"][bh]), qz["k8"])
+        v8 = decode_v_codes(g["v8"][bh])
+        assert np.array_equal(v8[:N], qz["v8"]) and np.all(v8[N:] == 0)
+        # selection
+        sc = O.scores(qbar, kbar)
+        ora_idx = O.select(sc, ksel)
+        flips = mask_mismatch(g["idx"][bh], ora_idx, sc)
+        assert len(flips) <= max(1, Nb // 50)
+        if linear:
+            H, z = O.linear_states(k, v)
+            hs = g["hs"][bh].astype(np.float64)
+            assert np.max(np.abs(hs - H)) <= 1e-5 * np.max(np.abs(H))
+            assert np.max(np.abs(g["zs"][bh] - z)) <= 1e-5 * np.max(np.abs(z))
+            assert np.max(np.abs(g["htot"][bh] - H.sum(0))) <= 1e-5 * np.max(np.abs(H.sum(0)))
+        # outputs against the oracle run on the same inputs (its own mask)
+        r = O.sagesla_head(q, k, v, wbits, cfg.topk, quant=True)
+        ok_rows = np.ones(N, bool)
+        for i in flips:
+            ok_rows[i * 64:(i + 1) * 64] = False
+        want = r["out"][:N][ok_rows]
+        got = out_h[b, h][ok_rows]
+        assert cos(got, want) >= 0.9995, (bh, cos(got, want))
+        assert np.max(np.abs(got - want)) <= 2e-2
+        if linear:
+            W = O.bf16_to_f64(wbits)
+            y_want = (r["out_l"][:N] @ W)[ok_rows]
+            y_got = g["y"][bh][ok_rows]
+            assert cos(y_got, y_want) >= 0.9995, (bh, cos(y_got, y_want))
+            assert np.max(np.abs(y_got - y_want)) <= 2e-2
+    # O_s alone: rerun the sparse stage without the linear part on the same workspace
+    if linear:
+        os_ = torch.empty_like(out)
+        st = S.lib().sagesla_sparse_attn(
+            *(ws.data_ptr() + S.workspace_layout(cfg.B, cfg.H, N, topk=cfg.topk, linear=True)[n]
+              for n in ("q8", "sq", "k8", "sk", "v8", "vamax", "idx")),
+            None, cfg.B, cfg.H, N, 128, 64, cfg.topk, os_.data_ptr(),
+            torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        os_h = os_.float().cpu().numpy()
+        for bh in range(cfg.B * cfg.H):
+            b, h = divmod(bh, cfg.H)
+            r = O.sagesla_head(bits["q"][b, h], bits["k"][b, h], bits["v"][b, h], wbits, cfg.topk)
+            c = cos(os_h[b, h], r["out_s"][:N])
+            assert c >= 0.9995, c
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiles-ragged"])
+def test_deterministic_and_finite(name):
+    cfg, x, ws, out, g, bits, wbits = _run(name)
+    out2 = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=cfg.topk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert torch.equal(out, out2)
+
+
+def test_dense_topk_one_matches_oracle():
+    cfg = synth.scaled(synth.CONFIGS["i2v-a14b-720p"], H=2, grid=(2, 12, 20), seed=26, topk=1.0)
+    print("\n[case] dense topk=1 N=%d" % cfg.N, flush=True)
+    x = synth.make_inputs(cfg, device="cuda")
+    out = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=1.0)  # proj given, branch empty
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
+    for h in range(cfg.H):
+        r = O.sagesla_head(bits["q"][0, h], bits["k"][0, h], bits["v"][0, h], None, 1.0)
+        assert cos(o[0, h], r["out"][:cfg.N]) >= 0.9995
+        assert np.max(np.abs(o[0, h] - r["out"][:cfg.N])) <= 2e-2
+
+
+def test_batch_of_two():
+    from dataclasses import replace
+    cfg = replace(synth.scaled(synth.CONFIGS["wan1.3b-480p"], H=2, grid=(2, 10, 19), seed=27, topk=0.25),
+                  B=2)
+    print("\n[case] B=2 N=%d" % cfg.N, flush=True)
+    x = synth.make_inputs(cfg, device="cuda")
+    out = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=cfg.topk)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
+    w = synth.bf16_bits(x["proj"])
+    for b in range(2):
+        for h in range(2):
+            r = O.sagesla_head(bits["q"][b, h], bits["k"][b, h], bits["v"][b, h], w, cfg.topk)
+            assert cos(o[b, h], r["out"][:cfg.N]) >= 0.9995
