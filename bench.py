@@ -25,7 +25,6 @@ import torch  # noqa: E402
 
 PEAK_INT8_FP8_TOPS = 5000.0  # MI355X dense INT8 / FP8 MFMA peak, TOP/s
 PEAK_HBM_GBS = 8000.0
-STAGES = ["pool", "head_stats", "select", "quant_kv", "linear_total", "linear_complement", "sparse_attn"]
 
 
 def parse():
@@ -85,14 +84,12 @@ def main():
             ("select", lambda: L.sagesla_select(P["qbar"], P["kbart"], B, H, N, d, 64, topk, P["idx"], sp)),
             ("quant_kv", lambda: L.sagesla_quant_kv(
                 k.data_ptr(), v.data_ptr(), P["kmean"], P["vamax"], B, H, N, d, 64, P["k8"], P["sk"], P["v8"],
-                P["hs"] if use_lin else None, P["zs"] if use_lin else None, P["hpart"] if use_lin else None,
-                P["zpart"] if use_lin else None, sp)),
+                P["hs"] if use_lin else None, P["hpart"] if use_lin else None, sp)),
         ] + ([
-            ("linear_total", lambda: L.sagesla_linear_total(P["hpart"], P["zpart"], B, H, N, d, 64, P["htot"],
-                                                            P["ztot"], sp)),
+            ("linear_total", lambda: L.sagesla_linear_total(P["hpart"], B, H, N, d, 64, P["htot"], sp)),
             ("linear_complement", lambda: L.sagesla_linear_complement(
-                q.data_ptr(), P["idx"], P["hs"], P["zs"], P["htot"], P["ztot"], proj.data_ptr(), B, H, N, d, 64,
-                topk, P["y"], sp)),
+                q.data_ptr(), P["idx"], P["hs"], P["htot"], proj.data_ptr(), B, H, N, d, 64, topk, P["ulist"],
+                P["umask"], P["ucount"], P["hc"], P["y"], sp)),
         ] if use_lin else []) + [
             ("sparse_attn", lambda: L.sagesla_sparse_attn(
                 P["q8"], P["sq"], P["k8"], P["sk"], P["v8"], P["vamax"], P["idx"], P["y"] if use_lin else None,

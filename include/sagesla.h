@@ -71,13 +71,14 @@ enum {
     SAGESLA_WS_SK,        /* fp32 [BH][Nb]      K block scales                             */
     SAGESLA_WS_V8,        /* e4m3 [BH][Nb][8192] V codes, MFMA operand order               */
     SAGESLA_WS_IDX,       /* int32 [BH][Nb][ksel] kept key blocks, ascending               */
-    SAGESLA_WS_HS,        /* fp32 [BH][Nb][d][d] H_j = phi(K_j)^T V_j       (linear only)  */
-    SAGESLA_WS_ZS,        /* fp32 [BH][Nb][d]    z_j = colsum phi(K_j)      (linear only)  */
-    SAGESLA_WS_HPART,     /* fp32 [BH][Nc][d][d] sums of 16 consecutive H_j (linear only)  */
-    SAGESLA_WS_ZPART,     /* fp32 [BH][Nc][d]    sums of 16 consecutive z_j (linear only)  */
-    SAGESLA_WS_HTOT,      /* fp32 [BH][d][d]     sum of all H_j             (linear only)  */
-    SAGESLA_WS_ZTOT,      /* fp32 [BH][d]        sum of all z_j             (linear only)  */
-    SAGESLA_WS_Y,         /* fp32 [BH][N][d]     O_l W_proj                 (linear only)  */
+    SAGESLA_WS_HS,        /* bf16 [BH][Nb][129][d] state S_j: rows c<128 = H_j^T, row 128 = z_j */
+    SAGESLA_WS_HPART,     /* fp32 [BH][Nc][129][d] sums of 16 consecutive S_j (linear)      */
+    SAGESLA_WS_HTOT,      /* fp32 [BH][129][d]  sum of all S_j                  (linear)   */
+    SAGESLA_WS_ULIST,     /* int32 [BH][Ng][Nb] union of kept blocks of each query group   */
+    SAGESLA_WS_UMASK,     /* u32 [BH][Ng][Nb][4] per union entry: which of the 128 keep it */
+    SAGESLA_WS_UCOUNT,    /* int32 [BH][Ng]     union sizes                     (linear)   */
+    SAGESLA_WS_HC,        /* bf16 [BH][Nb][129][d] complement states total - kept (linear) */
+    SAGESLA_WS_Y,         /* bf16 [BH][N][d]    O_l W_proj                      (linear)   */
     SAGESLA_WS_COUNT
 };
 /*
@@ -86,7 +87,8 @@ enum {
  *         (t in 0..1, s in 0..3, e in 0..15); rows past N are 0.
  *  V8:    byte (dt*64 + l)*32 + e holds channel 32*dt + r of token
  *         32*(e/16) + 8*((e%16)/4) + 4*g + e%4 (dt in 0..3, e in 0..31); rows past N are 0.
- * Nc = ceil(Nb/16).
+ * H_j[a][c] = sum_t phi(k_t)[a] v_t[c], z_j[a] = sum_t phi(k_t)[a] over the tokens of block j.
+ * Nc = ceil(Nb/16) partial sums; Ng = ceil(Nb/128) query-block groups.
  */
 
 int sagesla_version(void);
@@ -130,26 +132,28 @@ sagesla_status sagesla_head_stats(const void *ksum, const void *vamax_blk, int B
 sagesla_status sagesla_select(const void *qbar, const void *kbart, int B, int H, int N, int d,
                               int block, double topk, void *idx, sagesla_stream_t stream);
 
-/* K smoothing + INT8, V FP8, and (when hs != NULL) the linear-branch states H_j, z_j
- * and their 16-block partial sums. */
+/* K smoothing + INT8, V FP8, and (when hs != NULL) the linear-branch states S_j and
+ * their 16-block fp32 partial sums. */
 sagesla_status sagesla_quant_kv(const void *k, const void *v, const void *kmean,
                                 const void *vamax, int B, int H, int N, int d, int block,
-                                void *k8, void *sk, void *v8, void *hs, void *zs, void *hpart,
-                                void *zpart, sagesla_stream_t stream);
+                                void *k8, void *sk, void *v8, void *hs, void *hpart,
+                                sagesla_stream_t stream);
 
-/* Totals H = sum_j H_j, z = sum_j z_j from the partial sums. */
-sagesla_status sagesla_linear_total(const void *hpart, const void *zpart, int B, int H, int N,
-                                    int d, int block, void *htot, void *ztot,
-                                    sagesla_stream_t stream);
+/* Totals S_total = sum_j S_j (fp32) from the partial sums. */
+sagesla_status sagesla_linear_total(const void *hpart, int B, int H, int N, int d, int block,
+                                    void *htot, sagesla_stream_t stream);
 
-/* Linear branch: complement = total - kept, O_l = phi(q) H^c / (phi(q).z^c), y = O_l W. */
+/* Linear branch: per group of 128 query blocks the union of their kept sets (ulist,
+ * umask, ucount), the complement states hc = S_total - sum_kept S_j (a 0/1-mask product
+ * on the matrix cores), and y = O_l W with O_l = phi(q) H^c / (phi(q) . z^c). */
 sagesla_status sagesla_linear_complement(const void *q, const void *idx, const void *hs,
-                                         const void *zs, const void *htot, const void *ztot,
-                                         const void *proj, int B, int H, int N, int d,
-                                         int block, double topk, void *y,
+                                         const void *htot, const void *proj, int B, int H,
+                                         int N, int d, int block, double topk, void *ulist,
+                                         void *umask, void *ucount, void *hc, void *y,
                                          sagesla_stream_t stream);
 
-/* Sparse attention over the kept blocks and the epilogue out = O_s (+ y if y != NULL). */
+/* Sparse attention over the kept blocks and the epilogue out = O_s (+ y if y != NULL;
+ * y is bf16 [B,H,N,d]). */
 sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k8,
                                    const void *sk, const void *v8, const void *vamax,
                                    const void *idx, const void *y, int B, int H, int N, int d,

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libsagesla.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 
 WS_REGIONS = ["qbar", "kbart", "ksum", "vamax_blk", "kmean", "vamax", "q8", "sq", "k8", "sk", "v8", "idx",
-              "hs", "zs", "hpart", "zpart", "htot", "ztot", "y"]
+              "hs", "hpart", "htot", "ulist", "umask", "ucount", "hc", "y"]
 WS_COUNT = len(WS_REGIONS)
 
 EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_workspace_size",
@@ -52,9 +52,9 @@ def lib():
             "sagesla_pool": (i32, [P, P, P] + dims + [i32] + [P] * 6 + [P]),
             "sagesla_head_stats": (i32, [P, P] + dims + [i32, P, P, P]),
             "sagesla_select": (i32, [P, P] + dims + [i32, f64, P, P]),
-            "sagesla_quant_kv": (i32, [P, P, P, P] + dims + [i32] + [P] * 7 + [P]),
-            "sagesla_linear_total": (i32, [P, P] + dims + [i32, P, P, P]),
-            "sagesla_linear_complement": (i32, [P] * 7 + dims + [i32, f64, P, P]),
+            "sagesla_quant_kv": (i32, [P, P, P, P] + dims + [i32] + [P] * 5 + [P]),
+            "sagesla_linear_total": (i32, [P] + dims + [i32, P, P]),
+            "sagesla_linear_complement": (i32, [P] * 5 + dims + [i32, f64] + [P] * 5 + [P]),
             "sagesla_sparse_attn": (i32, [P] * 8 + dims + [i32, f64, P, P]),
         }
         for name, (res, args) in sigs.items():
@@ -146,6 +146,8 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
     BH, Nb = B * H, (N + block - 1) // block
     k = ksel(N, topk, block)
     Nc = (Nb + 15) // 16
+    Ng = (Nb + 127) // 128
+    SE = 129 * d
     spec = {
         "qbar": (torch.float64, (BH, Nb, d)), "kbart": (torch.float64, (BH, d, Nb)),
         "ksum": (torch.float64, (BH, Nb, d)), "vamax_blk": (torch.float32, (BH, Nb, d)),
@@ -153,10 +155,10 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
         "q8": (torch.int8, (BH, Nb, 8192)), "sq": (torch.float32, (BH, Nb)),
         "k8": (torch.int8, (BH, Nb, 8192)), "sk": (torch.float32, (BH, Nb)),
         "v8": (torch.uint8, (BH, Nb, 8192)), "idx": (torch.int32, (BH, Nb, k)),
-        "hs": (torch.float32, (BH, Nb, d, d)), "zs": (torch.float32, (BH, Nb, d)),
-        "hpart": (torch.float32, (BH, Nc, d, d)), "zpart": (torch.float32, (BH, Nc, d)),
-        "htot": (torch.float32, (BH, d, d)), "ztot": (torch.float32, (BH, d)),
-        "y": (torch.float32, (BH, N, d)),
+        "hs": (torch.bfloat16, (BH, Nb, 129, d)), "hpart": (torch.float32, (BH, Nc, 129, d)),
+        "htot": (torch.float32, (BH, 129, d)), "ulist": (torch.int32, (BH, Ng, Nb)),
+        "umask": (torch.int32, (BH, Ng, Nb, 4)), "ucount": (torch.int32, (BH, Ng)),
+        "hc": (torch.bfloat16, (BH, Nb, 129, d)), "y": (torch.bfloat16, (BH, N, d)),
     }
     total = ws.numel()
     out = {}

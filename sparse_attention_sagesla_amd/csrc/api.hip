@@ -15,10 +15,10 @@ hipError_t launch_pool(const void*, const void*, const void*, int, int, int, voi
 hipError_t launch_head_stats(const void*, const void*, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_select(const void*, const void*, int, int, int, void*, hipStream_t);
 hipError_t launch_quant_kv(const void*, const void*, const void*, const void*, int, int, int, void*, void*,
-                           void*, void*, void*, void*, void*, hipStream_t);
-hipError_t launch_linear_total(const void*, const void*, int, int, void*, void*, hipStream_t);
-hipError_t launch_linear_complement(const void*, const void*, const void*, const void*, const void*,
-                                    const void*, const void*, int, int, int, int, void*, hipStream_t);
+                           void*, void*, void*, hipStream_t);
+hipError_t launch_linear_total(const void*, int, int, void*, hipStream_t);
+hipError_t launch_linear_complement(const void*, const void*, const void*, const void*, const void*, int, int,
+                                    int, int, void*, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
                               const void*, const void*, int, int, int, int, void*, hipStream_t);
 }  // namespace sagesla
@@ -30,7 +30,7 @@ namespace {
 constexpr int kMaxN = 1 << 20;
 
 struct Geom {
-  int BH, N, Nb, ksel, Nc;
+  int BH, N, Nb, ksel, Nc, Ng;
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -54,6 +54,7 @@ sagesla_status check_sizes(int B, int H, int N, int d, int block, Geom* gm) {
   gm->N = N;
   gm->Nb = Nb;
   gm->Nc = (Nb + kChunk - 1) / kChunk;
+  gm->Ng = (Nb + kGroup - 1) / kGroup;
   gm->ksel = Nb;
   return SAGESLA_OK;
 }
@@ -95,7 +96,8 @@ sagesla_status from_hip(hipError_t e) { return e == hipSuccess ? SAGESLA_OK : SA
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* total) {
-  const size_t BH = gm.BH, Nb = gm.Nb, N = gm.N, D = kD, Nc = gm.Nc, ks = gm.ksel;
+  const size_t BH = gm.BH, Nb = gm.Nb, N = gm.N, D = kD, Nc = gm.Nc, Ng = gm.Ng, ks = gm.ksel;
+  const size_t SE = kStateElems;
   size_t sz[SAGESLA_WS_COUNT] = {};
   sz[SAGESLA_WS_QBAR] = BH * Nb * D * 8;
   sz[SAGESLA_WS_KBART] = BH * Nb * D * 8;
@@ -110,13 +112,14 @@ void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* t
   sz[SAGESLA_WS_V8] = BH * Nb * kBlkBytes;
   sz[SAGESLA_WS_IDX] = BH * Nb * ks * 4;
   if (linear) {
-    sz[SAGESLA_WS_HS] = BH * Nb * D * D * 4;
-    sz[SAGESLA_WS_ZS] = BH * Nb * D * 4;
-    sz[SAGESLA_WS_HPART] = BH * Nc * D * D * 4;
-    sz[SAGESLA_WS_ZPART] = BH * Nc * D * 4;
-    sz[SAGESLA_WS_HTOT] = BH * D * D * 4;
-    sz[SAGESLA_WS_ZTOT] = BH * D * 4;
-    sz[SAGESLA_WS_Y] = BH * N * D * 4;
+    sz[SAGESLA_WS_HS] = BH * Nb * SE * 2;
+    sz[SAGESLA_WS_HPART] = BH * Nc * SE * 4;
+    sz[SAGESLA_WS_HTOT] = BH * SE * 4;
+    sz[SAGESLA_WS_ULIST] = BH * Ng * Nb * 4;
+    sz[SAGESLA_WS_UMASK] = BH * Ng * Nb * 16;
+    sz[SAGESLA_WS_UCOUNT] = BH * Ng * 4;
+    sz[SAGESLA_WS_HC] = BH * Nb * SE * 2;
+    sz[SAGESLA_WS_Y] = BH * N * D * 2;
   }
   size_t o = 0;
   for (int r = 0; r < SAGESLA_WS_COUNT; r++) {
@@ -211,17 +214,15 @@ sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const vo
     return from_hip(e);
   if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb,
                            P(SAGESLA_WS_K8), P(SAGESLA_WS_SK), P(SAGESLA_WS_V8),
-                           linear ? P(SAGESLA_WS_HS) : nullptr, linear ? P(SAGESLA_WS_ZS) : nullptr,
-                           linear ? P(SAGESLA_WS_HPART) : nullptr, linear ? P(SAGESLA_WS_ZPART) : nullptr,
+                           linear ? P(SAGESLA_WS_HS) : nullptr, linear ? P(SAGESLA_WS_HPART) : nullptr,
                            st)) != hipSuccess)
     return from_hip(e);
   if (linear) {
-    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), P(SAGESLA_WS_ZPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT),
-                                 P(SAGESLA_WS_ZTOT), st)) != hipSuccess)
+    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st)) != hipSuccess)
       return from_hip(e);
-    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_ZS),
-                                      P(SAGESLA_WS_HTOT), P(SAGESLA_WS_ZTOT), proj, gm.BH, gm.N, gm.Nb,
-                                      gm.ksel, P(SAGESLA_WS_Y), st)) != hipSuccess)
+    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj, gm.BH,
+                                      gm.N, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
+                                      P(SAGESLA_WS_UCOUNT), P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
       return from_hip(e);
   }
   e = launch_sparse_attn(P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), P(SAGESLA_WS_K8), P(SAGESLA_WS_SK),
@@ -264,41 +265,42 @@ sagesla_status sagesla_select(const void* qbar, const void* kbart, int B, int H,
 }
 
 sagesla_status sagesla_quant_kv(const void* k, const void* v, const void* kmean, const void* vamax, int B, int H,
-                                int N, int d, int block, void* k8, void* sk, void* v8, void* hs, void* zs,
-                                void* hpart, void* zpart, sagesla_stream_t stream) {
+                                int N, int d, int block, void* k8, void* sk, void* v8, void* hs, void* hpart,
+                                sagesla_stream_t stream) {
   Geom gm;
   sagesla_status s = check_sizes(B, H, N, d, block, &gm);
   if (s != SAGESLA_OK) return s;
   if ((s = check_ptrs({k, v, kmean, vamax, k8, sk, v8})) != SAGESLA_OK) return s;
   const bool st = hs != nullptr;
-  if (st && (s = check_ptrs({hs, zs, hpart, zpart})) != SAGESLA_OK) return s;
-  if (!st && (zs || hpart || zpart)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  if (st && (s = check_ptrs({hs, hpart})) != SAGESLA_OK) return s;
+  if (!st && hpart) return SAGESLA_ERR_INVALID_ARGUMENT;
   if ((s = check_device()) != SAGESLA_OK) return s;
-  return from_hip(launch_quant_kv(k, v, kmean, vamax, gm.BH, gm.N, gm.Nb, k8, sk, v8, hs, zs, hpart, zpart,
+  return from_hip(launch_quant_kv(k, v, kmean, vamax, gm.BH, gm.N, gm.Nb, k8, sk, v8, hs, hpart,
                                   (hipStream_t)stream));
 }
 
-sagesla_status sagesla_linear_total(const void* hpart, const void* zpart, int B, int H, int N, int d, int block,
-                                    void* htot, void* ztot, sagesla_stream_t stream) {
+sagesla_status sagesla_linear_total(const void* hpart, int B, int H, int N, int d, int block, void* htot,
+                                    sagesla_stream_t stream) {
   Geom gm;
   sagesla_status s = check_sizes(B, H, N, d, block, &gm);
   if (s != SAGESLA_OK) return s;
-  if ((s = check_ptrs({hpart, zpart, htot, ztot})) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({hpart, htot})) != SAGESLA_OK) return s;
   if ((s = check_device()) != SAGESLA_OK) return s;
-  return from_hip(launch_linear_total(hpart, zpart, gm.BH, gm.Nb, htot, ztot, (hipStream_t)stream));
+  return from_hip(launch_linear_total(hpart, gm.BH, gm.Nb, htot, (hipStream_t)stream));
 }
 
-sagesla_status sagesla_linear_complement(const void* q, const void* idx, const void* hs, const void* zs,
-                                         const void* htot, const void* ztot, const void* proj, int B, int H, int N,
-                                         int d, int block, double topk, void* y, sagesla_stream_t stream) {
+sagesla_status sagesla_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
+                                         const void* proj, int B, int H, int N, int d, int block, double topk,
+                                         void* ulist, void* umask, void* ucount, void* hc, void* y,
+                                         sagesla_stream_t stream) {
   Geom gm;
   sagesla_status s = check_sizes(B, H, N, d, block, &gm);
   if (s != SAGESLA_OK) return s;
   if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
-  if ((s = check_ptrs({q, idx, hs, zs, htot, ztot, proj, y})) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, idx, hs, htot, proj, ulist, umask, ucount, hc, y})) != SAGESLA_OK) return s;
   if ((s = check_device()) != SAGESLA_OK) return s;
-  return from_hip(launch_linear_complement(q, idx, hs, zs, htot, ztot, proj, gm.BH, gm.N, gm.Nb, gm.ksel, y,
-                                           (hipStream_t)stream));
+  return from_hip(launch_linear_complement(q, idx, hs, htot, proj, gm.BH, gm.N, gm.Nb, gm.ksel, ulist, umask,
+                                           ucount, hc, y, (hipStream_t)stream));
 }
 
 sagesla_status sagesla_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk, const void* v8,

@@ -1,63 +1,226 @@
-// Linear branch of SLA for one query block: complement state = total - kept blocks,
-// O_l = phi(q) H^c / (phi(q) . z^c), then y = O_l W_proj.
+// Linear branch of SLA: complement state = total - kept blocks, then
+// O_l = phi(q) H^c / (phi(q) . z^c) and y = O_l W_proj.
 //
-// SLA sends what it does not compute exactly to a linear-attention variant
-// (bonega.ai blog, SLA paragraph; tiemojia.cn article, 2.2.1); the per-key-block states
-// and the "total minus kept" complement make the cost independent of how many blocks
-// are not kept. phi is the softmax over the d channels of the raw bf16 row.
+// SLA sends what it does not compute exactly to a linear-attention variant (bonega.ai
+// blog, SLA paragraph; tiemojia.cn article, 2.2.1). With per-key-block states S_j
+// (H_j^T and z_j, see quant_kv.hip) the complement of query block i is
+//   S^c_i = S_total - sum_{j kept by i} S_j,
+// so its cost does not depend on how many blocks are left to the linear branch.
+// Neighbouring query blocks keep mostly the same key blocks, so the kept sums of a
+// group of 128 consecutive query blocks are one matrix product on the matrix cores:
+//   M[i][e] = sum_{u in union} C[i][u] * S_{union[u]}[e],  C = 0/1 kept mask,
+// over the union of the group's kept sets (each state row is read once per group).
+// phi is the softmax over the d channels of the raw bf16 row.
 #include "common.h"
 
 namespace sagesla {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef float v4f_ __attribute__((ext_vector_type(4)));
+
+constexpr int kUnionRange = 4096;  // key blocks per LDS pass of the union kernel
+
+// ---------------------------------------------------------------- union of a group
+
+// Per (bh, group): the ascending union of the kept key blocks of query blocks
+// g*128 .. g*128+127, with, per union entry, a 128-bit mask of the query blocks that
+// keep it. ulist: [BH][ng][Nb], umask: [BH][ng][Nb][4], ucount: [BH][ng].
+__global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __restrict__ idx, int Nb, int ksel,
+                                                           int ngroups, int32_t* __restrict__ ulist,
+                                                           uint32_t* __restrict__ umask,
+                                                           int32_t* __restrict__ ucount) {
+  __shared__ uint32_t s_flags[kUnionRange][4];
+  __shared__ int s_tmp[8];
+  const int bh = blockIdx.x / ngroups, grp = blockIdx.x % ngroups, t = threadIdx.x;
+  const int q0 = grp * kGroup, nq = min(kGroup, Nb - q0);
+  const size_t gbase = (size_t)bh * ngroups + grp;
+  int count = 0;
+  for (int r0 = 0; r0 < Nb; r0 += kUnionRange) {
+    const int rl = min(kUnionRange, Nb - r0);
+    for (int e = t; e < rl * 4; e += 256) (&s_flags[0][0])[e] = 0u;
+    __syncthreads();
+    const int32_t* src = idx + ((size_t)bh * Nb + q0) * ksel;
+    for (int e = t; e < nq * ksel; e += 256) {
+      const int j = src[e] - r0;
+      const int qb = e / ksel;
+      if (j >= 0 && j < rl) atomicOr(&s_flags[j][qb >> 5], 1u << (qb & 31));
+    }
+    __syncthreads();
+    // compact the non-empty entries in ascending order: thread t owns a contiguous range
+    const int per = (rl + 255) / 256, j0 = t * per, j1 = min(rl, j0 + per);
+    int n = 0;
+    for (int j = j0; j < j1; j++) n += (s_flags[j][0] | s_flags[j][1] | s_flags[j][2] | s_flags[j][3]) != 0u;
+    // block exclusive scan of n
+    const int lane = t & 63, w = t >> 6;
+    int incl = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_tmp[w] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if (k < w) off += s_tmp[k];
+      tot += s_tmp[k];
+    }
+    int pos = count + off + incl - n;
+    for (int j = j0; j < j1; j++) {
+      const uint32_t m0 = s_flags[j][0], m1 = s_flags[j][1], m2 = s_flags[j][2], m3 = s_flags[j][3];
+      if ((m0 | m1 | m2 | m3) == 0u) continue;
+      ulist[gbase * Nb + pos] = r0 + j;
+      *(uint4*)(umask + (gbase * Nb + pos) * 4) = make_uint4(m0, m1, m2, m3);
+      pos++;
+    }
+    count += tot;
+    __syncthreads();
+  }
+  if (t == 0) ucount[gbase] = count;
+}
+
+// ---------------------------------------------------------------- masked sum on MFMA
+
+constexpr int kBs = 40;  // LDS row stride (bf16) of the transposed state tile: 80 B
+
+// Per (bh, group, state row c in 0..128): for the group's 128 query blocks i,
+//   hc[i][c][a] = htot[c][a] - sum_u C[i][u] S_{union[u]}[c][a]   (a = 0..127)
+// as a [128 x U] x [U x 128] product on v_mfma_f32_16x16x32_bf16 (the 0/1 mask is
+// exact in bf16, the states are bf16, the sums fp32). Wave w owns query blocks
+// 32w .. 32w+31 (2 M-tiles) and all 8 column tiles.
+__global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
+    const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
+    const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
+    uint16_t* __restrict__ hc) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kD * kBs];
+  __shared__ uint32_t s_m[2][32][4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[kGroup * kD];
+
+  const int per_bh = ngroups * 129;
+  const int bh = blockIdx.x / per_bh, rem = blockIdx.x % per_bh;
+  const int grp = rem / 129, c = rem % 129;
+  const size_t gbase = (size_t)bh * ngroups + grp;
+  const int U = ucount[gbase];
+  const int32_t* ul = ulist + gbase * Nb;
+  const uint32_t* um = umask + gbase * Nb * 4;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, kg = lane >> 4;
+
+  v4f_ acc[2][8];
+#pragma unroll
+  for (int m = 0; m < 2; m++)
+#pragma unroll
+    for (int n = 0; n < 8; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (U + 31) / 32;
+  // 32 states x 128 columns per step: thread t holds 16 B (8 columns) of states t/16 and
+  // t/16 + 16, loaded a step ahead and written transposed ([column][state]) into LDS.
+  uint4 pre[2];
+  uint32_t pmask = 0u;
+  auto load = [&](int step) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int u = step * 32 + (t >> 4) + 16 * h;
+      pre[h] = make_uint4(0, 0, 0, 0);
+      if (u < U) pre[h] = *(const uint4*)(hs + ((size_t)bh * Nb + ul[u]) * kStateElems + c * kD + (t & 15) * 8);
+    }
+    if (t < 128) {
+      const int u = step * 32 + (t >> 2);
+      pmask = u < U ? um[(size_t)u * 4 + (t & 3)] : 0u;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int k = (t >> 4) + 16 * h, ch = t & 15;
+      const uint16_t* vh = (const uint16_t*)&pre[h];
+#pragma unroll
+      for (int x = 0; x < 8; x++) s_b[buf][(ch * 8 + x) * kBs + k] = vh[x];
+    }
+    if (t < 128) s_m[buf][t >> 2][t & 3] = pmask;
+  };
+  if (nsteps > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int step = 0; step < nsteps; step++) {
+    const int buf = step & 1;
+    if (step + 1 < nsteps) load(step + 1);
+    // A operand: rows = query blocks 32w + 16m + l16, k = union entries 8kg .. 8kg+7
+    v8s a[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const int bit = 16 * m + l16;
+#pragma unroll
+      for (int x = 0; x < 8; x++) a[m][x] = ((s_m[buf][8 * kg + x][w] >> bit) & 1u) ? (short)0x3F80 : (short)0;
+    }
+#pragma unroll
+    for (int n = 0; n < 8; n++) {
+      const v8bf b = *(const v8bf*)(&s_b[buf][(16 * n + l16) * kBs + 8 * kg]);
+#pragma unroll
+      for (int m = 0; m < 2; m++)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[m]), b, acc[m][n], 0, 0, 0);
+    }
+    if (step + 1 < nsteps) store(buf ^ 1);
+    __syncthreads();
+  }
+  // hc = htot - M, staged through LDS for 16-byte stores
+  const float* ht = htot + (size_t)bh * kStateElems + c * kD;
+#pragma unroll
+  for (int n = 0; n < 8; n++) {
+    const int col = 16 * n + l16;
+    const float tot = ht[col];
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int qi = 32 * w + 16 * m + 4 * kg + v;
+        s_out[qi * kD + col] = f32_to_bf16(tot - acc[m][n][v]);
+      }
+  }
+  __syncthreads();
+  const int q0 = grp * kGroup;
+  for (int e = t; e < kGroup * 16; e += 256) {
+    const int qi = e >> 4, ch = e & 15;
+    if (q0 + qi < Nb)
+      *(uint4*)(hc + ((size_t)bh * Nb + q0 + qi) * kStateElems + c * kD + ch * 8) = *(const uint4*)(s_out + qi * kD + ch * 8);
+  }
+}
+
+// ---------------------------------------------------------------- output per query block
+
 constexpr int kLs = 136;  // LDS row stride (bf16) for 128-wide tiles: 272 B, 16-B aligned
 
-// One workgroup (256 threads, 4 waves) per (bh, query block).
-__global__ __launch_bounds__(256) void linear_complement_kernel(
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ idx, const float* __restrict__ hs,
-    const float* __restrict__ zs, const float* __restrict__ htot, const float* __restrict__ ztot,
-    const uint16_t* __restrict__ proj, int N, int Nb, int ksel, int tiles, int per_xcd,
-    float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[kD * kLs];   // H^c transposed, then W transposed
+// One workgroup (256 threads, 4 waves) per (bh, query block i):
+//   O_l[r] = phi(q_r) H^c_i / (phi(q_r) . z^c_i),  y[r] = O_l[r] W_proj  (bf16).
+// hc holds S^c_i = [H^c_i^T ; z^c_i] (129 x 128) in bf16.
+__global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restrict__ q,
+                                                         const uint16_t* __restrict__ hc,
+                                                         const uint16_t* __restrict__ proj, int N, int Nb,
+                                                         int tiles, int per_xcd, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kD * kLs];  // W transposed [c][a]
   __shared__ __attribute__((aligned(16))) uint16_t s_a[kBlk * kLs];  // phi(Q), then O_l
   __shared__ float s_zc[kD];
   __shared__ float s_den[kBlk];
 
   const int tile = xcd_tile(blockIdx.x, per_xcd);
-  if (tile >= tiles) return;  // grid is rounded up to a multiple of 8
+  if (tile >= tiles) return;
   const int bh = tile / Nb, i = tile % Nb;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, r = lane & 31;
   const int n = block_len(i, N);
+  const uint16_t* S = hc + ((size_t)bh * Nb + i) * kStateElems;
 
-  // ---- complement H^c = H_total - sum_{kept} H_j (thread owns 16 float4 chunks)
-  v4f acc[16];
-  const float* ht = htot + (size_t)bh * kD * kD;
+  if (t < kD) s_zc[t] = bf16_to_f32(S[kD * kD + t]);
+  for (int e = t; e < kD * kD / 8; e += 256) {
+    const int a = e / 16, c0 = (e % 16) * 8;  // W[a][c0..c0+7]
+    uint4 wv = *(const uint4*)(proj + a * kD + c0);
+    const uint16_t* wh = (const uint16_t*)&wv;
 #pragma unroll
-  for (int m = 0; m < 16; m++) acc[m] = *(const v4f*)(ht + 4 * (t + 256 * m));
-  v4f zacc = {0.f, 0.f, 0.f, 0.f};
-  if (t < 32) zacc = *(const v4f*)(ztot + (size_t)bh * kD + 4 * t);
-  const int32_t* crit = idx + ((size_t)bh * Nb + i) * ksel;
-  for (int u = 0; u < ksel; u++) {
-    const int j = crit[u];
-    const float* hj = hs + ((size_t)bh * Nb + j) * kD * kD;
-#pragma unroll
-    for (int m = 0; m < 16; m++) acc[m] -= *(const v4f*)(hj + 4 * (t + 256 * m));
-    if (t < 32) zacc -= *(const v4f*)(zs + ((size_t)bh * Nb + j) * kD + 4 * t);
-  }
-  // H^c[a][c] with a = (t + 256m)/32, c = 4*(t%32) + e -> LDS transposed [c][a] as bf16
-#pragma unroll
-  for (int m = 0; m < 16; m++) {
-    const int a = (t >> 5) + 8 * m, c0 = 4 * (t & 31);
-#pragma unroll
-    for (int e = 0; e < 4; e++) s_b[(c0 + e) * kLs + a] = f32_to_bf16(acc[m][e]);
-  }
-  if (t < 32) {
-#pragma unroll
-    for (int e = 0; e < 4; e++) s_zc[4 * t + e] = zacc[e];
+    for (int x = 0; x < 8; x++) s_w[(c0 + x) * kLs + a] = wh[x];
   }
   __syncthreads();
-
-  // ---- phi(q) rows (16 lanes per row) -> LDS bf16, and den = phi(q) . z^c in fp32
+  // phi(q) rows (16 lanes per row) -> LDS bf16; den = phi(q) . z^c in fp32
   {
     const int rg = t >> 4, ch = t & 15;
 #pragma unroll
@@ -82,7 +245,7 @@ __global__ __launch_bounds__(256) void linear_complement_kernel(
       float den = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        float ph = x[e] / s;
+        const float ph = x[e] / s;
         den += ph * s_zc[ch * 8 + e];
         s_a[row * kLs + ch * 8 + e] = f32_to_bf16(ph);
       }
@@ -92,22 +255,20 @@ __global__ __launch_bounds__(256) void linear_complement_kernel(
     }
   }
   __syncthreads();
-
-  // ---- numerator phi(Q) H^c on MFMA: wave w -> rows 32*(w%2).., column tiles 2*(w/2), +1
+  // numerator phi(Q) H^c: B operand rows come straight from S (row c = output column)
   const int rt = w & 1, ct0 = 2 * (w >> 1);
   v16f num[2] = {(v16f){}, (v16f){}};
 #pragma unroll
   for (int s = 0; s < 8; s++) {
     const int kk = 16 * s + 8 * g;
-    v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
+    const v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
 #pragma unroll
     for (int c = 0; c < 2; c++) {
-      v8bf b = *(const v8bf*)(s_b + (32 * (ct0 + c) + r) * kLs + kk);
+      const v8bf b = *(const v8bf*)(S + (32 * (ct0 + c) + r) * kD + kk);
       num[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, num[c], 0, 0, 0);
     }
   }
   __syncthreads();
-  // O_l = num / den -> LDS (row-major bf16); W transposed -> s_b
 #pragma unroll
   for (int c = 0; c < 2; c++)
 #pragma unroll
@@ -117,45 +278,47 @@ __global__ __launch_bounds__(256) void linear_complement_kernel(
       const float den = s_den[row];
       s_a[row * kLs + col] = f32_to_bf16(den != 0.f ? num[c][qq] / den : 0.f);
     }
-  for (int e = t; e < kD * kD / 8; e += 256) {
-    const int a = e / 16, c0 = (e % 16) * 8;  // W[a][c0..c0+7]
-    uint4 wv = *(const uint4*)(proj + a * kD + c0);
-    const uint16_t* wh = (const uint16_t*)&wv;
-#pragma unroll
-    for (int x = 0; x < 8; x++) s_b[(c0 + x) * kLs + a] = wh[x];
-  }
   __syncthreads();
-  // ---- y = O_l W on MFMA
+  // y = O_l W
   v16f yo[2] = {(v16f){}, (v16f){}};
 #pragma unroll
   for (int s = 0; s < 8; s++) {
     const int kk = 16 * s + 8 * g;
-    v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
+    const v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
 #pragma unroll
     for (int c = 0; c < 2; c++) {
-      v8bf b = *(const v8bf*)(s_b + (32 * (ct0 + c) + r) * kLs + kk);
+      const v8bf b = *(const v8bf*)(s_w + (32 * (ct0 + c) + r) * kLs + kk);
       yo[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, yo[c], 0, 0, 0);
     }
   }
-  float* ydst = y + ((size_t)bh * N + (size_t)i * kBlk) * kD;
+  uint16_t* ydst = y + ((size_t)bh * N + (size_t)i * kBlk) * kD;
 #pragma unroll
   for (int c = 0; c < 2; c++)
 #pragma unroll
     for (int qq = 0; qq < 16; qq++) {
       const int row = 32 * rt + 8 * (qq >> 2) + 4 * g + (qq & 3);
-      if (row < n) ydst[(size_t)row * kD + 32 * (ct0 + c) + r] = yo[c][qq];
+      if (row < n) ydst[(size_t)row * kD + 32 * (ct0 + c) + r] = f32_to_bf16(yo[c][qq]);
     }
 }
 
-hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* zs,
-                                    const void* htot, const void* ztot, const void* proj, int BH,
-                                    int N, int Nb, int ksel, void* y, hipStream_t st) {
+int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
+
+hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
+                                    const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
+                                    void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
+  const int ng = linear_groups(Nb);
+  hipLaunchKernelGGL(linear_union_kernel, dim3(BH * ng), dim3(256), 0, st, (const int32_t*)idx, Nb, ksel, ng,
+                     (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129), dim3(256), 0, st, (const uint16_t*)hs,
+                     (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
+                     Nb, ng, (uint16_t*)hc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles = BH * Nb;
   const int per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(linear_complement_kernel, dim3(per_xcd * 8), dim3(256), 0, st,
-                     (const uint16_t*)q, (const int32_t*)idx, (const float*)hs, (const float*)zs,
-                     (const float*)htot, (const float*)ztot, (const uint16_t*)proj, N, Nb, ksel,
-                     tiles, per_xcd, (float*)y);
+  hipLaunchKernelGGL(linear_out_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)hc, (const uint16_t*)proj, N, Nb, tiles, per_xcd, (uint16_t*)y);
   return hipGetLastError();
 }
 

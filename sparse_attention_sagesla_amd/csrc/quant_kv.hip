@@ -9,6 +9,10 @@
 // needs, per key block j, H_j = phi(K_j)^T V_j and z_j = colsum phi(K_j) with
 // phi = softmax over the d channels of the raw K row; they are computed here from the
 // same loads, on bf16 MFMA with phi split into bf16 hi + lo parts (V is exact in bf16).
+// Each block's state is stored transposed, in bf16, with z as one more row:
+// S_j[c][a] = H_j[a][c] for c < 128 and S_j[128][a] = z_j[a] (129 x 128), which is the
+// operand order of the complement kernels; fp32 sums of 16 consecutive blocks feed the
+// exact totals.
 #include "common.h"
 
 namespace sagesla {
@@ -21,8 +25,8 @@ constexpr int kTs = 72;  // LDS row stride (bf16) of the transposed tiles: 144 B
 __global__ __launch_bounds__(256) void quant_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ kmean,
     const float* __restrict__ vamax, int N, int Nb, int Nc, int8_t* __restrict__ k8,
-    float* __restrict__ sk, uint8_t* __restrict__ v8, float* __restrict__ hs, float* __restrict__ zs,
-    float* __restrict__ hpart, float* __restrict__ zpart) {
+    float* __restrict__ sk, uint8_t* __restrict__ v8, uint16_t* __restrict__ hs,
+    float* __restrict__ hpart) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v8[kBlkBytes];
   __shared__ __attribute__((aligned(16))) uint16_t s_phi_hi[kD * kTs];
   __shared__ __attribute__((aligned(16))) uint16_t s_phi_lo[kD * kTs];
@@ -141,86 +145,80 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(
 #pragma unroll
       for (int e = 0; e < 8; e++) s_z[rg][ch * 8 + e] = zc[e];
       __syncthreads();
+      float zsum_t = 0.f;
       if (t < kD) {
-        float zsum = 0.f;
-        for (int q = 0; q < 16; q++) zsum += s_z[q][t];
-        zs[((size_t)bh * Nb + j) * kD + t] = zsum;
-        zp += zsum;
+        for (int q = 0; q < 16; q++) zsum_t += s_z[q][t];
+        zp += zsum_t;
       }
-      // H_j = phi^T V on MFMA: wave w owns rows a in [32w, 32w+32), all 4 column tiles
+      // H_j^T = V^T phi on MFMA: wave w owns rows c in [32w, 32w+32), all 4 column tiles a
       v16f acc[4];
 #pragma unroll
       for (int c = 0; c < 4; c++) acc[c] = (v16f){};
 #pragma unroll
       for (int s = 0; s < 4; s++) {
         const int tok = 16 * s + 8 * g;
-        v8bf ah = *(const v8bf*)(s_phi_hi + (32 * w + r) * kTs + tok);
-        v8bf al = *(const v8bf*)(s_phi_lo + (32 * w + r) * kTs + tok);
+        v8bf av = *(const v8bf*)(s_vt + (32 * w + r) * kTs + tok);
 #pragma unroll
         for (int c = 0; c < 4; c++) {
-          v8bf b = *(const v8bf*)(s_vt + (32 * c + r) * kTs + tok);
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[c], 0, 0, 0);
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[c], 0, 0, 0);
+          v8bf bh_ = *(const v8bf*)(s_phi_hi + (32 * c + r) * kTs + tok);
+          v8bf bl_ = *(const v8bf*)(s_phi_lo + (32 * c + r) * kTs + tok);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh_, acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl_, acc[c], 0, 0, 0);
         }
       }
-      float* hdst = hs + ((size_t)bh * Nb + j) * kD * kD;
+      uint16_t* hdst = hs + ((size_t)bh * Nb + j) * kStateElems;
 #pragma unroll
       for (int c = 0; c < 4; c++)
 #pragma unroll
         for (int q = 0; q < 16; q++) {
-          int a = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);
-          hdst[a * kD + 32 * c + r] = acc[c][q];
+          const int row = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);  // channel c of V
+          hdst[row * kD + 32 * c + r] = f32_to_bf16(acc[c][q]);
           part[c][q] += acc[c][q];
         }
+      if (t < kD) hdst[kD * kD + t] = f32_to_bf16(zsum_t);
     }
     __syncthreads();
   }
   if (states) {
-    float* pdst = hpart + ((size_t)bh * Nc + chunk) * kD * kD;
+    float* pdst = hpart + ((size_t)bh * Nc + chunk) * kStateElems;
 #pragma unroll
     for (int c = 0; c < 4; c++)
 #pragma unroll
       for (int q = 0; q < 16; q++) {
-        int a = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);
-        pdst[a * kD + 32 * c + r] = part[c][q];
+        const int row = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);
+        pdst[row * kD + 32 * c + r] = part[c][q];
       }
-    if (t < kD) zpart[((size_t)bh * Nc + chunk) * kD + t] = zp;
+    if (t < kD) pdst[kD * kD + t] = zp;
   }
 }
 
-// Totals over the partial sums, one workgroup of 256 threads per (bh, 1024 elements).
-__global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart,
-                                                           const float* __restrict__ zpart, int Nc,
-                                                           float* __restrict__ htot,
-                                                           float* __restrict__ ztot) {
-  const int bh = blockIdx.x / 16, part = blockIdx.x % 16, t = threadIdx.x;
+// Totals over the partial sums: htot[bh][e] = sum_c hpart[bh][c][e], e < 129*128.
+// One workgroup of 256 threads per (bh, 1024 elements).
+__global__ __launch_bounds__(256) void linear_total_kernel(const float* __restrict__ hpart, int Nc,
+                                                           float* __restrict__ htot) {
+  constexpr int kParts = (kStateElems + 1023) / 1024;
+  const int bh = blockIdx.x / kParts, part = blockIdx.x % kParts, t = threadIdx.x;
   const int e = part * 1024 + t * 4;
+  if (e >= kStateElems) return;
   v4f s = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < Nc; c++) s += *(const v4f*)(hpart + ((size_t)bh * Nc + c) * kD * kD + e);
-  *(v4f*)(htot + (size_t)bh * kD * kD + e) = s;
-  if (part == 0 && t < kD) {
-    float z = 0.f;
-    for (int c = 0; c < Nc; c++) z += zpart[((size_t)bh * Nc + c) * kD + t];
-    ztot[(size_t)bh * kD + t] = z;
-  }
+  for (int c = 0; c < Nc; c++) s += *(const v4f*)(hpart + ((size_t)bh * Nc + c) * kStateElems + e);
+  *(v4f*)(htot + (size_t)bh * kStateElems + e) = s;
 }
 
 hipError_t launch_quant_kv(const void* k, const void* v, const void* kmean, const void* vamax, int BH,
-                           int N, int Nb, void* k8, void* sk, void* v8, void* hs, void* zs, void* hpart,
-                           void* zpart, hipStream_t st) {
+                           int N, int Nb, void* k8, void* sk, void* v8, void* hs, void* hpart, hipStream_t st) {
   const int Nc = (Nb + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(quant_kv_kernel, dim3(BH * Nc), dim3(256), 0, st, (const uint16_t*)k,
                      (const uint16_t*)v, (const float*)kmean, (const float*)vamax, N, Nb, Nc,
-                     (int8_t*)k8, (float*)sk, (uint8_t*)v8, (float*)hs, (float*)zs, (float*)hpart,
-                     (float*)zpart);
+                     (int8_t*)k8, (float*)sk, (uint8_t*)v8, (uint16_t*)hs, (float*)hpart);
   return hipGetLastError();
 }
 
-hipError_t launch_linear_total(const void* hpart, const void* zpart, int BH, int Nb, void* htot,
-                               void* ztot, hipStream_t st) {
+hipError_t launch_linear_total(const void* hpart, int BH, int Nb, void* htot, hipStream_t st) {
   const int Nc = (Nb + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(linear_total_kernel, dim3(BH * 16), dim3(256), 0, st, (const float*)hpart,
-                     (const float*)zpart, Nc, (float*)htot, (float*)ztot);
+  constexpr int kParts = (kStateElems + 1023) / 1024;
+  hipLaunchKernelGGL(linear_total_kernel, dim3(BH * kParts), dim3(256), 0, st, (const float*)hpart, Nc,
+                     (float*)htot);
   return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ __device__ __forceinline__ int key_of_slot(int g, int t, int v) { return 32 * t 
 __global__ __launch_bounds__(128) void sparse_attn_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
     const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
-    const int32_t* __restrict__ idx, const float* __restrict__ y, int N, int Nb, int ksel, int tiles,
+    const int32_t* __restrict__ idx, const uint16_t* __restrict__ y, int N, int Nb, int ksel, int tiles,
     int per_xcd, float c0, uint16_t* __restrict__ out) {
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= tiles) return;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(128) void sparse_attn_kernel(
   const int qrow = i * kBlk + 32 * w + r;
   if (qrow < N) {
     uint16_t* orow = out + ((size_t)bh * N + qrow) * kD;
-    const float* yrow = y ? y + ((size_t)bh * N + qrow) * kD : nullptr;
+    const uint16_t* yrow = y ? y + ((size_t)bh * N + qrow) * kD : nullptr;
 #pragma unroll
     for (int d = 0; d < 4; d++)
 #pragma unroll
@@ -150,9 +150,11 @@ __global__ __launch_bounds__(128) void sparse_attn_kernel(
 #pragma unroll
         for (int e = 0; e < 4; e++) o[e] = acc[d][4 * v4 + e] * ((vamax[(size_t)bh * kD + c + e] / 448.0f) * inv_l);
         if (yrow) {
-          v4f yv = *(const v4f*)(yrow + c);
-#pragma unroll
-          for (int e = 0; e < 4; e++) o[e] += yv[e];
+          const uint2 yv = *(const uint2*)(yrow + c);
+          o[0] += bf16_to_f32((uint16_t)(yv.x & 0xffff));
+          o[1] += bf16_to_f32((uint16_t)(yv.x >> 16));
+          o[2] += bf16_to_f32((uint16_t)(yv.y & 0xffff));
+          o[3] += bf16_to_f32((uint16_t)(yv.y >> 16));
         }
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
@@ -169,7 +171,7 @@ hipError_t launch_sparse_attn(const void* q8, const void* sq, const void* k8, co
   const int per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const int8_t*)q8,
                      (const float*)sq, (const int8_t*)k8, (const float*)sk, (const uint8_t*)v8,
-                     (const float*)vamax, (const int32_t*)idx, (const float*)y, N, Nb, ksel, tiles,
+                     (const float*)vamax, (const int32_t*)idx, (const uint16_t*)y, N, Nb, ksel, tiles,
                      per_xcd, log2e_over_sqrt_d(), (uint16_t*)out);
   return hipGetLastError();
 }

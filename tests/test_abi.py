@@ -109,10 +109,11 @@ def test_stage_entry_points_reject_bad_arguments():
     assert L.sagesla_select(p, p, 1, 1, 64, 128, 64, 2.0, p, None) == _lib.ERR_INVALID_ARGUMENT
     assert L.sagesla_sparse_attn(p, p, p, p, p, p, p, 0x7, 1, 1, 64, 128, 64, 0.5, p, None) == \
         _lib.ERR_INVALID_ARGUMENT
-    assert L.sagesla_quant_kv(p, p, p, p, 1, 1, 64, 128, 64, p, p, p, None, p, None, None, None) == \
+    assert L.sagesla_quant_kv(p, p, p, p, 1, 1, 64, 128, 64, p, p, p, None, p, None) == \
         _lib.ERR_INVALID_ARGUMENT
-    assert L.sagesla_linear_complement(p, p, p, p, p, p, None, 1, 1, 64, 128, 64, 0.1, p, None) == \
+    assert L.sagesla_linear_complement(p, p, p, p, None, 1, 1, 64, 128, 64, 0.1, p, p, p, p, p, None) == \
         _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_linear_total(p, 1, 1, 64, 128, 64, None, None) == _lib.ERR_INVALID_ARGUMENT
 
 
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path; a GPU is present")

@@ -74,7 +74,7 @@ def test_full_size_sampled(name):
         if has_y:
             W = O.bf16_to_f64(wbits)
             yg, yo = [], []
-            y_all = views["y"][h].cpu().numpy()
+            y_all = views["y"][h].float().cpu().numpy()
             for pos, i in enumerate(qbl):
                 if pos in flips:
                     continue

@@ -40,7 +40,7 @@ def _run(name):
     out = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=cfg.topk, workspace=ws)
     torch.cuda.synchronize()
     views = S.workspace_views(ws, cfg.B, cfg.H, cfg.N, topk=cfg.topk, linear=x["proj"] is not None)
-    host = {k: v.cpu().numpy() for k, v in views.items()}
+    host = {k: (v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy() for k, v in views.items()}
     bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
     wbits = synth.bf16_bits(x["proj"]) if x["proj"] is not None else None
     return cfg, x, ws, out, host, bits, wbits
@@ -78,10 +78,31 @@ def test_stage_parity(name):
         assert len(flips) <= max(1, Nb // 50)
         if linear:
             H, z = O.linear_states(k, v)
-            hs = g["hs"][bh].astype(np.float64)
-            assert np.max(np.abs(hs - H)) <= 1e-5 * np.max(np.abs(H))
-            assert np.max(np.abs(g["zs"][bh] - z)) <= 1e-5 * np.max(np.abs(z))
-            assert np.max(np.abs(g["htot"][bh] - H.sum(0))) <= 1e-5 * np.max(np.abs(H.sum(0)))
+            # S_j = [H_j^T ; z_j] in bf16: each element within half a bf16 ulp (+ fp32 slack)
+            St = np.concatenate([H.transpose(0, 2, 1), z[:, None, :]], axis=1)
+            hs = g["hs"][bh]
+            assert np.all(np.abs(hs - St) <= 2.0 ** -8 * np.abs(St) + 1e-6 * np.max(np.abs(St)))
+            tot = St.sum(0)
+            assert np.max(np.abs(g["htot"][bh] - tot)) <= 1e-5 * np.max(np.abs(tot))
+            # union of each group's kept sets, with the per-query-block masks
+            gidx = g["idx"][bh]
+            for grp in range((Nb + 127) // 128):
+                rows = range(128 * grp, min(Nb, 128 * grp + 128))
+                want = sorted(set(np.concatenate([gidx[i] for i in rows]).tolist()))
+                cnt = int(g["ucount"][bh][grp])
+                assert cnt == len(want) and list(g["ulist"][bh][grp][:cnt]) == want
+                um = g["umask"][bh][grp][:cnt].view(np.uint32)
+                for u, j in enumerate(want):
+                    keepers = [i for i in rows if j in set(gidx[i].tolist())]
+                    got = [128 * grp + 32 * wd + bb for wd in range(4) for bb in range(32) if (um[u][wd] >> bb) & 1]
+                    assert got == keepers
+            # complement states: total minus the kept blocks (with the GPU's kept sets)
+            for i in range(Nb):
+                keep = np.zeros(Nb, bool)
+                keep[gidx[i]] = True
+                want_c = St[~keep].sum(0)
+                err = np.max(np.abs(g["hc"][bh][i] - want_c))
+                assert err <= 4e-3 * np.max(np.abs(want_c)), (i, err)
         # outputs against the oracle run on the same inputs (its own mask)
         r = O.sagesla_head(q, k, v, wbits, cfg.topk, quant=True)
         ok_rows = np.ones(N, bool)
@@ -94,7 +115,7 @@ def test_stage_parity(name):
         if linear:
             W = O.bf16_to_f64(wbits)
             y_want = (r["out_l"][:N] @ W)[ok_rows]
-            y_got = g["y"][bh][ok_rows]
+            y_got = g["y"][bh][ok_rows].astype(np.float64)
             assert cos(y_got, y_want) >= 0.9995, (bh, cos(y_got, y_want))
             assert np.max(np.abs(y_got - y_want)) <= 2e-2
     # O_s alone: rerun the sparse stage without the linear part on the same workspace
