@@ -39,6 +39,7 @@ def lib():
             "oracle_pool": (None, [P, i32, i32, i32, P]),
             "oracle_scores": (None, [P, P, i32, i32, i32, P]),
             "oracle_select": (None, [P, i32, i32, i32, P]),
+            "oracle_order_best_first": (None, [P, i32, P]),
             "oracle_k_mean": (None, [P, i32, i32, P]),
             "oracle_quant_blocks": (None, [P, i32, i32, i32, P, P]),
             "oracle_quant_v": (None, [P, i32, i32, P, P]),
@@ -123,6 +124,14 @@ def select(score_mat, k: int):
     idx = np.empty((nq, k), np.int32)
     lib().oracle_select(_p(s), nq, nk, k, _p(idx))
     return idx
+
+
+def order_best_first(score_row, kept):
+    """Processing order of one row's kept blocks: best score first, then ascending."""
+    row = _c(score_row, np.float64)
+    out = np.array(kept, np.int32, copy=True)
+    lib().oracle_order_best_first(_p(row), len(out), _p(out))
+    return out
 
 
 def k_mean(k_bits):
@@ -225,7 +234,8 @@ def sagesla_head(q_bits, k_bits, v_bits, w_bits, topk, quant=True, qblocks=None,
     """SageSLA forward of one head. Returns dict(out, out_s, out_l, idx, ksel, qblocks).
 
     out/out_s/out_l are [len(qblocks)*blk, d] fp64; rows past N in the last block are 0.
-    idx is [Nb, ksel]; rows of query blocks not listed in qblocks are -1.
+    idx is [Nb, ksel] in processing order (best first, then ascending); rows of query
+    blocks not listed in qblocks are -1.
     """
     q = _c(q_bits, np.uint16)
     k = _c(k_bits, np.uint16)

@@ -22,7 +22,8 @@
  * The pages give no formulas. Every step below that they leave open follows one
  * stated reading (block granularity 64, mean pooling, scores qbar.kbar/sqrt(d),
  * ceil(topk*Nb) blocks per query block, K-mean smoothing, per-block INT8 Q/K,
- * per-channel FP8 e4m3 V, e4m3(448 p) probabilities, phi = softmax over channels,
+ * per-channel FP8 e4m3 V, e4m3(448 p) probabilities normalised by their own sum,
+ * kept blocks processed best first, phi = softmax over channels,
  * O = O_s + O_l W_proj). Parity of those choices is unpinned by the pages; the
  * implementation of each is pinned by the tests in tests/test_oracle_*.py.
  *
@@ -206,6 +207,24 @@ void oracle_select(const double *scores, int nq, int Nb, int ksel, int32_t *idx)
     free(taken);
 }
 
+/*
+ * Processing order of a row's kept blocks (reading): the block with the highest score
+ * first (lowest index on ties), then the other kept blocks in ascending index order.
+ * The running softmax maximum then starts at (almost always) its final value.
+ * row: one score row [Nb]; kept: the ksel kept indices in ascending order (rewritten).
+ */
+void oracle_order_best_first(const double *row, int ksel, int32_t *kept)
+{
+    int best = 0;
+    for (int u = 1; u < ksel; u++)
+        if (row[kept[u]] > row[kept[best]])
+            best = u; /* strict '>' keeps the lower index on ties */
+    int32_t jb = kept[best];
+    for (int u = best; u > 0; u--)
+        kept[u] = kept[u - 1];
+    kept[0] = jb;
+}
+
 /* ---------------------------------------------------------------- O4: K smoothing */
 
 /*
@@ -300,15 +319,16 @@ int32_t oracle_dot_i8(const int8_t *a, const int8_t *b, int d)
 
 /*
  * Quantized sparse attention for the rows of query block qb (reading of SageAttention
- * on the kept blocks): for each kept key block j in ascending order,
+ * on the kept blocks): for each kept key block j in the row's processing order,
  *   S = q8 . k8 (int32), a = (s_q[i]*s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
  *   x = fp32(S)*a, m' = max(m, max x), alpha = exp2f(m - m'),
  *   w = exp2f(fmaf(fp32(S), a, L - m')) with L = fp32(log2(448)), i.e. w = 448 p for
  *     p = 2^(x - m') (the exponent argument is formed in fp32 exactly as the FP8 code
  *     decision is taken on the GPU),
- *   l = l*alpha + sum w (fp64), p8 = e4m3(w) (saturating), 
- *   acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
- * Output row: acc[c] * sv[c] / l. Keys past N are skipped.
+ *   p8 = e4m3(w) (saturating),
+ *   l = l*alpha + sum dec(p8), acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
+ * Output row: acc[c] * sv[c] / l, i.e. the average of the dequantized V rows weighted by
+ * the FP8 probabilities actually used. Keys past N are skipped.
  * out: [blk][d] (rows past N left untouched).
  */
 void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
@@ -342,19 +362,16 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
             float mn = m > mb ? m : mb;
             float alpha = exp2f(m - mn);
             float bias = L - mn;
-            double wsum = 0.0;
             l *= (double)alpha;
             for (int c = 0; c < d; c++)
                 acc[c] *= (double)alpha;
             for (int t = 0; t < nk; t++) {
-                float w = exp2f(fmaf(sf[t], a, bias));
-                wsum += (double)w;
-                double pq = dec8(oracle_e4m3_encode(w));
+                double pq = dec8(oracle_e4m3_encode(exp2f(fmaf(sf[t], a, bias))));
+                l += pq;
                 const uint8_t *vrow = v8 + (size_t)(j * blk + t) * d;
                 for (int c = 0; c < d; c++)
                     acc[c] += pq * dec8(vrow[c]);
             }
-            l += wsum;
             m = mn;
         }
         for (int c = 0; c < d; c++)
@@ -565,6 +582,7 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
             continue;
         oracle_scores(qbar + (size_t)qb * d, kbar, 1, Nb, d, srow);
         oracle_select(srow, 1, Nb, ksel, idx + (size_t)qb * ksel);
+        oracle_order_best_first(srow, ksel, idx + (size_t)qb * ksel);
     }
     if (idx_out)
         memcpy(idx_out, idx, sizeof(int32_t) * (size_t)Nb * ksel);

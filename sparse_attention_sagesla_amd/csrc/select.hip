@@ -4,7 +4,9 @@
 // explainer, news.qq.com, "First key: attention"; 0.1-0.15 recommended in "From
 // training to deployment"). Scores are s_ij = Qbar_i . Kbar_j / sqrt(d) in fp64, the
 // selection key is that score rounded to fp32, and equal keys prefer the lower key
-// index. The kept indices are written in ascending order.
+// index. The kept indices are written in processing order: the best block first
+// (highest key, lowest index on ties), then the others ascending, so that the attention
+// kernel's running maximum starts near its final value.
 #include "common.h"
 
 namespace sagesla {
@@ -15,6 +17,24 @@ constexpr int kSelThreads = 256;
 __device__ __forceinline__ uint32_t ord_key(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* s_u) {
+  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  if ((threadIdx.x & 63) == 0) s_u[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = max(max(s_u[0], s_u[1]), max(s_u[2], s_u[3]));
+  __syncthreads();
+  return x;
+}
+
+__device__ __forceinline__ int block_min_i32(int x, uint32_t* s_u) {
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  if ((threadIdx.x & 63) == 0) s_u[threadIdx.x >> 6] = (uint32_t)x;
+  __syncthreads();
+  x = min(min((int)s_u[0], (int)s_u[1]), min((int)s_u[2], (int)s_u[3]));
+  __syncthreads();
+  return x;
 }
 
 // exclusive prefix sum over the 256 threads of the block; returns this thread's prefix,
@@ -51,6 +71,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
   __shared__ int s_hist[256];
   __shared__ int s_tmp[8];
   __shared__ int s_sel[2];
+  __shared__ uint32_t s_red[4];
 
   const int bh = blockIdx.x / groups, g0 = (blockIdx.x % groups) * R;
   const int nr = min(R, Nb - g0);
@@ -121,8 +142,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
       kk = s_sel[1];
       __syncthreads();
     }
-    // keys > prefix are all kept; of the keys == prefix keep the kk lowest indices
+    // the best block (highest key, lowest index) goes first
     const int j0 = t * per, j1 = min(Nb, j0 + per);
+    uint32_t kmax = 0u;
+    for (int j = j0; j < j1; j++) kmax = max(kmax, keys[j]);
+    kmax = block_max_u32(kmax, s_red);
+    int jb = INT_MAX;
+    for (int j = j0; j < j1; j++)
+      if (keys[j] == kmax) { jb = j; break; }
+    jb = block_min_i32(jb, s_red);
+    // keys > prefix are all kept; of the keys == prefix keep the kk lowest indices
     int n_eq = 0;
     for (int j = j0; j < j1; j++) n_eq += (keys[j] == prefix);
     int tot;
@@ -132,12 +161,15 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
       int e = eq_before;
       for (int j = j0; j < j1; j++) {
         uint32_t u = keys[j];
-        if (u > prefix) n_keep++;
-        else if (u == prefix) { n_keep += (e < kk); e++; }
+        bool keep = false;
+        if (u > prefix) keep = true;
+        else if (u == prefix) { keep = (e < kk); e++; }
+        n_keep += keep && j != jb;
       }
     }
-    int pos = block_excl_scan(n_keep, s_tmp, &tot);
+    int pos = 1 + block_excl_scan(n_keep, s_tmp, &tot);
     int32_t* out = idx + ((size_t)bh * Nb + g0 + r) * ksel;
+    if (t == 0) out[0] = jb;
     {
       int e = eq_before;
       for (int j = j0; j < j1; j++) {
@@ -145,7 +177,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
         bool keep = false;
         if (u > prefix) keep = true;
         else if (u == prefix) { keep = (e < kk); e++; }
-        if (keep) out[pos++] = j;
+        if (keep && j != jb) out[pos++] = j;
       }
     }
     __syncthreads();
@@ -153,7 +185,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
 }
 
 int select_rows_per_group(int Nb) {
-  int R = 32768 / Nb;  // keys of R rows in at most 128 KiB of LDS
+  int R = 16384 / Nb;  // keys of R rows in at most 64 KiB of LDS
   return R < 1 ? 1 : (R > 8 ? 8 : R);
 }
 

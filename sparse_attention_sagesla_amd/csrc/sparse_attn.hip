@@ -10,11 +10,13 @@
 // Per query block i (64 rows) and kept key block j (ascending), for each row:
 //   S = q8 . k8 (int32), a = (s_q[i] * s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
 //   m' = max(m, max float(S)*a), alpha = 2^(m - m'),
-//   w = 2^fma(float(S), a, log2(448) - m')  (= 448 p with p = 2^(x - m')),
-//   l = l*alpha + sum w, P8 = e4m3(w), acc = acc*alpha + P8 . V8.
-// Epilogue: O = acc * s_v / l (+ y), rounded to bf16.
+//   P8 = e4m3(2^fma(float(S), a, log2(448) - m'))  (= e4m3(448 p), p = 2^(x - m')),
+//   l = l*alpha + sum P8, acc = acc*alpha + P8 . V8   (l on the matrix cores too).
+// Epilogue: O = acc * s_v / l (+ y), rounded to bf16: the average of the dequantized V
+// rows weighted by the FP8 probabilities actually used. Kept blocks arrive best first.
 //
 // Work split: one workgroup of 2 waves per (bh, i); wave w owns query rows 32w..32w+31.
+// The K/V code tiles go through an LDS ring filled by direct global-to-LDS loads.
 // S^T = K8 Q8^T is computed so that each lane holds one query and 32 of the 64 keys:
 // the row max and row sum stay in registers plus one exchange with lane l^32, and the
 // probabilities are already in the B-operand layout of O^T = V8^T P8^T (the V8 code
@@ -32,17 +34,106 @@ static float log2e_over_sqrt_d() { return (float)(1.4426950408889634 / sqrt((dou
 
 __device__ __forceinline__ int key_of_slot(int g, int t, int v) { return 32 * t + 8 * (v >> 2) + 4 * g + (v & 3); }
 
-__global__ __launch_bounds__(128) void sparse_attn_kernel(
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Per-wave state of the online softmax for 32 query rows (one per lane pair l, l^32).
+struct RowState {
+  float m;
+  v16f acc[4];  // O^T accumulators (4 tiles of 32 channels)
+  v16f lacc;    // row sums of the FP8 weights (every element holds the same sum)
+};
+
+// Online softmax of one 64-key tile (S^T accumulators) -> FP8 probabilities in the
+// B-operand layout of O^T = V8^T P8^T.
+// MASK: the tile is the partial last block; keys at or past nvalid take no part.
+template <bool MASK>
+__device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a, int g, int nvalid) {
+  if (MASK) {
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int v = 0; v < 16; v++)
+        if (key_of_slot(g, tt, v) >= nvalid) S[tt][v] = INT_MIN;
+  }
+  int mx = INT_MIN;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) mx = max(mx, S[tt][v]);
+  {
+    // the builtin returns unsigned lanes: compare as signed
+    auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    mx = max((int)sw[0], (int)sw[1]);
+  }
+  const float mn = fmaxf(st.m, (float)mx * a);
+  // rescale only when some row's running max moved (alpha == 1 otherwise)
+  if (__builtin_amdgcn_ballot_w64(mn > st.m) != 0) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+#pragma unroll
+    for (int d = 0; d < 4; d++) st.acc[d] *= alpha;
+    st.lacc *= alpha;
+  }
+  st.m = mn;
+  // 448 p = 2^fma(S, a, log2(448) - m'). For the row maximum the fused product may land
+  // a few ulps above log2(448); the FP8 conversion saturates (448, 464] to 448.
+  const float bias = kLog2_448 - mn;
+  v8i pb;
+#pragma unroll
+  for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; v4++) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int sv = S[tt][4 * v4 + e];
+        p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, a, bias));
+        if (MASK && sv == INT_MIN) p[e] = 0.f;
+      }
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+      pb[4 * tt + v4] = wd;
+    }
+  return pb;
+}
+
+// One workgroup of 2 waves per (bh, query block i); wave w owns query rows 32w..32w+31.
+// The K and V code tiles of each kept block are DMA-loaded straight into an LDS ring of
+// two stages (wave 0 the K tile, wave 1 the V tile, 8 x 1 KB each) one block ahead, and
+// both waves read their MFMA operands from there. The loop is unrolled by two so every
+// LDS access names its stage statically, which keeps the reads of the current stage
+// independent of the DMA writing the other one.
+__global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
     const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
     const int32_t* __restrict__ idx, const uint16_t* __restrict__ y, int N, int Nb, int ksel, int tiles,
     int per_xcd, float c0, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kBlkBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kBlkBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kBlkBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_v1[kBlkBytes];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= tiles) return;
   const int bh = tile / Nb, i = tile % Nb;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, r = l & 31;
   const size_t hb = (size_t)bh * Nb;
+  const int32_t* crit = idx + (hb + i) * ksel;
+  // wave 0 streams K code tiles, wave 1 V code tiles
+  const uint8_t* src_base = w == 0 ? (const uint8_t*)k8 : v8;
+  auto issue = [&](uint8_t* dk, uint8_t* dv, int j) {
+    const uint8_t* src = src_base + (hb + j) * kBlkBytes + l * 16;
+    // one LDS object per DMA instruction (wave-uniform branch)
+    if (w == 0) {
+#pragma unroll
+      for (int n = 0; n < 8; n++)
+        __builtin_amdgcn_global_load_lds((const void*)(src + n * 1024), (lds_ptr_t)(dk + n * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 8; n++)
+        __builtin_amdgcn_global_load_lds((const void*)(src + n * 1024), (lds_ptr_t)(dv + n * 1024), 16, 0, 0);
+    }
+  };
 
+  issue(s_k0, s_v0, crit[0]);
   // Q8 B-operand for query tile w: 4 steps of 16 bytes
   v4i qb[4];
   {
@@ -52,26 +143,26 @@ __global__ __launch_bounds__(128) void sparse_attn_kernel(
   }
   const float sqi = sq[hb + i];
   const int nlast = block_len(Nb - 1, N);  // valid keys in the last block
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                    0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  float m = -INFINITY, lsum = 0.f;
-  v16f acc[4];
+  RowState st;
+  st.m = -INFINITY;
 #pragma unroll
-  for (int d = 0; d < 4; d++) acc[d] = (v16f){};
+  for (int d = 0; d < 4; d++) st.acc[d] = (v16f){};
+  st.lacc = (v16f){};
 
-  const int32_t* crit = idx + (hb + i) * ksel;
-  for (int u = 0; u < ksel; u++) {
+  // one kept block: tile in (ck, cv), next block's DMA into (nk, nv)
+  auto step = [&](int u, const uint8_t* ck, const uint8_t* cv, uint8_t* nk, uint8_t* nv) {
     const int j = crit[u];
-    const int8_t* kb = k8 + (hb + j) * kBlkBytes;
-    const uint8_t* vb = v8 + (hb + j) * kBlkBytes;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's tile of block u has landed (and Q)
+    __syncthreads();                // and the other wave's
     v4i ka[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-      for (int s = 0; s < 4; s++) ka[tt][s] = *(const v4i*)(kb + ((tt * 4 + s) * 64 + l) * 16);
-    v8i va[4];
-#pragma unroll
-    for (int d = 0; d < 4; d++) va[d] = *(const v8i*)(vb + (d * 64 + l) * 32);
-
+      for (int s = 0; s < 4; s++) ka[tt][s] = *(const v4i*)(ck + ((tt * 4 + s) * 64 + l) * 16);
+    if (u + 1 < ksel) issue(nk, nv, crit[u + 1]);
     v16i S[2];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {
@@ -79,64 +170,27 @@ __global__ __launch_bounds__(128) void sparse_attn_kernel(
 #pragma unroll
       for (int s = 0; s < 4; s++) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[tt][s], qb[s], S[tt], 0, 0, 0);
     }
-    // keys past N in a partial last block do not take part
-    if (j == Nb - 1 && nlast < kBlk) {
-#pragma unroll
-      for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-        for (int v = 0; v < 16; v++)
-          if (key_of_slot(g, tt, v) >= nlast) S[tt][v] = INT_MIN;
-    }
-    int mx = INT_MIN;
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) mx = max(mx, S[tt][v]);
-    {
-      // the builtin returns unsigned lanes: compare as signed
-      auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
-      mx = max((int)sw[0], (int)sw[1]);
-    }
     const float a = (sqi * sk[hb + j]) * c0;
-    const float mn = fmaxf(m, (float)mx * a);
-    // rescale only when some row's running max moved (alpha == 1 otherwise)
-    if (__builtin_amdgcn_ballot_w64(mn > m) != 0) {
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
-      lsum *= alpha;
+    const v8i pb = (j == Nb - 1 && nlast < kBlk) ? softmax_tile<true>(st, S, a, g, nlast)
+                                                 : softmax_tile<false>(st, S, a, g, kBlk);
 #pragma unroll
-      for (int d = 0; d < 4; d++) acc[d] *= alpha;
+    for (int d = 0; d < 4; d++) {
+      const v8i va = *(const v8i*)(cv + (d * 64 + l) * 32);
+      st.acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, st.acc[d], 0, 0, 0, 0, 0, 0);
     }
-    m = mn;
-    // 448 p = 2^fma(S, a, log2(448) - m'). For the row maximum the fused product may land
-    // a few ulps above log2(448); the FP8 conversion saturates (448, 464] to 448.
-    const float bias = kLog2_448 - mn;
-    v8i pb;
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-      for (int v4 = 0; v4 < 4; v4++) {
-        float p[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const int sv = S[tt][4 * v4 + e];
-          p[e] = sv == INT_MIN ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, a, bias));
-          lsum += p[e];
-        }
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-        pb[4 * tt + v4] = wd;
-      }
-#pragma unroll
-    for (int d = 0; d < 4; d++)
-      acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[d], pb, acc[d], 0, 0, 0, 0, 0, 0);
-  }
+    // row sums of the FP8 weights on the matrix cores
+    st.lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, st.lacc, 0, 0, 0, 0, 0, 0);
+  };
 
-  // epilogue: lsum (the sum of w = 448 p) is split over lanes l and l^32
-  {
-    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum), __float_as_int(lsum), false, false);
-    lsum = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  int u = 0;
+  for (; u + 1 < ksel; u += 2) {
+    step(u, s_k0, s_v0, s_k1, s_v1);
+    step(u + 1, s_k1, s_v1, s_k0, s_v0);
   }
-  const float inv_l = 1.0f / lsum;
+  if (u < ksel) step(u, s_k0, s_v0, s_k1, s_v1);
+
+  // epilogue: every element of lacc holds this query's sum of the FP8 weights
+  const float inv_l = 1.0f / st.lacc[0];
   const int qrow = i * kBlk + 32 * w + r;
   if (qrow < N) {
     uint16_t* orow = out + ((size_t)bh * N + qrow) * kD;
@@ -148,7 +202,7 @@ __global__ __launch_bounds__(128) void sparse_attn_kernel(
         const int c = 32 * d + 8 * v4 + 4 * g;
         float o[4];
 #pragma unroll
-        for (int e = 0; e < 4; e++) o[e] = acc[d][4 * v4 + e] * ((vamax[(size_t)bh * kD + c + e] / 448.0f) * inv_l);
+        for (int e = 0; e < 4; e++) o[e] = st.acc[d][4 * v4 + e] * ((vamax[(size_t)bh * kD + c + e] / 448.0f) * inv_l);
         if (yrow) {
           const uint2 yv = *(const uint2*)(yrow + c);
           o[0] += bf16_to_f32((uint16_t)(yv.x & 0xffff));

@@ -7,9 +7,9 @@
 * The linear branch (SLA's linear-attention half: bonega.ai blog, SLA paragraph;
   tiemojia.cn article, 2.2.1) is checked token by token against
   sum_t phi(q).phi(k_t) v_t / sum_t phi(q).phi(k_t) over the dropped keys.
-* Quantized: rows of the FP8 probability matrix sum to one within the e4m3 bound,
-  V -> 2V doubles the output exactly, token permutations inside a block permute it,
-  and the quantized dense result is close to textbook attention.
+* Quantized: the output is normalised by the sum of the FP8 weights it uses (a constant
+  V comes back exactly), V -> 2V doubles the output exactly, token permutations inside a
+  block permute it, and the quantized dense result is close to textbook attention.
 """
 import numpy as np
 import pytest
@@ -79,10 +79,22 @@ def test_rows_sum_to_one():
     ones = _bits(np.ones((N, 128), np.float32))
     exact = O.sagesla_head(q, k, ones, None, 0.5, quant=False)
     assert np.max(np.abs(exact["out"][:N] - 1.0)) <= 1e-12
+    # quantized: the output is normalised by the sum of the FP8 weights it uses, so a
+    # constant V (code 448, scale 1/448) comes back exactly
     quant = O.sagesla_head(q, k, ones, None, 0.5, quant=True)
-    # each FP8 probability is within 2^-4 relative of p*448 (or 2^-10*... absolute below 2^-6),
-    # so sum dec(p8) / (448 l) stays within 2^-4 of 1
-    assert np.max(np.abs(quant["out"][:N] - 1.0)) <= 2.0 ** -4
+    deq = 448.0 * float(np.float32(1.0) / np.float32(448.0))  # code 448 times scale fp32(1/448)
+    assert np.max(np.abs(quant["out"][:N] - deq)) <= 1e-12
+
+
+def test_constant_v_rows_exact_under_quantization():
+    N = 64 * 5 + 7
+    q, k, _, _ = _rand_head(N, seed=16)
+    u = np.linspace(-3, 3, 128).astype(np.float32)
+    vc = _bits(np.tile(u, (N, 1)))
+    r = O.sagesla_head(q, k, vc, None, 0.3, quant=True)
+    v8, sv = O.quant_v(vc)
+    want = O.e4m3_decode(v8[0]) * sv.astype(np.float64)  # every row is the same dequantized row
+    assert np.max(np.abs(r["out"][:N] - want[None, :])) <= 1e-12
 
 
 def test_quantized_dense_close_to_textbook():

@@ -130,3 +130,18 @@ def test_mask_invariances():
         row = np.sort(s[i])[::-1]
         kk = base.shape[1]
         assert abs(row[kk - 1] - row[kk]) < 1e-9
+
+
+def test_processing_order_best_first_then_ascending():
+    rng = np.random.default_rng(12)
+    for trial in range(50):
+        Nb = int(rng.integers(2, 40))
+        row = rng.normal(size=Nb)
+        if trial % 3 == 0:
+            row = np.round(row * 2) / 2  # ties
+        k = int(rng.integers(1, Nb + 1))
+        kept = O.select(row[None, :], k)[0]
+        got = O.order_best_first(row, kept)
+        best = kept[np.lexsort((kept, -row[kept]))[0]]  # highest score, lowest index
+        assert got[0] == best
+        assert list(got[1:]) == sorted(set(kept.tolist()) - {best})
