@@ -85,7 +85,7 @@ enum {
  * Code layouts (one 64-token block = 8192 bytes; lane l in 0..63, g = l/32, r = l%32):
  *  Q8/K8: byte ((t*4 + s)*64 + l)*16 + e holds row 32*t + r, channel 64*g + 16*s + e
  *         (t in 0..1, s in 0..3, e in 0..15); rows past N are 0.
- *  V8:    byte (dt*64 + l)*32 + e holds channel 32*dt + r of token
+ *  V8:    byte ((dt*2 + e/16)*64 + l)*16 + e%16 holds channel 32*dt + r of token
  *         32*(e/16) + 8*((e%16)/4) + 4*g + e%4 (dt in 0..3, e in 0..31); rows past N are 0.
  * H_j[a][c] = sum_t phi(k_t)[a] v_t[c], z_j[a] = sum_t phi(k_t)[a] over the tokens of block j.
  * Nc = ceil(Nb/16) partial sums; Ng = ceil(Nb/128) query-block groups.

@@ -49,13 +49,14 @@ __device__ __forceinline__ int qk_code_offset(int row, int ch) {
 }
 
 // Byte offset of (token, channel) of a 64x128 FP8 V block in MFMA operand order:
-// (dt*64 + lane)*32 + e with dt = ch/32, r = ch%32, and the token decomposed as
-// token = 32*(e/16) + 8*((e%16)/4) + 4*g + e%4, lane = 32*g + r.
+// ((dt*2 + e/16)*64 + lane)*16 + e%16 with dt = ch/32, r = ch%32, lane = 32*g + r, where
+// the token is decomposed as token = 32*(e/16) + 8*((e%16)/4) + 4*g + e%4 (e in 0..31:
+// the operand's 32 bytes, stored as two lane-contiguous 16-byte halves).
 __device__ __forceinline__ int v_code_offset(int tok, int ch) {
   int dt = ch >> 5, r = ch & 31;
   int t = tok >> 5, rem = tok & 31, a = rem >> 3, g = (rem >> 2) & 1, b = rem & 3;
   int e = 16 * t + 4 * a + b;
-  return (dt * 64 + (g * 32 + r)) * 32 + e;
+  return ((dt * 2 + (e >> 4)) * 64 + (g * 32 + r)) * 16 + (e & 15);
 }
 
 // XCD-aware tile order: consecutive workgroup ids go round-robin over the 8 XCDs, so

@@ -38,9 +38,8 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Per-wave state of the online softmax for 32 query rows (one per lane pair l, l^32).
 struct RowState {
-  float m;
+  float m, l;   // running max and running sum of the FP8 weights
   v16f acc[4];  // O^T accumulators (4 tiles of 32 channels)
-  v16f lacc;    // row sums of the FP8 weights (every element holds the same sum)
 };
 
 // Online softmax of one 64-key tile (S^T accumulators) -> FP8 probabilities in the
@@ -71,7 +70,7 @@ __device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a,
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
 #pragma unroll
     for (int d = 0; d < 4; d++) st.acc[d] *= alpha;
-    st.lacc *= alpha;
+    st.l *= alpha;
   }
   st.m = mn;
   // 448 p = 2^fma(S, a, log2(448) - m'). For the row maximum the fused product may land
@@ -100,8 +99,7 @@ __device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a,
 // The K and V code tiles of each kept block are DMA-loaded straight into an LDS ring of
 // two stages (wave 0 the K tile, wave 1 the V tile, 8 x 1 KB each) one block ahead, and
 // both waves read their MFMA operands from there. The loop is unrolled by two so every
-// LDS access names its stage statically, which keeps the reads of the current stage
-// independent of the DMA writing the other one.
+// LDS access names its stage statically; all LDS reads of a step precede its DMA.
 __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
     const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
@@ -114,7 +112,8 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= tiles) return;
   const int bh = tile / Nb, i = tile % Nb;
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, g = l >> 5, r = l & 31;
+  const int t = threadIdx.x, l = t & 63, g = l >> 5, r = l & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
   const size_t hb = (size_t)bh * Nb;
   const int32_t* crit = idx + (hb + i) * ksel;
   // wave 0 streams K code tiles, wave 1 V code tiles
@@ -143,25 +142,35 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   }
   const float sqi = sq[hb + i];
   const int nlast = block_len(Nb - 1, N);  // valid keys in the last block
-  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                    0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
   RowState st;
   st.m = -INFINITY;
+  st.l = 0.f;
 #pragma unroll
   for (int d = 0; d < 4; d++) st.acc[d] = (v16f){};
-  st.lacc = (v16f){};
+
+  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                    0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
   // one kept block: tile in (ck, cv), next block's DMA into (nk, nv)
   auto step = [&](int u, const uint8_t* ck, const uint8_t* cv, uint8_t* nk, uint8_t* nv) {
     const int j = crit[u];
     __builtin_amdgcn_s_waitcnt(0);  // this wave's tile of block u has landed (and Q)
     __syncthreads();                // and the other wave's
+    // every LDS read of this block precedes the next block's DMA, so no read waits on it
     v4i ka[2][4];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
       for (int s = 0; s < 4; s++) ka[tt][s] = *(const v4i*)(ck + ((tt * 4 + s) * 64 + l) * 16);
+    v8i va[4];
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      // V operand: two lane-contiguous 16-byte halves (conflict-free LDS reads)
+      const v4i lo = *(const v4i*)(cv + ((2 * d) * 64 + l) * 16);
+      const v4i hi = *(const v4i*)(cv + ((2 * d + 1) * 64 + l) * 16);
+      va[d] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
     if (u + 1 < ksel) issue(nk, nv, crit[u + 1]);
     v16i S[2];
 #pragma unroll
@@ -174,12 +183,12 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     const v8i pb = (j == Nb - 1 && nlast < kBlk) ? softmax_tile<true>(st, S, a, g, nlast)
                                                  : softmax_tile<false>(st, S, a, g, kBlk);
 #pragma unroll
-    for (int d = 0; d < 4; d++) {
-      const v8i va = *(const v8i*)(cv + (d * 64 + l) * 32);
-      st.acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pb, st.acc[d], 0, 0, 0, 0, 0, 0);
-    }
-    // row sums of the FP8 weights on the matrix cores
-    st.lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, st.lacc, 0, 0, 0, 0, 0, 0);
+    for (int d = 0; d < 4; d++)
+      st.acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[d], pb, st.acc[d], 0, 0, 0, 0, 0, 0);
+    // this block's row sums of the FP8 weights on the matrix cores (every element of
+    // the tile holds the sum for the lane's query)
+    const v16f lblk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, (v16f){}, 0, 0, 0, 0, 0, 0);
+    st.l += lblk[0];
   };
 
   int u = 0;
@@ -189,8 +198,7 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   }
   if (u < ksel) step(u, s_k0, s_v0, s_k1, s_v1);
 
-  // epilogue: every element of lacc holds this query's sum of the FP8 weights
-  const float inv_l = 1.0f / st.lacc[0];
+  const float inv_l = 1.0f / st.l;
   const int qrow = i * kBlk + 32 * w + r;
   if (qrow < N) {
     uint16_t* orow = out + ((size_t)bh * N + qrow) * kD;

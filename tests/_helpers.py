@@ -14,14 +14,15 @@ def _qk_map():
 
 
 def _v_map():
-    # byte (dt*64 + lane)*32 + e  <->  channel 32dt + r of token 32(e/16) + 8((e%16)/4) + 4g + e%4
+    # byte ((dt*2 + e/16)*64 + lane)*16 + e%16  <->  channel 32dt + r of token
+    # 32(e/16) + 8((e%16)/4) + 4g + e%4
     m = np.empty((64, 128), np.int64)
     for dt in range(4):
         for lane in range(64):
             g, r = lane // 32, lane % 32
             for e in range(32):
                 tok = 32 * (e // 16) + 8 * ((e % 16) // 4) + 4 * g + e % 4
-                m[tok, 32 * dt + r] = (dt * 64 + lane) * 32 + e
+                m[tok, 32 * dt + r] = ((dt * 2 + e // 16) * 64 + lane) * 16 + e % 16
     return m
 
 
