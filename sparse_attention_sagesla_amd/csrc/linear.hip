@@ -82,7 +82,15 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------- masked sum on MFMA
 
-constexpr int kBs = 40;  // LDS row stride (bf16) of the transposed state tile: 80 B
+constexpr int kBp = 144;  // LDS row pitch (bf16) of the [state][column] tile: 288 B (bank spread)
+typedef short v4s_ __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
+
+// gfx950 transposing LDS read: within each group of 16 lanes, lanes 4a..4a+3 each name
+// 4 consecutive 16-bit elements of row a of a 4 x 16 tile, and lane j receives column j.
+__device__ __forceinline__ v4s_ lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
+}
 
 // Per (bh, group, state row c in 0..128): for the group's 128 query blocks i,
 //   hc[i][c][a] = htot[c][a] - sum_u C[i][u] S_{union[u]}[c][a]   (a = 0..127)
@@ -93,9 +101,12 @@ __global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
     const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
     const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
     uint16_t* __restrict__ hc) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kD * kBs];
+  // operand tiles during the K-loop, then (after the last barrier) the output tile
+  __shared__ __attribute__((aligned(16))) uint16_t s_raw[kGroup * kD];
   __shared__ uint32_t s_m[2][32][4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[kGroup * kD];
+  uint16_t (*s_b)[32 * kBp] = reinterpret_cast<uint16_t (*)[32 * kBp]>(s_raw);
+  uint16_t* s_out = s_raw;
+  static_assert(2 * 32 * kBp <= kGroup * kD, "operand tiles must fit in the output tile");
 
   const int per_bh = ngroups * 129;
   const int bh = blockIdx.x / per_bh, rem = blockIdx.x % per_bh;
@@ -114,7 +125,8 @@ __global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
 
   const int nsteps = (U + 31) / 32;
   // 32 states x 128 columns per step: thread t holds 16 B (8 columns) of states t/16 and
-  // t/16 + 16, loaded a step ahead and written transposed ([column][state]) into LDS.
+  // t/16 + 16, loaded a step ahead and stored row-major ([state][column]) into LDS; the
+  // MFMA B operand (8 consecutive states of one column) comes from transposing reads.
   uint4 pre[2];
   uint32_t pmask = 0u;
   auto load = [&](int step) {
@@ -133,9 +145,7 @@ __global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       const int k = (t >> 4) + 16 * h, ch = t & 15;
-      const uint16_t* vh = (const uint16_t*)&pre[h];
-#pragma unroll
-      for (int x = 0; x < 8; x++) s_b[buf][(ch * 8 + x) * kBs + k] = vh[x];
+      *(uint4*)(&s_b[buf][k * kBp + ch * 8]) = pre[h];
     }
     if (t < 128) s_m[buf][t >> 2][t & 3] = pmask;
   };
@@ -155,9 +165,14 @@ __global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
 #pragma unroll
       for (int x = 0; x < 8; x++) a[m][x] = ((s_m[buf][8 * kg + x][w] >> bit) & 1u) ? (short)0x3F80 : (short)0;
     }
+    // lane (kg, l16): states 8kg..8kg+7 of column 16n + l16, as two 4 x 16 transposes
+    const int ta = l16 >> 2, tb = l16 & 3;
 #pragma unroll
     for (int n = 0; n < 8; n++) {
-      const v8bf b = *(const v8bf*)(&s_b[buf][(16 * n + l16) * kBs + 8 * kg]);
+      const v4s_ r0 = lds_read_tr16(&s_b[buf][(8 * kg + ta) * kBp + 16 * n + 4 * tb]);
+      const v4s_ r1 = lds_read_tr16(&s_b[buf][(8 * kg + 4 + ta) * kBp + 16 * n + 4 * tb]);
+      const v8s bs = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+      const v8bf b = __builtin_bit_cast(v8bf, bs);
 #pragma unroll
       for (int m = 0; m < 2; m++)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[m]), b, acc[m][n], 0, 0, 0);

@@ -101,21 +101,35 @@ __global__ __launch_bounds__(256) void pool_kernel(
 }
 
 // Per head: K channel mean over all N tokens (fp64 sum of block sums, rounded to fp32)
-// and V channel max |v|. One workgroup of 128 threads per head.
-__global__ __launch_bounds__(128) void head_stats_kernel(const double* __restrict__ ksum,
+// and V channel max |v|. 16 workgroups per head, each 8 channels x 32 block-strided
+// parts, reduced in a fixed order (the block sums are exact, so is their sum).
+__global__ __launch_bounds__(256) void head_stats_kernel(const double* __restrict__ ksum,
                                                          const float* __restrict__ vamax_blk, int N,
                                                          int Nb, float* __restrict__ kmean,
                                                          float* __restrict__ vamax) {
-  const int bh = blockIdx.x, c = threadIdx.x;
+  __shared__ double s_s[32][8];
+  __shared__ float s_m[32][8];
+  const int bh = blockIdx.x >> 4, c = (blockIdx.x & 15) * 8 + (threadIdx.x & 7), part = threadIdx.x >> 3;
   double s = 0.0;
   float mx = 0.f;
-  for (int i = 0; i < Nb; i++) {
+  for (int i = part; i < Nb; i += 32) {
     size_t o = ((size_t)bh * Nb + i) * kD + c;
     s += ksum[o];
     mx = fmaxf(mx, vamax_blk[o]);
   }
-  kmean[(size_t)bh * kD + c] = (float)(s / N);
-  vamax[(size_t)bh * kD + c] = mx;
+  s_s[part][threadIdx.x & 7] = s;
+  s_m[part][threadIdx.x & 7] = mx;
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    double tot = 0.0;
+    float m = 0.f;
+    for (int p = 0; p < 32; p++) {
+      tot += s_s[p][threadIdx.x];
+      m = fmaxf(m, s_m[p][threadIdx.x]);
+    }
+    kmean[(size_t)bh * kD + c] = (float)(tot / N);
+    vamax[(size_t)bh * kD + c] = m;
+  }
 }
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int BH, int N, int Nb, void* qbar,
@@ -128,7 +142,7 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, int BH, int 
 
 hipError_t launch_head_stats(const void* ksum, const void* vamax_blk, int BH, int N, int Nb,
                              void* kmean, void* vamax, hipStream_t st) {
-  hipLaunchKernelGGL(head_stats_kernel, dim3(BH), dim3(kD), 0, st, (const double*)ksum,
+  hipLaunchKernelGGL(head_stats_kernel, dim3(BH * 16), dim3(256), 0, st, (const double*)ksum,
                      (const float*)vamax_blk, N, Nb, (float*)kmean, (float*)vamax);
   return hipGetLastError();
 }
