@@ -19,59 +19,17 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t x, uint32_t* s_u) {
-  for (int o = 32; o > 0; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  if ((threadIdx.x & 63) == 0) s_u[threadIdx.x >> 6] = x;
-  __syncthreads();
-  x = max(max(s_u[0], s_u[1]), max(s_u[2], s_u[3]));
-  __syncthreads();
-  return x;
-}
-
-__device__ __forceinline__ int block_min_i32(int x, uint32_t* s_u) {
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  if ((threadIdx.x & 63) == 0) s_u[threadIdx.x >> 6] = (uint32_t)x;
-  __syncthreads();
-  x = min(min((int)s_u[0], (int)s_u[1]), min((int)s_u[2], (int)s_u[3]));
-  __syncthreads();
-  return x;
-}
-
-// exclusive prefix sum over the 256 threads of the block; returns this thread's prefix,
-// *total receives the block total. Uses s_tmp[4 + 1].
-__device__ __forceinline__ int block_excl_scan(int x, int* s_tmp, int* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int incl = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  if (lane == 63) s_tmp[w] = incl;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int k = 0; k < 4; k++) {
-    int c = s_tmp[k];
-    if (k < w) off += c;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + incl - x;
-}
-
-// R query blocks of one head per workgroup. Dynamic LDS: keys [R][Nb] uint32.
+// R query blocks of one head per workgroup (4 waves). Dynamic LDS: keys [R][Nb] uint32.
+// Phase 1: all threads score the R rows against every key block (4 key blocks per
+// thread in flight). Phase 2: one wave per row selects, with a wave-private histogram
+// and ballots (no workgroup barriers).
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __restrict__ qbar,
                                                              const double* __restrict__ kbart, int Nb,
                                                              int ksel, int R, int groups,
                                                              int32_t* __restrict__ idx) {
   extern __shared__ uint32_t s_keys[];  // [R][Nb]
   __shared__ double s_qb[8][kD];
-  __shared__ int s_hist[256];
-  __shared__ int s_tmp[8];
-  __shared__ int s_sel[2];
-  __shared__ uint32_t s_red[4];
+  __shared__ uint32_t s_hist[4][256];
 
   const int bh = blockIdx.x / groups, g0 = (blockIdx.x % groups) * R;
   const int nr = min(R, Nb - g0);
@@ -80,107 +38,119 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
     s_qb[e / kD][e % kD] = qbar[((size_t)bh * Nb + g0 + e / kD) * kD + e % kD];
   __syncthreads();
 
-  // scores: thread per key block j, R rows at once; kbart is channel-major so the
-  // loads of consecutive threads are contiguous.
+  // ---- phase 1: scores (fp64, channel order fixed), keys = order-preserving fp32 bits
   const double inv_sqrt_d = 1.0 / sqrt((double)kD);
   const double* kb = kbart + (size_t)bh * kD * Nb;
-  for (int j = t; j < Nb; j += kSelThreads) {
-    double acc[8];
+  constexpr int JT = 4;
+  for (int j0 = t; j0 < Nb; j0 += kSelThreads * JT) {
+    double acc[JT][8];
 #pragma unroll
-    for (int r = 0; r < 8; r++) acc[r] = 0.0;
+    for (int q = 0; q < JT; q++)
+#pragma unroll
+      for (int r = 0; r < 8; r++) acc[q][r] = 0.0;
+#pragma unroll 4
     for (int c = 0; c < kD; c++) {
-      double kv = kb[(size_t)c * Nb + j];
+      double kv[JT];
 #pragma unroll
-      for (int r = 0; r < 8; r++)
-        if (r < nr) acc[r] = __fma_rn(s_qb[r][c], kv, acc[r]);
+      for (int q = 0; q < JT; q++) {
+        const int j = j0 + q * kSelThreads;
+        kv[q] = j < Nb ? kb[(size_t)c * Nb + j] : 0.0;
+      }
+#pragma unroll
+      for (int r = 0; r < 8; r++) {
+        const double qv = s_qb[r][c];
+#pragma unroll
+        for (int q = 0; q < JT; q++) acc[q][r] = __fma_rn(qv, kv[q], acc[q][r]);
+      }
     }
 #pragma unroll
-    for (int r = 0; r < 8; r++)
-      if (r < nr) s_keys[r * Nb + j] = ord_key((float)(acc[r] * inv_sqrt_d));
+    for (int q = 0; q < JT; q++) {
+      const int j = j0 + q * kSelThreads;
+      if (j < Nb) {
+#pragma unroll
+        for (int r = 0; r < 8; r++)
+          if (r < nr) s_keys[r * Nb + j] = ord_key((float)(acc[q][r] * inv_sqrt_d));
+      }
+    }
   }
   __syncthreads();
 
-  const int per = (Nb + kSelThreads - 1) / kSelThreads;  // contiguous range per thread
-  for (int r = 0; r < nr; r++) {
+  // ---- phase 2: one wave per row
+  const int lane = t & 63, w = t >> 6;
+  uint32_t* hist = s_hist[w];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int r = w; r < nr; r += 4) {
     const uint32_t* keys = s_keys + r * Nb;
     // radix select (4 x 8 bits, most significant first) of the ksel-th largest key
     uint32_t prefix = 0, mask = 0;
     int kk = ksel;
     for (int pass = 0; pass < 4; pass++) {
       const int shift = 24 - 8 * pass;
-      s_hist[t] = 0;
-      __syncthreads();
-      for (int j = t; j < Nb; j += kSelThreads) {
-        uint32_t u = keys[j];
-        if ((u & mask) == prefix) atomicAdd(&s_hist[(u >> shift) & 255], 1);
-      }
-      __syncthreads();
-      if (t < 64) {
-        // lane t owns bins 4t..4t+3; suffix sums from the top bin down
-        int h0 = s_hist[4 * t], h1 = s_hist[4 * t + 1], h2 = s_hist[4 * t + 2], h3 = s_hist[4 * t + 3];
-        int loc = h0 + h1 + h2 + h3;
-        int suf = loc;  // inclusive suffix over lanes >= t
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          int y = __shfl_down(suf, o);
-          if (t + o < 64) suf += y;
-        }
-        int above = suf - loc;  // keys in bins above this lane's four
-        int hs[4] = {h0, h1, h2, h3};
-#pragma unroll
-        for (int b = 3; b >= 0; b--) {
-          if (above < kk && above + hs[b] >= kk) {
-            s_sel[0] = 4 * t + b;
-            s_sel[1] = kk - above;
-          }
-          above += hs[b];
-        }
+      for (int b = 0; b < 4; b++) hist[4 * lane + b] = 0u;
+      // the wave's LDS operations execute in order; keep the compiler from moving them
+      __builtin_amdgcn_wave_barrier();
+      for (int j = lane; j < Nb; j += 64) {
+        const uint32_t u = keys[j];
+        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
       }
-      __syncthreads();
-      prefix |= (uint32_t)s_sel[0] << shift;
+      __builtin_amdgcn_wave_barrier();
+      // lane owns bins 4*lane .. 4*lane+3; suffix counts from the top bin down
+      const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+      const int loc = h0 + h1 + h2 + h3;
+      int suf = loc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_down(suf, o);
+        if (lane + o < 64) suf += y;
+      }
+      int above = suf - loc;
+      const int hs[4] = {h0, h1, h2, h3};
+      int sel_bin = -1, sel_k = 0;
+#pragma unroll
+      for (int b = 3; b >= 0; b--) {
+        if (above < kk && above + hs[b] >= kk) {
+          sel_bin = 4 * lane + b;
+          sel_k = kk - above;
+        }
+        above += hs[b];
+      }
+      const unsigned long long who = __ballot(sel_bin >= 0);
+      const int src = __ffsll((long long)who) - 1;
+      sel_bin = __shfl(sel_bin, src);
+      sel_k = __shfl(sel_k, src);
+      prefix |= (uint32_t)sel_bin << shift;
       mask |= 255u << shift;
-      kk = s_sel[1];
-      __syncthreads();
+      kk = sel_k;
+      __builtin_amdgcn_wave_barrier();
     }
-    // the best block (highest key, lowest index) goes first
-    const int j0 = t * per, j1 = min(Nb, j0 + per);
+    // best block: highest key, lowest index
     uint32_t kmax = 0u;
-    for (int j = j0; j < j1; j++) kmax = max(kmax, keys[j]);
-    kmax = block_max_u32(kmax, s_red);
+    for (int j = lane; j < Nb; j += 64) kmax = max(kmax, keys[j]);
+    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
     int jb = INT_MAX;
-    for (int j = j0; j < j1; j++)
-      if (keys[j] == kmax) { jb = j; break; }
-    jb = block_min_i32(jb, s_red);
-    // keys > prefix are all kept; of the keys == prefix keep the kk lowest indices
-    int n_eq = 0;
-    for (int j = j0; j < j1; j++) n_eq += (keys[j] == prefix);
-    int tot;
-    int eq_before = block_excl_scan(n_eq, s_tmp, &tot);
-    int n_keep = 0;
-    {
-      int e = eq_before;
-      for (int j = j0; j < j1; j++) {
-        uint32_t u = keys[j];
-        bool keep = false;
-        if (u > prefix) keep = true;
-        else if (u == prefix) { keep = (e < kk); e++; }
-        n_keep += keep && j != jb;
-      }
+    for (int j0 = 0; j0 < Nb && jb == INT_MAX; j0 += 64) {
+      const int j = j0 + lane;
+      const unsigned long long hit = __ballot(j < Nb && keys[j] == kmax);
+      if (hit) jb = j0 + __ffsll((long long)hit) - 1;
     }
-    int pos = 1 + block_excl_scan(n_keep, s_tmp, &tot);
+    // keys > prefix are kept; of the keys == prefix the kk lowest indices; ascending
+    // after the best block
     int32_t* out = idx + ((size_t)bh * Nb + g0 + r) * ksel;
-    if (t == 0) out[0] = jb;
-    {
-      int e = eq_before;
-      for (int j = j0; j < j1; j++) {
-        uint32_t u = keys[j];
-        bool keep = false;
-        if (u > prefix) keep = true;
-        else if (u == prefix) { keep = (e < kk); e++; }
-        if (keep && j != jb) out[pos++] = j;
-      }
+    if (lane == 0) out[0] = jb;
+    int pos = 1, eq_seen = 0;
+    for (int j0 = 0; j0 < Nb; j0 += 64) {
+      const int j = j0 + lane;
+      const uint32_t u = j < Nb ? keys[j] : 0u;
+      const bool eq = j < Nb && u == prefix;
+      const unsigned long long eqm = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(eqm & below);
+      const bool keep = j < Nb && (u > prefix || (eq && eq_rank < kk)) && j != jb;
+      const unsigned long long km = __ballot(keep);
+      if (keep) out[pos + __popcll(km & below)] = j;
+      pos += __popcll(km);
+      eq_seen += __popcll(eqm);
     }
-    __syncthreads();
   }
 }
 

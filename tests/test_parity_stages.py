@@ -73,9 +73,15 @@ def test_stage_parity(name):
         assert np.array_equal(v8[:N], qz["v8"]) and np.all(v8[N:] == 0)
         # selection
         sc = O.scores(qbar, kbar)
-        ora_idx = O.select(sc, ksel)
+        ora_idx = np.stack([O.order_best_first(sc[i], row) for i, row in enumerate(O.select(sc, ksel))])
         flips = mask_mismatch(g["idx"][bh], ora_idx, sc)
         assert len(flips) <= max(1, Nb // 50)
+        # processing order: best block first (up to near-ties), then strictly ascending
+        for i in range(Nb):
+            gi = g["idx"][bh][i]
+            assert np.all(np.diff(gi[1:]) > 0)
+            if i not in flips and gi[0] != ora_idx[i][0]:
+                assert abs(sc[i][gi[0]] - sc[i][ora_idx[i][0]]) < 1e-5
         if linear:
             H, z = O.linear_states(k, v)
             # S_j = [H_j^T ; z_j] in bf16: each element within half a bf16 ulp (+ fp32 slack)
