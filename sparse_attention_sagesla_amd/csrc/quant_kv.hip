@@ -18,161 +18,206 @@
 namespace sagesla {
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v4s_ __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
 
-constexpr int kTs = 72;  // LDS row stride (bf16) of the transposed tiles: 144 B, 16-B aligned
+constexpr int kTp = 144;  // LDS row pitch (bf16) of the [token][channel] tiles: 288 B (bank spread)
 
-// One workgroup (256 threads, 4 waves) per (bh, chunk of 16 key blocks).
-__global__ __launch_bounds__(256) void quant_kv_kernel(
+// gfx950 transposing LDS read: within each group of 16 lanes, lanes 4a..4a+3 each name
+// 4 consecutive 16-bit elements of row a of a 4 x 16 tile, and lane j receives column j.
+__device__ __forceinline__ v4s_ lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
+}
+
+// 8 consecutive tokens t0..t0+7 of channel column (16-lane group base c0 + lane%16) of a
+// row-major [token][channel] bf16 tile: the K=8 slice of a bf16 MFMA operand.
+__device__ __forceinline__ v8bf tile_col8(const uint16_t* tile, int t0, int c0, int lane) {
+  const int j = lane & 15, a = j >> 2, b = j & 3;
+  const v4s_ r0 = lds_read_tr16(tile + (t0 + a) * kTp + c0 + 4 * b);
+  const v4s_ r1 = lds_read_tr16(tile + (t0 + 4 + a) * kTp + c0 + 4 * b);
+  const v8s v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(v8bf, v);
+}
+
+constexpr int kQkThreads = 512;
+
+// One workgroup (512 threads, 8 waves) per (bh, chunk of 16 key blocks). Thread t
+// covers rows t/16 + 32m (m = 0, 1) and channels 8*(t%16) .. +7 of each block. In the
+// state product wave w owns rows c in [32(w%4), +32) and column tiles 2(w/4), 2(w/4)+1.
+__global__ __launch_bounds__(kQkThreads) void quant_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ kmean,
     const float* __restrict__ vamax, int N, int Nb, int Nc, int8_t* __restrict__ k8,
     float* __restrict__ sk, uint8_t* __restrict__ v8, uint16_t* __restrict__ hs,
     float* __restrict__ hpart) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_v8[kBlkBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t s_phi_hi[kD * kTs];
-  __shared__ __attribute__((aligned(16))) uint16_t s_phi_lo[kD * kTs];
-  __shared__ __attribute__((aligned(16))) uint16_t s_vt[kD * kTs];
-  __shared__ float s_z[16][kD];
-  __shared__ float s_amax[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[kBlk * kTp];       // V (bf16), [token][channel]
+  __shared__ __attribute__((aligned(16))) uint16_t s_phi[2][kBlk * kTp];  // phi(K) hi, lo parts
+  __shared__ float s_z[8][kD];
+  __shared__ float s_amax[8];
 
   const int bh = blockIdx.x / Nc, chunk = blockIdx.x % Nc;
   const int t = threadIdx.x, rg = t >> 4, ch = t & 15;
-  const int lane = t & 63, w = t >> 6, g = lane >> 5, r = lane & 31;
+  const int lane = t & 63, g = lane >> 5, r = lane & 31, hl = (lane >> 4) & 1;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wr = w & 3, wc = w >> 2;
   const bool states = hs != nullptr;
 
-  float mu[8], inv_v[8];
+  float mu[8];
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    mu[e] = kmean[(size_t)bh * kD + ch * 8 + e];
-    float am = vamax[(size_t)bh * kD + ch * 8 + e];
-    inv_v[e] = am > 0.f ? 448.0f / am : 0.f;
-  }
+  for (int e = 0; e < 8; e++) mu[e] = kmean[(size_t)bh * kD + ch * 8 + e];
+  // V code chunk (dt, half) = (w/2, w%2); the lane's channel is 32*dt + r
+  const int vdt = w >> 1, vhalf = w & 1;
+  const float am_v = vamax[(size_t)bh * kD + 32 * vdt + r];
+  const float inv_v = am_v > 0.f ? 448.0f / am_v : 0.f;
 
-  v16f part[4];
+  v16f part[2];
   float zp = 0.f;
-#pragma unroll
-  for (int c = 0; c < 4; c++) part[c] = (v16f){};
+  part[0] = (v16f){};
+  part[1] = (v16f){};
 
   const int j0 = chunk * kChunk, j1 = min(Nb, j0 + kChunk);
   for (int j = j0; j < j1; j++) {
     const int n = block_len(j, N);
     const size_t base = ((size_t)bh * N + (size_t)j * kBlk) * kD;
-    float kr[4][8], vr[4][8];
+    uint4 kraw[2];
     float amax = 0.f;
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      int row = rg + 16 * m;
-      uint4 ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
+    for (int m = 0; m < 2; m++) {
+      const int row = rg + 32 * m;
+      uint4 vraw = make_uint4(0, 0, 0, 0);
+      kraw[m] = make_uint4(0, 0, 0, 0);
       if (row < n) {
-        size_t off = base + (size_t)row * kD + ch * 8;
-        ka = *(const uint4*)(k + off);
-        va = *(const uint4*)(v + off);
+        const size_t off = base + (size_t)row * kD + ch * 8;
+        kraw[m] = *(const uint4*)(k + off);
+        vraw = *(const uint4*)(v + off);
       }
-      const uint16_t* kh = (const uint16_t*)&ka;
-      const uint16_t* vh = (const uint16_t*)&va;
+      // V row-major into LDS for the V codes and the state product (zeros past N)
+      *(uint4*)(s_v + row * kTp + ch * 8) = vraw;
+      const uint16_t* kh = (const uint16_t*)&kraw[m];
+      if (row < n) {
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        kr[m][e] = bf16_to_f32(kh[e]);
-        vr[m][e] = bf16_to_f32(vh[e]);
-        if (row < n) amax = fmaxf(amax, fabsf(kr[m][e] - mu[e]));
+        for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf(bf16_to_f32(kh[e]) - mu[e]));
       }
     }
     for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
     if (lane == 0) s_amax[w] = amax;
-    // V codes into LDS in operand order
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      int row = rg + 16 * m;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        int pk = 0;
-        if (row < n) pk = __builtin_amdgcn_cvt_pk_fp8_f32(vr[m][e] * inv_v[e], vr[m][e + 1] * inv_v[e + 1], 0, false);
-        s_v8[v_code_offset(row, ch * 8 + e)] = (uint8_t)(pk & 0xff);
-        s_v8[v_code_offset(row, ch * 8 + e + 1)] = (uint8_t)((pk >> 8) & 0xff);
-      }
-    }
-    __syncthreads();
-    amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
-    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    if (t == 0) sk[(size_t)bh * Nb + j] = amax > 0.f ? amax / 127.0f : 0.f;
-    int8_t* kdst = k8 + ((size_t)bh * Nb + j) * kBlkBytes;
-#pragma unroll
-    for (int m = 0; m < 4; m++) {
-      int row = rg + 16 * m;
-      uint32_t lo = 0, hi = 0;
-      if (row < n) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q_int8(kr[m][e] - mu[e], inv) << (8 * e);
-#pragma unroll
-        for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q_int8(kr[m][e + 4] - mu[e + 4], inv) << (8 * e);
-      }
-      *(uint2*)(kdst + qk_code_offset(row, ch * 8)) = make_uint2(lo, hi);
-    }
-    {
-      uint8_t* vdst = v8 + ((size_t)bh * Nb + j) * kBlkBytes;
-      *(uint4*)(vdst + t * 32) = *(const uint4*)(s_v8 + t * 32);
-      *(uint4*)(vdst + t * 32 + 16) = *(const uint4*)(s_v8 + t * 32 + 16);
-    }
+    // phi = softmax over channels of each raw K row (16 lanes share a row)
     if (states) {
-      // phi = softmax over channels of each raw K row (16 lanes share a row)
       float zc[8];
 #pragma unroll
       for (int e = 0; e < 8; e++) zc[e] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 4; m++) {
-        int row = rg + 16 * m;
-        float mx = kr[m][0];
+      for (int m = 0; m < 2; m++) {
+        const int row = rg + 32 * m;
+        const uint16_t* kh = (const uint16_t*)&kraw[m];
+        float x[8];
 #pragma unroll
-        for (int e = 1; e < 8; e++) mx = fmaxf(mx, kr[m][e]);
+        for (int e = 0; e < 8; e++) x[e] = bf16_to_f32(kh[e]);
+        float mx = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; e++) mx = fmaxf(mx, x[e]);
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-        float ex[8], s = 0.f;
+        float ssum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) { ex[e] = expf(kr[m][e] - mx); s += ex[e]; }
+        for (int e = 0; e < 8; e++) { x[e] = expf(x[e] - mx); ssum += x[e]; }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+        for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+        uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          float ph = row < n ? ex[e] / s : 0.f;
-          zc[e] += ph;
-          uint16_t hb = f32_to_bf16(ph);
-          uint16_t lb = f32_to_bf16(ph - bf16_to_f32(hb));
-          int c = ch * 8 + e;
-          s_phi_hi[c * kTs + row] = hb;
-          s_phi_lo[c * kTs + row] = lb;
-          s_vt[c * kTs + row] = row < n ? f32_to_bf16(vr[m][e]) : (uint16_t)0;
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = row < n ? x[e] / ssum : 0.f, p1 = row < n ? x[e + 1] / ssum : 0.f;
+          zc[e] += p0;
+          zc[e + 1] += p1;
+          const uint16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
+          const uint16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0)), l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
+          hw[e / 2] = h0 | ((uint32_t)h1 << 16);
+          lw[e / 2] = l0 | ((uint32_t)l1 << 16);
         }
+        *(uint4*)(s_phi[0] + row * kTp + ch * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+        *(uint4*)(s_phi[1] + row * kTp + ch * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
       }
+      // the wave's 4 row groups share channels: reduce over lanes ch, ch+16, ch+32, ch+48
 #pragma unroll
-      for (int e = 0; e < 8; e++) s_z[rg][ch * 8 + e] = zc[e];
-      __syncthreads();
+      for (int e = 0; e < 8; e++) {
+        zc[e] += __shfl_xor(zc[e], 16);
+        zc[e] += __shfl_xor(zc[e], 32);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; e++) s_z[w][ch * 8 + e] = zc[e];
+      }
+    }
+    __syncthreads();
+    // K: smoothed INT8 codes with one scale per block
+    amax = s_amax[0];
+#pragma unroll
+    for (int q = 1; q < 8; q++) amax = fmaxf(amax, s_amax[q]);
+    const float inv = amax > 0.f ? 127.0f / amax : 0.f;
+    if (t == 0) sk[(size_t)bh * Nb + j] = amax > 0.f ? amax / 127.0f : 0.f;
+    int8_t* kdst = k8 + ((size_t)bh * Nb + j) * kBlkBytes;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const int row = rg + 32 * m;
+      const uint16_t* kh = (const uint16_t*)&kraw[m];
+      uint32_t lo = 0, hi = 0;
+      if (row < n) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q_int8(bf16_to_f32(kh[e]) - mu[e], inv) << (8 * e);
+#pragma unroll
+        for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q_int8(bf16_to_f32(kh[e + 4]) - mu[e + 4], inv) << (8 * e);
+      }
+      *(uint2*)(kdst + qk_code_offset(row, ch * 8)) = make_uint2(lo, hi);
+    }
+    // V: FP8 codes straight in operand order. Chunk (dt, half, lane) holds channel
+    // 32*dt + r at tokens 32*half + 4*g + {0..3, 8..11, 16..19, 24..27}: four
+    // transposing reads of 4 consecutive tokens each.
+    {
+      uint8_t* vdst = v8 + ((size_t)bh * Nb + j) * kBlkBytes;
+      const int c0 = 32 * vdt + 16 * hl, jj = lane & 15, a = jj >> 2, b = jj & 3;
+      uint32_t wd[4];
+#pragma unroll
+      for (int qd = 0; qd < 4; qd++) {
+        const v4s_ rv = lds_read_tr16(s_v + (32 * vhalf + 4 * g + 8 * qd + a) * kTp + c0 + 4 * b);
+        const float f0 = bf16_to_f32((uint16_t)rv[0]) * inv_v, f1 = bf16_to_f32((uint16_t)rv[1]) * inv_v;
+        const float f2 = bf16_to_f32((uint16_t)rv[2]) * inv_v, f3 = bf16_to_f32((uint16_t)rv[3]) * inv_v;
+        int pk = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f1, 0, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, pk, true);
+        wd[qd] = (uint32_t)pk;
+      }
+      *(uint4*)(vdst + (w * 64 + lane) * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+    }
+    if (states) {
       float zsum_t = 0.f;
       if (t < kD) {
-        for (int q = 0; q < 16; q++) zsum_t += s_z[q][t];
+#pragma unroll
+        for (int q = 0; q < 8; q++) zsum_t += s_z[q][t];
         zp += zsum_t;
       }
-      // H_j^T = V^T phi on MFMA: wave w owns rows c in [32w, 32w+32), all 4 column tiles a
-      v16f acc[4];
-#pragma unroll
-      for (int c = 0; c < 4; c++) acc[c] = (v16f){};
+      // H_j^T = V^T phi on MFMA; both operands are 8-token slices read transposed from
+      // the row-major tiles
+      v16f acc[2];
+      acc[0] = (v16f){};
+      acc[1] = (v16f){};
 #pragma unroll
       for (int s = 0; s < 4; s++) {
-        const int tok = 16 * s + 8 * g;
-        v8bf av = *(const v8bf*)(s_vt + (32 * w + r) * kTs + tok);
+        const int t0 = 16 * s + 8 * g;
+        const v8bf av = tile_col8(s_v, t0, 32 * wr + 16 * hl, lane);
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          v8bf bh_ = *(const v8bf*)(s_phi_hi + (32 * c + r) * kTs + tok);
-          v8bf bl_ = *(const v8bf*)(s_phi_lo + (32 * c + r) * kTs + tok);
+        for (int c = 0; c < 2; c++) {
+          const int a0 = 32 * (2 * wc + c) + 16 * hl;
+          const v8bf bh_ = tile_col8(s_phi[0], t0, a0, lane);
+          const v8bf bl_ = tile_col8(s_phi[1], t0, a0, lane);
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh_, acc[c], 0, 0, 0);
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl_, acc[c], 0, 0, 0);
         }
       }
       uint16_t* hdst = hs + ((size_t)bh * Nb + j) * kStateElems;
 #pragma unroll
-      for (int c = 0; c < 4; c++)
+      for (int c = 0; c < 2; c++)
 #pragma unroll
         for (int q = 0; q < 16; q++) {
-          const int row = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);  // channel c of V
-          hdst[row * kD + 32 * c + r] = f32_to_bf16(acc[c][q]);
+          const int row = 32 * wr + 8 * (q >> 2) + 4 * g + (q & 3);  // channel of V
+          hdst[row * kD + 32 * (2 * wc + c) + r] = f32_to_bf16(acc[c][q]);
           part[c][q] += acc[c][q];
         }
       if (t < kD) hdst[kD * kD + t] = f32_to_bf16(zsum_t);
@@ -182,11 +227,11 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(
   if (states) {
     float* pdst = hpart + ((size_t)bh * Nc + chunk) * kStateElems;
 #pragma unroll
-    for (int c = 0; c < 4; c++)
+    for (int c = 0; c < 2; c++)
 #pragma unroll
       for (int q = 0; q < 16; q++) {
-        const int row = 32 * w + 8 * (q >> 2) + 4 * g + (q & 3);
-        pdst[row * kD + 32 * c + r] = part[c][q];
+        const int row = 32 * wr + 8 * (q >> 2) + 4 * g + (q & 3);
+        pdst[row * kD + 32 * (2 * wc + c) + r] = part[c][q];
       }
     if (t < kD) pdst[kD * kD + t] = zp;
   }
@@ -208,7 +253,7 @@ __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restri
 hipError_t launch_quant_kv(const void* k, const void* v, const void* kmean, const void* vamax, int BH,
                            int N, int Nb, void* k8, void* sk, void* v8, void* hs, void* hpart, hipStream_t st) {
   const int Nc = (Nb + kChunk - 1) / kChunk;
-  hipLaunchKernelGGL(quant_kv_kernel, dim3(BH * Nc), dim3(256), 0, st, (const uint16_t*)k,
+  hipLaunchKernelGGL(quant_kv_kernel, dim3(BH * Nc), dim3(kQkThreads), 0, st, (const uint16_t*)k,
                      (const uint16_t*)v, (const float*)kmean, (const float*)vamax, N, Nb, Nc,
                      (int8_t*)k8, (float*)sk, (uint8_t*)v8, (uint16_t*)hs, (float*)hpart);
   return hipGetLastError();
