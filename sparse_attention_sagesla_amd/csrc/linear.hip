@@ -205,115 +205,166 @@ __global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
 
 // ---------------------------------------------------------------- output per query block
 
-constexpr int kLs = 136;  // LDS row stride (bf16) for 128-wide tiles: 272 B, 16-B aligned
+constexpr int kLs = 136;   // LDS row pitch (bf16) of the 128-wide tiles: 272 B
+constexpr int kOutQB = 4;  // consecutive query blocks per workgroup (W_proj staged once)
 
-// One workgroup (256 threads, 4 waves) per (bh, query block i):
+// Rows a0..a0+7 of column c0 + lane%16 of a row-major [a][c] bf16 LDS tile (pitch kLs),
+// through two transposing reads: the K=8 slice of a bf16 MFMA operand.
+__device__ __forceinline__ v8bf tile_col8(const uint16_t* tile, int a0, int c0, int lane) {
+  const int j = lane & 15, a = j >> 2, b = j & 3;
+  const v4s_ r0 = lds_read_tr16(tile + (a0 + a) * kLs + c0 + 4 * b);
+  const v4s_ r1 = lds_read_tr16(tile + (a0 + 4 + a) * kLs + c0 + 4 * b);
+  const v8s v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+  return __builtin_bit_cast(v8bf, v);
+}
+
+// Per-block inputs held in registers (the next block's are fetched during this one).
+struct OutLoads {
+  uint4 q[4];    // raw q: rows t/16 + 16 mm, channels 8 (t%16) .. +7
+  v8bf sa[8];    // S^c rows 32 w + l%32, k-steps s: the A operands of num^T
+  float zc;      // z^c[t] (t < 128)
+};
+
+__device__ __forceinline__ void out_load(OutLoads& L, const uint16_t* q, const uint16_t* hc, int bh, int i, int N,
+                                         int Nb, int t, int w, int lane) {
+  const int n = block_len(i, N), rg = t >> 4, ch = t & 15;
+#pragma unroll
+  for (int mm = 0; mm < 4; mm++) {
+    const int row = rg + 16 * mm;
+    L.q[mm] = make_uint4(0, 0, 0, 0);
+    if (row < n) L.q[mm] = *(const uint4*)(q + ((size_t)bh * N + (size_t)i * kBlk + row) * kD + ch * 8);
+  }
+  const uint16_t* S = hc + ((size_t)bh * Nb + i) * kStateElems;
+  const int c = 32 * w + (lane & 31), g = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 8; s++) L.sa[s] = *(const v8bf*)(S + c * kD + 16 * s + 8 * g);
+  L.zc = t < kD ? bf16_to_f32(S[kD * kD + t]) : 0.f;
+}
+
+// One workgroup (256 threads, 4 waves) per kOutQB consecutive query blocks of one head:
 //   O_l[r] = phi(q_r) H^c_i / (phi(q_r) . z^c_i),  y[r] = O_l[r] W_proj  (bf16).
-// hc holds S^c_i = [H^c_i^T ; z^c_i] (129 x 128) in bf16.
+// hc holds S^c_i = [H^c_i^T ; z^c_i] (129 x 128) in bf16. Both products are taken
+// transposed, num^T = S^c phi^T and y^T = W^T O_l^T, so that every operand is a
+// contiguous row (S^c from memory, phi and O_l from LDS) or a transposing LDS read of
+// row-major W, and each lane ends with 4 consecutive channels of one row.
+// Wave w owns channels 32 w .. 32 w + 31 of both products, for all 64 rows.
 __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ hc,
                                                          const uint16_t* __restrict__ proj, int N, int Nb,
-                                                         int tiles, int per_xcd, uint16_t* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[kD * kLs];  // W transposed [c][a]
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[kBlk * kLs];  // phi(Q), then O_l
+                                                         int groups, int per_xcd, uint16_t* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[kD * kLs];    // W_proj [a][c]
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[kBlk * kLs];  // phi(Q) [m][a], then O_l [m][c]
   __shared__ float s_zc[kD];
   __shared__ float s_den[kBlk];
 
-  const int tile = xcd_tile(blockIdx.x, per_xcd);
-  if (tile >= tiles) return;
-  const int bh = tile / Nb, i = tile % Nb;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, g = lane >> 5, r = lane & 31;
-  const int n = block_len(i, N);
-  const uint16_t* S = hc + ((size_t)bh * Nb + i) * kStateElems;
+  const int gid = xcd_tile(blockIdx.x, per_xcd);
+  if (gid >= groups) return;
+  const int nqb = (Nb + kOutQB - 1) / kOutQB;
+  const int bh = gid / nqb, i0 = (gid % nqb) * kOutQB, i1 = min(Nb, i0 + kOutQB);
+  const int t = threadIdx.x, lane = t & 63, g = lane >> 5, r = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-  if (t < kD) s_zc[t] = bf16_to_f32(S[kD * kD + t]);
-  for (int e = t; e < kD * kD / 8; e += 256) {
-    const int a = e / 16, c0 = (e % 16) * 8;  // W[a][c0..c0+7]
-    uint4 wv = *(const uint4*)(proj + a * kD + c0);
-    const uint16_t* wh = (const uint16_t*)&wv;
-#pragma unroll
-    for (int x = 0; x < 8; x++) s_w[(c0 + x) * kLs + a] = wh[x];
+  OutLoads cur, nxt;
+  out_load(cur, q, hc, bh, i0, N, Nb, t, w, lane);
+  for (int e = t; e < kD * 16; e += 256) {
+    const int a = e >> 4, c8 = (e & 15) * 8;
+    *(uint4*)(s_w + a * kLs + c8) = *(const uint4*)(proj + a * kD + c8);
   }
-  __syncthreads();
-  // phi(q) rows (16 lanes per row) -> LDS bf16; den = phi(q) . z^c in fp32
-  {
-    const int rg = t >> 4, ch = t & 15;
+  for (int i = i0; i < i1; i++) {
+    if (i + 1 < i1) out_load(nxt, q, hc, bh, i + 1, N, Nb, t, w, lane);
+    const int n = block_len(i, N);
+    __syncthreads();  // the previous block is done with s_a, s_zc, s_den
+    if (t < kD) s_zc[t] = cur.zc;
+    __syncthreads();
+    // phi(q) rows (16 lanes per row) -> s_a; den = phi(q) . z^c in fp32
+    {
+      const int rg = t >> 4, ch = t & 15;
 #pragma unroll
-    for (int mm = 0; mm < 4; mm++) {
-      const int row = rg + 16 * mm;
-      float x[8];
-      uint4 qa = {0, 0, 0, 0};
-      if (row < n) qa = *(const uint4*)(q + ((size_t)bh * N + (size_t)i * kBlk + row) * kD + ch * 8);
-      const uint16_t* qh = (const uint16_t*)&qa;
+      for (int mm = 0; mm < 4; mm++) {
+        const int row = rg + 16 * mm;
+        const uint16_t* qh = (const uint16_t*)&cur.q[mm];
+        float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = bf16_to_f32(qh[e]);
-      float mx = x[0];
+        for (int e = 0; e < 8; e++) x[e] = bf16_to_f32(qh[e]);
+        float mx = x[0];
 #pragma unroll
-      for (int e = 1; e < 8; e++) mx = fmaxf(mx, x[e]);
+        for (int e = 1; e < 8; e++) mx = fmaxf(mx, x[e]);
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-      float s = 0.f;
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; e++) { x[e] = expf(x[e] - mx); s += x[e]; }
+        for (int e = 0; e < 8; e++) { x[e] = __expf(x[e] - mx); sum += x[e]; }
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-      float den = 0.f;
+        for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o);
+        const float inv = 1.0f / sum;
+        float den = 0.f;
+        uint32_t pk[4];
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const float ph = x[e] / s;
-        den += ph * s_zc[ch * 8 + e];
-        s_a[row * kLs + ch * 8 + e] = f32_to_bf16(ph);
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = x[e] * inv, p1 = x[e + 1] * inv;
+          den += p0 * s_zc[ch * 8 + e] + p1 * s_zc[ch * 8 + e + 1];
+          pk[e / 2] = f32_to_bf16(p0) | ((uint32_t)f32_to_bf16(p1) << 16);
+        }
+        *(uint4*)(s_a + row * kLs + ch * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) den += __shfl_xor(den, o);
+        if (ch == 0) s_den[row] = den;
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) den += __shfl_xor(den, o);
-      if (ch == 0) s_den[row] = den;
     }
+    __syncthreads();
+    // num^T[c][m] = S^c[c][:] . phi[m][:]
+    v16f num[2] = {(v16f){}, (v16f){}};
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const v8bf b = *(const v8bf*)(s_a + (32 * mt + r) * kLs + 16 * s + 8 * g);
+        num[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.sa[s], b, num[mt], 0, 0, 0);
+      }
+    __syncthreads();  // phi fully read
+    // O_l[m][c] = num^T[c][m] / den[m] -> s_a row-major, 4 consecutive channels per store
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      const float den = s_den[32 * mt + r];
+      const float inv = den != 0.f ? 1.0f / den : 0.f;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        const int c = 32 * w + 8 * q4 + 4 * g;
+        uint2 pk;
+        pk.x = f32_to_bf16(num[mt][4 * q4] * inv) | ((uint32_t)f32_to_bf16(num[mt][4 * q4 + 1] * inv) << 16);
+        pk.y = f32_to_bf16(num[mt][4 * q4 + 2] * inv) | ((uint32_t)f32_to_bf16(num[mt][4 * q4 + 3] * inv) << 16);
+        *(uint2*)(s_a + (32 * mt + r) * kLs + c) = pk;
+      }
+    }
+    __syncthreads();
+    // y^T[c][m] = W[:][c] . O_l[m][:]
+    v16f yo[2] = {(v16f){}, (v16f){}};
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const v8bf a = tile_col8(s_w, 16 * s + 8 * g, 32 * w + 16 * ((lane >> 4) & 1), lane);
+#pragma unroll
+      for (int mt = 0; mt < 2; mt++) {
+        const v8bf b = *(const v8bf*)(s_a + (32 * mt + r) * kLs + 16 * s + 8 * g);
+        yo[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, yo[mt], 0, 0, 0);
+      }
+    }
+    uint16_t* ydst = y + ((size_t)bh * N + (size_t)i * kBlk) * kD;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+      const int m = 32 * mt + r;
+      if (m < n) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          const int c = 32 * w + 8 * q4 + 4 * g;
+          uint2 pk;
+          pk.x = f32_to_bf16(yo[mt][4 * q4]) | ((uint32_t)f32_to_bf16(yo[mt][4 * q4 + 1]) << 16);
+          pk.y = f32_to_bf16(yo[mt][4 * q4 + 2]) | ((uint32_t)f32_to_bf16(yo[mt][4 * q4 + 3]) << 16);
+          *(uint2*)(ydst + (size_t)m * kD + c) = pk;
+        }
+      }
+    }
+    cur = nxt;
   }
-  __syncthreads();
-  // numerator phi(Q) H^c: B operand rows come straight from S (row c = output column)
-  const int rt = w & 1, ct0 = 2 * (w >> 1);
-  v16f num[2] = {(v16f){}, (v16f){}};
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    const int kk = 16 * s + 8 * g;
-    const v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const v8bf b = *(const v8bf*)(S + (32 * (ct0 + c) + r) * kD + kk);
-      num[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, num[c], 0, 0, 0);
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int c = 0; c < 2; c++)
-#pragma unroll
-    for (int qq = 0; qq < 16; qq++) {
-      const int row = 32 * rt + 8 * (qq >> 2) + 4 * g + (qq & 3);
-      const int col = 32 * (ct0 + c) + r;
-      const float den = s_den[row];
-      s_a[row * kLs + col] = f32_to_bf16(den != 0.f ? num[c][qq] / den : 0.f);
-    }
-  __syncthreads();
-  // y = O_l W
-  v16f yo[2] = {(v16f){}, (v16f){}};
-#pragma unroll
-  for (int s = 0; s < 8; s++) {
-    const int kk = 16 * s + 8 * g;
-    const v8bf a = *(const v8bf*)(s_a + (32 * rt + r) * kLs + kk);
-#pragma unroll
-    for (int c = 0; c < 2; c++) {
-      const v8bf b = *(const v8bf*)(s_w + (32 * (ct0 + c) + r) * kLs + kk);
-      yo[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, yo[c], 0, 0, 0);
-    }
-  }
-  uint16_t* ydst = y + ((size_t)bh * N + (size_t)i * kBlk) * kD;
-#pragma unroll
-  for (int c = 0; c < 2; c++)
-#pragma unroll
-    for (int qq = 0; qq < 16; qq++) {
-      const int row = 32 * rt + 8 * (qq >> 2) + 4 * g + (qq & 3);
-      if (row < n) ydst[(size_t)row * kD + 32 * (ct0 + c) + r] = f32_to_bf16(yo[c][qq]);
-    }
 }
 
 int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
@@ -330,10 +381,10 @@ hipError_t launch_linear_complement(const void* q, const void* idx, const void* 
                      (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
                      Nb, ng, (uint16_t*)hc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int tiles = BH * Nb;
-  const int per_xcd = (tiles + 7) / 8;
+  const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
+  const int per_xcd = (groups + 7) / 8;
   hipLaunchKernelGGL(linear_out_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)hc, (const uint16_t*)proj, N, Nb, tiles, per_xcd, (uint16_t*)y);
+                     (const uint16_t*)hc, (const uint16_t*)proj, N, Nb, groups, per_xcd, (uint16_t*)y);
   return hipGetLastError();
 }
 
