@@ -75,7 +75,7 @@ enum {
     SAGESLA_WS_HPART,     /* fp32 [BH][Nc][129][d] sums of 16 consecutive S_j (linear)      */
     SAGESLA_WS_HTOT,      /* fp32 [BH][129][d]  sum of all S_j                  (linear)   */
     SAGESLA_WS_ULIST,     /* int32 [BH][Ng][Nb] union of kept blocks of each query group   */
-    SAGESLA_WS_UMASK,     /* u32 [BH][Ng][Nb][4] per union entry: which of the 128 keep it */
+    SAGESLA_WS_UMASK,     /* u32 [BH][Ng][Nb][8] per union entry: which of the 256 keep it */
     SAGESLA_WS_UCOUNT,    /* int32 [BH][Ng]     union sizes                     (linear)   */
     SAGESLA_WS_HC,        /* bf16 [BH][Nb][129][d] complement states total - kept (linear) */
     SAGESLA_WS_Y,         /* bf16 [BH][N][d]    O_l W_proj                      (linear)   */
@@ -88,7 +88,7 @@ enum {
  *  V8:    byte ((dt*2 + e/16)*64 + l)*16 + e%16 holds channel 32*dt + r of token
  *         32*(e/16) + 8*((e%16)/4) + 4*g + e%4 (dt in 0..3, e in 0..31); rows past N are 0.
  * H_j[a][c] = sum_t phi(k_t)[a] v_t[c], z_j[a] = sum_t phi(k_t)[a] over the tokens of block j.
- * Nc = ceil(Nb/16) partial sums; Ng = ceil(Nb/128) query-block groups.
+ * Nc = ceil(Nb/16) partial sums; Ng = ceil(Nb/256) query-block groups.
  */
 
 int sagesla_version(void);
@@ -143,7 +143,7 @@ sagesla_status sagesla_quant_kv(const void *k, const void *v, const void *kmean,
 sagesla_status sagesla_linear_total(const void *hpart, int B, int H, int N, int d, int block,
                                     void *htot, sagesla_stream_t stream);
 
-/* Linear branch: per group of 128 query blocks the union of their kept sets (ulist,
+/* Linear branch: per group of 256 query blocks the union of their kept sets (ulist,
  * umask, ucount), the complement states hc = S_total - sum_kept S_j (a 0/1-mask product
  * on the matrix cores), and y = O_l W with O_l = phi(q) H^c / (phi(q) . z^c). */
 sagesla_status sagesla_linear_complement(const void *q, const void *idx, const void *hs,

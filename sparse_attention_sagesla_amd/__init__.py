@@ -5,7 +5,7 @@ kernels (``csrc/``, interface in ``include/sagesla.h``); this package only marsh
 tensors into it. The library is loaded on first use; there is no CPU fallback.
 """
 from . import synth  # noqa: F401  (seeded synthetic inputs)
-from ._lib import (SageSLAError, alloc_workspace, fwd, ksel, lib, status_string,  # noqa: F401
+from ._lib import (GROUP, SageSLAError, alloc_workspace, fwd, ksel, lib, status_string,  # noqa: F401
                    workspace_layout, workspace_size, workspace_views)
 
 __all__ = ["fwd", "ksel", "workspace_size", "workspace_layout", "workspace_views", "alloc_workspace",

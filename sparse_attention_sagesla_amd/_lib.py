@@ -19,6 +19,7 @@ OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 WS_REGIONS = ["qbar", "kbart", "ksum", "vamax_blk", "kmean", "vamax", "q8", "sq", "k8", "sk", "v8", "idx",
               "hs", "hpart", "htot", "ulist", "umask", "ucount", "hc", "y"]
 WS_COUNT = len(WS_REGIONS)
+GROUP = 256  # query blocks per group of the linear-branch complement (union lists, masks)
 
 EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_workspace_size",
            "sagesla_workspace_layout", "sagesla_fwd", "sagesla_pool", "sagesla_head_stats", "sagesla_select",
@@ -146,7 +147,7 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
     BH, Nb = B * H, (N + block - 1) // block
     k = ksel(N, topk, block)
     Nc = (Nb + 15) // 16
-    Ng = (Nb + 127) // 128
+    Ng = (Nb + GROUP - 1) // GROUP
     SE = 129 * d
     spec = {
         "qbar": (torch.float64, (BH, Nb, d)), "kbart": (torch.float64, (BH, d, Nb)),
@@ -157,7 +158,7 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
         "v8": (torch.uint8, (BH, Nb, 8192)), "idx": (torch.int32, (BH, Nb, k)),
         "hs": (torch.bfloat16, (BH, Nb, 129, d)), "hpart": (torch.float32, (BH, Nc, 129, d)),
         "htot": (torch.float32, (BH, 129, d)), "ulist": (torch.int32, (BH, Ng, Nb)),
-        "umask": (torch.int32, (BH, Ng, Nb, 4)), "ucount": (torch.int32, (BH, Ng)),
+        "umask": (torch.int32, (BH, Ng, Nb, GROUP // 32)), "ucount": (torch.int32, (BH, Ng)),
         "hc": (torch.bfloat16, (BH, Nb, 129, d)), "y": (torch.bfloat16, (BH, N, d)),
     }
     total = ws.numel()

@@ -10,7 +10,8 @@ constexpr int kBlk = 64;        // tokens per block
 constexpr int kBlkBytes = 8192; // one block of INT8/FP8 codes (64 x 128)
 constexpr int kChunk = 16;      // key blocks per linear-state partial sum
 constexpr int kStateElems = 129 * 128;  // one block's linear state: H^T (128 x 128) and z (1 x 128)
-constexpr int kGroup = 128;     // query blocks per group in the complement kernels
+constexpr int kGroup = 256;     // query blocks per group in the complement kernels
+constexpr int kMaskWords = kGroup / 32;  // 32-bit words of one union entry's membership mask
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));

@@ -18,18 +18,18 @@ namespace sagesla {
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f_ __attribute__((ext_vector_type(4)));
 
-constexpr int kUnionRange = 4096;  // key blocks per LDS pass of the union kernel
+constexpr int kUnionRange = 1024;  // key blocks per LDS pass of the union kernel
 
 // ---------------------------------------------------------------- union of a group
 
-// Per (bh, group): the ascending union of the kept key blocks of query blocks
-// g*128 .. g*128+127, with, per union entry, a 128-bit mask of the query blocks that
-// keep it. ulist: [BH][ng][Nb], umask: [BH][ng][Nb][4], ucount: [BH][ng].
+// Per (bh, group): the ascending union of the kept key blocks of the group's kGroup
+// query blocks, with, per union entry, a kGroup-bit mask of the query blocks that keep
+// it. ulist: [BH][ng][Nb], umask: [BH][ng][Nb][kMaskWords], ucount: [BH][ng].
 __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __restrict__ idx, int Nb, int ksel,
                                                            int ngroups, int32_t* __restrict__ ulist,
                                                            uint32_t* __restrict__ umask,
                                                            int32_t* __restrict__ ucount) {
-  __shared__ uint32_t s_flags[kUnionRange][4];
+  __shared__ uint32_t s_flags[kUnionRange][kMaskWords];
   __shared__ int s_tmp[8];
   const int bh = blockIdx.x / ngroups, grp = blockIdx.x % ngroups, t = threadIdx.x;
   const int q0 = grp * kGroup, nq = min(kGroup, Nb - q0);
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
   int count = 0;
   for (int r0 = 0; r0 < Nb; r0 += kUnionRange) {
     const int rl = min(kUnionRange, Nb - r0);
-    for (int e = t; e < rl * 4; e += 256) (&s_flags[0][0])[e] = 0u;
+    for (int e = t; e < rl * kMaskWords; e += 256) (&s_flags[0][0])[e] = 0u;
     __syncthreads();
     const int32_t* src = idx + ((size_t)bh * Nb + q0) * ksel;
     for (int e = t; e < nq * ksel; e += 256) {
@@ -48,8 +48,14 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
     __syncthreads();
     // compact the non-empty entries in ascending order: thread t owns a contiguous range
     const int per = (rl + 255) / 256, j0 = t * per, j1 = min(rl, j0 + per);
+    auto any = [&](int j) {
+      uint32_t o = 0u;
+#pragma unroll
+      for (int x = 0; x < kMaskWords; x++) o |= s_flags[j][x];
+      return o != 0u;
+    };
     int n = 0;
-    for (int j = j0; j < j1; j++) n += (s_flags[j][0] | s_flags[j][1] | s_flags[j][2] | s_flags[j][3]) != 0u;
+    for (int j = j0; j < j1; j++) n += any(j);
     // block exclusive scan of n
     const int lane = t & 63, w = t >> 6;
     int incl = n;
@@ -68,10 +74,12 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
     }
     int pos = count + off + incl - n;
     for (int j = j0; j < j1; j++) {
-      const uint32_t m0 = s_flags[j][0], m1 = s_flags[j][1], m2 = s_flags[j][2], m3 = s_flags[j][3];
-      if ((m0 | m1 | m2 | m3) == 0u) continue;
+      if (!any(j)) continue;
       ulist[gbase * Nb + pos] = r0 + j;
-      *(uint4*)(umask + (gbase * Nb + pos) * 4) = make_uint4(m0, m1, m2, m3);
+      uint4* dst = (uint4*)(umask + (gbase * Nb + pos) * kMaskWords);
+#pragma unroll
+      for (int x = 0; x < kMaskWords / 4; x++)
+        dst[x] = make_uint4(s_flags[j][4 * x], s_flags[j][4 * x + 1], s_flags[j][4 * x + 2], s_flags[j][4 * x + 3]);
       pos++;
     }
     count += tot;
@@ -82,7 +90,8 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------- masked sum on MFMA
 
-constexpr int kBp = 144;  // LDS row pitch (bf16) of the [state][column] tile: 288 B (bank spread)
+constexpr int kBp = 72;     // LDS row pitch (bf16) of a [state][64 columns] operand tile: 144 B
+constexpr int kMgSlots = 4;  // steps of 32 union entries in flight (registers, then LDS)
 typedef short v4s_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
 
@@ -92,114 +101,125 @@ __device__ __forceinline__ v4s_ lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
 }
 
-// Per (bh, group, state row c in 0..128): for the group's 128 query blocks i,
-//   hc[i][c][a] = htot[c][a] - sum_u C[i][u] S_{union[u]}[c][a]   (a = 0..127)
-// as a [128 x U] x [U x 128] product on v_mfma_f32_16x16x32_bf16 (the 0/1 mask is
+// Per (bh, group, state row c in 0..128, column half h): for the group's kGroup query
+// blocks i and columns a in 64 h .. 64 h + 63,
+//   hc[i][c][a] = htot[c][a] - sum_u C[i][u] S_{union[u]}[c][a]
+// as a [kGroup x U] x [U x 64] product on v_mfma_f32_16x16x32_bf16 (the 0/1 mask is
 // exact in bf16, the states are bf16, the sums fp32). Wave w owns query blocks
-// 32w .. 32w+31 (2 M-tiles) and all 8 column tiles.
-__global__ __launch_bounds__(256) void linear_mask_gemm_kernel(
+// 64w .. 64w+63 (4 M-tiles) and the 4 column tiles. Union entries stream in steps of
+// 32, fetched kMgSlots steps ahead.
+__global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
     const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
     const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
     uint16_t* __restrict__ hc) {
-  // operand tiles during the K-loop, then (after the last barrier) the output tile
-  __shared__ __attribute__((aligned(16))) uint16_t s_raw[kGroup * kD];
-  __shared__ uint32_t s_m[2][32][4];
-  uint16_t (*s_b)[32 * kBp] = reinterpret_cast<uint16_t (*)[32 * kBp]>(s_raw);
-  uint16_t* s_out = s_raw;
-  static_assert(2 * 32 * kBp <= kGroup * kD, "operand tiles must fit in the output tile");
+  __shared__ __attribute__((aligned(16))) uint16_t s_b[kMgSlots][32 * kBp];
+  __shared__ uint32_t s_m[kMgSlots][32][kMaskWords];
+  __shared__ __attribute__((aligned(16))) uint16_t s_out[kGroup / 2 * 64];
 
-  const int per_bh = ngroups * 129;
+  const int per_bh = ngroups * 129 * 2;
   const int bh = blockIdx.x / per_bh, rem = blockIdx.x % per_bh;
-  const int grp = rem / 129, c = rem % 129;
+  const int grp = rem / 258, c = (rem % 258) >> 1, half = rem & 1;
   const size_t gbase = (size_t)bh * ngroups + grp;
   const int U = ucount[gbase];
   const int32_t* ul = ulist + gbase * Nb;
-  const uint32_t* um = umask + gbase * Nb * 4;
+  const uint32_t* um = umask + gbase * Nb * kMaskWords;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, kg = lane >> 4;
 
-  v4f_ acc[2][8];
+  v4f_ acc[4][4];
 #pragma unroll
-  for (int m = 0; m < 2; m++)
+  for (int m = 0; m < 4; m++)
 #pragma unroll
-    for (int n = 0; n < 8; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 4; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (U + 31) / 32;
-  // 32 states x 128 columns per step: thread t holds 16 B (8 columns) of states t/16 and
-  // t/16 + 16, loaded a step ahead and stored row-major ([state][column]) into LDS; the
-  // MFMA B operand (8 consecutive states of one column) comes from transposing reads.
-  uint4 pre[2];
-  uint32_t pmask = 0u;
-  auto load = [&](int step) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const int u = step * 32 + (t >> 4) + 16 * h;
-      pre[h] = make_uint4(0, 0, 0, 0);
-      if (u < U) pre[h] = *(const uint4*)(hs + ((size_t)bh * Nb + ul[u]) * kStateElems + c * kD + (t & 15) * 8);
-    }
-    if (t < 128) {
-      const int u = step * 32 + (t >> 2);
-      pmask = u < U ? um[(size_t)u * 4 + (t & 3)] : 0u;
+  // 32 states x 64 columns per step: thread t holds 16 B (8 columns) of state t/8, and
+  // one mask word (entry t/8, word t%8); stored row-major ([state][column]) into LDS the
+  // step before use. The MFMA B operand (8 consecutive states of one column) comes from
+  // transposing reads.
+  uint4 pre[kMgSlots];
+  uint32_t pmask[kMgSlots];
+  const size_t col0 = (size_t)c * kD + 64 * half + (t & 7) * 8;
+  auto load = [&](int slot, int step) {
+    const int u = step * 32 + (t >> 3);
+    pre[slot] = make_uint4(0, 0, 0, 0);
+    pmask[slot] = 0u;
+    if (u < U) {
+      pre[slot] = *(const uint4*)(hs + ((size_t)bh * Nb + ul[u]) * kStateElems + col0);
+      pmask[slot] = um[(size_t)u * kMaskWords + (t & 7)];
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-      const int k = (t >> 4) + 16 * h, ch = t & 15;
-      *(uint4*)(&s_b[buf][k * kBp + ch * 8]) = pre[h];
-    }
-    if (t < 128) s_m[buf][t >> 2][t & 3] = pmask;
+  auto store = [&](int slot) {
+    *(uint4*)(&s_b[slot][(t >> 3) * kBp + (t & 7) * 8]) = pre[slot];
+    s_m[slot][t >> 3][t & 7] = pmask[slot];
   };
-  if (nsteps > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int step = 0; step < nsteps; step++) {
-    const int buf = step & 1;
-    if (step + 1 < nsteps) load(step + 1);
-    // A operand: rows = query blocks 32w + 16m + l16, k = union entries 8kg .. 8kg+7
-    v8s a[2];
+  auto step_body = [&](int slot) {
+    // A operand: rows = query blocks 64w + 16m + l16, k = union entries 8kg .. 8kg+7
+    v8s a[4];
 #pragma unroll
-    for (int m = 0; m < 2; m++) {
-      const int bit = 16 * m + l16;
+    for (int m = 0; m < 4; m++) {
+      const int word = 2 * w + (m >> 1), bit = 16 * (m & 1) + l16;
 #pragma unroll
-      for (int x = 0; x < 8; x++) a[m][x] = ((s_m[buf][8 * kg + x][w] >> bit) & 1u) ? (short)0x3F80 : (short)0;
+      for (int x = 0; x < 8; x++) a[m][x] = ((s_m[slot][8 * kg + x][word] >> bit) & 1u) ? (short)0x3F80 : (short)0;
     }
     // lane (kg, l16): states 8kg..8kg+7 of column 16n + l16, as two 4 x 16 transposes
     const int ta = l16 >> 2, tb = l16 & 3;
 #pragma unroll
-    for (int n = 0; n < 8; n++) {
-      const v4s_ r0 = lds_read_tr16(&s_b[buf][(8 * kg + ta) * kBp + 16 * n + 4 * tb]);
-      const v4s_ r1 = lds_read_tr16(&s_b[buf][(8 * kg + 4 + ta) * kBp + 16 * n + 4 * tb]);
+    for (int n = 0; n < 4; n++) {
+      const v4s_ r0 = lds_read_tr16(&s_b[slot][(8 * kg + ta) * kBp + 16 * n + 4 * tb]);
+      const v4s_ r1 = lds_read_tr16(&s_b[slot][(8 * kg + 4 + ta) * kBp + 16 * n + 4 * tb]);
       const v8s bs = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
       const v8bf b = __builtin_bit_cast(v8bf, bs);
 #pragma unroll
-      for (int m = 0; m < 2; m++)
+      for (int m = 0; m < 4; m++)
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[m]), b, acc[m][n], 0, 0, 0);
     }
-    if (step + 1 < nsteps) store(buf ^ 1);
-    __syncthreads();
-  }
-  // hc = htot - M, staged through LDS for 16-byte stores
-  const float* ht = htot + (size_t)bh * kStateElems + c * kD;
+  };
 #pragma unroll
-  for (int n = 0; n < 8; n++) {
-    const int col = 16 * n + l16;
-    const float tot = ht[col];
-#pragma unroll
-    for (int m = 0; m < 2; m++)
-#pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int qi = 32 * w + 16 * m + 4 * kg + v;
-        s_out[qi * kD + col] = f32_to_bf16(tot - acc[m][n][v]);
-      }
-  }
+  for (int p = 0; p < kMgSlots; p++)
+    if (p < nsteps) load(p, p);
+  if (nsteps > 0) store(0);
   __syncthreads();
+  // step s uses slot s % kMgSlots (LDS and registers); that register slot refills with
+  // step s + kMgSlots, and step s + 1 moves from its registers into LDS
+  for (int s0 = 0; s0 < nsteps; s0 += kMgSlots) {
+#pragma unroll
+    for (int ph = 0; ph < kMgSlots; ph++) {
+      const int step = s0 + ph;
+      if (step < nsteps) {
+        if (step + kMgSlots < nsteps) load(ph, step + kMgSlots);
+        step_body(ph);
+        if (step + 1 < nsteps) store((ph + 1) % kMgSlots);
+      }
+      __syncthreads();
+    }
+  }
+  // hc = htot - M, staged through LDS (two halves of kGroup/2 query blocks) for 16-byte stores
+  const float* ht = htot + (size_t)bh * kStateElems + c * kD + 64 * half;
   const int q0 = grp * kGroup;
-  for (int e = t; e < kGroup * 16; e += 256) {
-    const int qi = e >> 4, ch = e & 15;
-    if (q0 + qi < Nb)
-      *(uint4*)(hc + ((size_t)bh * Nb + q0 + qi) * kStateElems + c * kD + ch * 8) = *(const uint4*)(s_out + qi * kD + ch * 8);
+#pragma unroll
+  for (int hh = 0; hh < 2; hh++) {
+    if ((w >> 1) == hh) {
+#pragma unroll
+      for (int n = 0; n < 4; n++) {
+        const int col = 16 * n + l16;
+        const float tot = ht[col];
+#pragma unroll
+        for (int m = 0; m < 4; m++)
+#pragma unroll
+          for (int v = 0; v < 4; v++) {
+            const int qi = 64 * (w & 1) + 16 * m + 4 * kg + v;  // within the half
+            s_out[qi * 64 + col] = f32_to_bf16(tot - acc[m][n][v]);
+          }
+      }
+    }
+    __syncthreads();
+    for (int e = t; e < kGroup / 2 * 8; e += 256) {
+      const int qi = e >> 3, ch = e & 7, qb = q0 + kGroup / 2 * hh + qi;
+      if (qb < Nb)
+        *(uint4*)(hc + ((size_t)bh * Nb + qb) * kStateElems + c * kD + 64 * half + ch * 8) =
+            *(const uint4*)(s_out + qi * 64 + ch * 8);
+    }
+    __syncthreads();
   }
 }
 
@@ -377,7 +397,7 @@ hipError_t launch_linear_complement(const void* q, const void* idx, const void* 
                      (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129), dim3(256), 0, st, (const uint16_t*)hs,
+  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
                      (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
                      Nb, ng, (uint16_t*)hc);
   if ((e = hipGetLastError()) != hipSuccess) return e;

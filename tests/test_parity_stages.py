@@ -27,6 +27,8 @@ CASES = {
     "longrange": (synth.CONFIGS["i2v-a14b-720p"], dict(H=2, grid=(3, 24, 40), seed=23)),
     "one-block": (synth.CONFIGS["tiny"], dict(H=2, grid=(1, 1, 37), seed=24)),
     "ksel-1": (synth.CONFIGS["wan1.3b-480p"], dict(H=2, grid=(2, 16, 40), topk=1e-6, seed=25)),
+    # more query blocks than one complement group holds (300 blocks: groups of 256 + 44)
+    "two-groups": (synth.CONFIGS["wan1.3b-480p"], dict(H=1, grid=(3, 10, 640), seed=26)),
 }
 
 
@@ -92,15 +94,16 @@ def test_stage_parity(name):
             assert np.max(np.abs(g["htot"][bh] - tot)) <= 1e-5 * np.max(np.abs(tot))
             # union of each group's kept sets, with the per-query-block masks
             gidx = g["idx"][bh]
-            for grp in range((Nb + 127) // 128):
-                rows = range(128 * grp, min(Nb, 128 * grp + 128))
+            G = S.GROUP
+            for grp in range((Nb + G - 1) // G):
+                rows = range(G * grp, min(Nb, G * grp + G))
                 want = sorted(set(np.concatenate([gidx[i] for i in rows]).tolist()))
                 cnt = int(g["ucount"][bh][grp])
                 assert cnt == len(want) and list(g["ulist"][bh][grp][:cnt]) == want
                 um = g["umask"][bh][grp][:cnt].view(np.uint32)
                 for u, j in enumerate(want):
                     keepers = [i for i in rows if j in set(gidx[i].tolist())]
-                    got = [128 * grp + 32 * wd + bb for wd in range(4) for bb in range(32) if (um[u][wd] >> bb) & 1]
+                    got = [G * grp + 32 * wd + bb for wd in range(G // 32) for bb in range(32) if (um[u][wd] >> bb) & 1]
                     assert got == keepers
             # complement states: total minus the kept blocks (with the GPU's kept sets)
             for i in range(Nb):
