@@ -29,6 +29,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> bf16 round-to-nearest-even conversions packed in one word (a low, b high):
+// one gfx950 v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // INT8 code: round half to even of x*inv, clamped to [-127, 127]
 __device__ __forceinline__ int q_int8(float x, float inv) {
   float y = __builtin_rintf(x * inv);

@@ -22,6 +22,8 @@ typedef short v4s_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
 
 constexpr int kTp = 144;  // LDS row pitch (bf16) of the [token][channel] tiles: 288 B (bank spread)
+constexpr int kSp = 136;  // LDS row pitch (bf16) of the staged state tile: 272 B
+static_assert((kD + 1) * kSp <= 2 * 64 * kTp, "the staged state must fit in the phi area");
 
 // gfx950 transposing LDS read: within each group of 16 lanes, lanes 4a..4a+3 each name
 // 4 consecutive 16-bit elements of row a of a 4 x 16 tile, and lane j receives column j.
@@ -44,7 +46,7 @@ constexpr int kQkThreads = 512;
 // One workgroup (512 threads, 8 waves) per (bh, chunk of 16 key blocks). Thread t
 // covers rows t/16 + 32m (m = 0, 1) and channels 8*(t%16) .. +7 of each block. In the
 // state product wave w owns rows c in [32(w%4), +32) and column tiles 2(w/4), 2(w/4)+1.
-__global__ __launch_bounds__(kQkThreads) void quant_kv_kernel(
+__global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ kmean,
     const float* __restrict__ vamax, int N, int Nb, int Nc, int8_t* __restrict__ k8,
     float* __restrict__ sk, uint8_t* __restrict__ v8, uint16_t* __restrict__ hs,
@@ -75,23 +77,37 @@ __global__ __launch_bounds__(kQkThreads) void quant_kv_kernel(
   part[1] = (v16f){};
 
   const int j0 = chunk * kChunk, j1 = min(Nb, j0 + kChunk);
+  // raw K and V rows of block jj (zeros past N); each block's are fetched while the
+  // previous block is processed
+  uint4 kn[2], vn[2];
+  auto fetch = [&](int jj) {
+    const int nn = block_len(jj, N);
+    const size_t bb = ((size_t)bh * N + (size_t)jj * kBlk) * kD;
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const int row = rg + 32 * m;
+      kn[m] = make_uint4(0, 0, 0, 0);
+      vn[m] = make_uint4(0, 0, 0, 0);
+      if (row < nn) {
+        const size_t off = bb + (size_t)row * kD + ch * 8;
+        kn[m] = *(const uint4*)(k + off);
+        vn[m] = *(const uint4*)(v + off);
+      }
+    }
+  };
+  fetch(j0);
   for (int j = j0; j < j1; j++) {
     const int n = block_len(j, N);
-    const size_t base = ((size_t)bh * N + (size_t)j * kBlk) * kD;
-    uint4 kraw[2];
+    uint4 kraw[2], vraw[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) { kraw[m] = kn[m]; vraw[m] = vn[m]; }
+    if (j + 1 < j1) fetch(j + 1);
     float amax = 0.f;
 #pragma unroll
     for (int m = 0; m < 2; m++) {
       const int row = rg + 32 * m;
-      uint4 vraw = make_uint4(0, 0, 0, 0);
-      kraw[m] = make_uint4(0, 0, 0, 0);
-      if (row < n) {
-        const size_t off = base + (size_t)row * kD + ch * 8;
-        kraw[m] = *(const uint4*)(k + off);
-        vraw = *(const uint4*)(v + off);
-      }
-      // V row-major into LDS for the V codes and the state product (zeros past N)
-      *(uint4*)(s_v + row * kTp + ch * 8) = vraw;
+      // V row-major into LDS for the V codes and the state product
+      *(uint4*)(s_v + row * kTp + ch * 8) = vraw[m];
       const uint16_t* kh = (const uint16_t*)&kraw[m];
       if (row < n) {
 #pragma unroll
@@ -119,19 +135,19 @@ __global__ __launch_bounds__(kQkThreads) void quant_kv_kernel(
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         float ssum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; e++) { x[e] = expf(x[e] - mx); ssum += x[e]; }
+        for (int e = 0; e < 8; e++) { x[e] = __expf(x[e] - mx); ssum += x[e]; }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) ssum += __shfl_xor(ssum, o);
+        const float inv = row < n ? 1.0f / ssum : 0.f;
         uint32_t hw[4], lw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = row < n ? x[e] / ssum : 0.f, p1 = row < n ? x[e + 1] / ssum : 0.f;
+          const float p0 = x[e] * inv, p1 = x[e + 1] * inv;
           zc[e] += p0;
           zc[e + 1] += p1;
-          const uint16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-          const uint16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0)), l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
-          hw[e / 2] = h0 | ((uint32_t)h1 << 16);
-          lw[e / 2] = l0 | ((uint32_t)l1 << 16);
+          hw[e / 2] = pack_bf16x2(p0, p1);
+          lw[e / 2] = pack_bf16x2(p0 - bf16_to_f32((uint16_t)(hw[e / 2] & 0xffffu)),
+                                  p1 - bf16_to_f32((uint16_t)(hw[e / 2] >> 16)));
         }
         *(uint4*)(s_phi[0] + row * kTp + ch * 8) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
         *(uint4*)(s_phi[1] + row * kTp + ch * 8) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -211,16 +227,24 @@ __global__ __launch_bounds__(kQkThreads) void quant_kv_kernel(
           acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl_, acc[c], 0, 0, 0);
         }
       }
-      uint16_t* hdst = hs + ((size_t)bh * Nb + j) * kStateElems;
+      // the block's state S_j (129 x 128 bf16) is staged in the phi area for 16-byte stores
+      __syncthreads();  // every wave is done reading phi
+      uint16_t* s_st = &s_phi[0][0];
 #pragma unroll
       for (int c = 0; c < 2; c++)
 #pragma unroll
         for (int q = 0; q < 16; q++) {
           const int row = 32 * wr + 8 * (q >> 2) + 4 * g + (q & 3);  // channel of V
-          hdst[row * kD + 32 * (2 * wc + c) + r] = f32_to_bf16(acc[c][q]);
+          s_st[row * kSp + 32 * (2 * wc + c) + r] = f32_to_bf16(acc[c][q]);
           part[c][q] += acc[c][q];
         }
-      if (t < kD) hdst[kD * kD + t] = f32_to_bf16(zsum_t);
+      if (t < kD) s_st[kD * kSp + t] = f32_to_bf16(zsum_t);
+      __syncthreads();
+      uint16_t* hdst = hs + ((size_t)bh * Nb + j) * kStateElems;
+      for (int e = t; e < (kD + 1) * 16; e += kQkThreads) {
+        const int row = e >> 4, c8 = (e & 15) * 8;
+        *(uint4*)(hdst + row * kD + c8) = *(const uint4*)(s_st + row * kSp + c8);
+      }
     }
     __syncthreads();
   }
