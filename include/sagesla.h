@@ -75,7 +75,7 @@ enum {
     SAGESLA_WS_HPART,     /* fp32 [BH][Nc][129][d] sums of 16 consecutive S_j (linear)      */
     SAGESLA_WS_HTOT,      /* fp32 [BH][129][d]  sum of all S_j                  (linear)   */
     SAGESLA_WS_ULIST,     /* int32 [BH][Ng][Nb] union of kept blocks of each query group   */
-    SAGESLA_WS_UMASK,     /* u32 [BH][Ng][Nb][8] per union entry: which of the 256 keep it */
+    SAGESLA_WS_UMASK,     /* u32 [BH][Ng][ceil(Nb/32)][256] per query block: bits over union positions */
     SAGESLA_WS_UCOUNT,    /* int32 [BH][Ng]     union sizes                     (linear)   */
     SAGESLA_WS_HC,        /* bf16 [BH][Nb][129][d] complement states total - kept (linear) */
     SAGESLA_WS_Y,         /* bf16 [BH][N][d]    O_l W_proj                      (linear)   */

@@ -158,7 +158,7 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
         "v8": (torch.uint8, (BH, Nb, 8192)), "idx": (torch.int32, (BH, Nb, k)),
         "hs": (torch.bfloat16, (BH, Nb, 129, d)), "hpart": (torch.float32, (BH, Nc, 129, d)),
         "htot": (torch.float32, (BH, 129, d)), "ulist": (torch.int32, (BH, Ng, Nb)),
-        "umask": (torch.int32, (BH, Ng, Nb, GROUP // 32)), "ucount": (torch.int32, (BH, Ng)),
+        "umask": (torch.int32, (BH, Ng, (Nb + 31) // 32, GROUP)), "ucount": (torch.int32, (BH, Ng)),
         "hc": (torch.bfloat16, (BH, Nb, 129, d)), "y": (torch.bfloat16, (BH, N, d)),
     }
     total = ws.numel()

@@ -116,7 +116,7 @@ void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* t
     sz[SAGESLA_WS_HPART] = BH * Nc * SE * 4;
     sz[SAGESLA_WS_HTOT] = BH * SE * 4;
     sz[SAGESLA_WS_ULIST] = BH * Ng * Nb * 4;
-    sz[SAGESLA_WS_UMASK] = BH * Ng * Nb * 4 * kMaskWords;
+    sz[SAGESLA_WS_UMASK] = BH * Ng * kGroup * ((Nb + 31) / 32) * 4;
     sz[SAGESLA_WS_UCOUNT] = BH * Ng * 4;
     sz[SAGESLA_WS_HC] = BH * Nb * SE * 2;
     sz[SAGESLA_WS_Y] = BH * N * D * 2;

@@ -23,17 +23,23 @@ constexpr int kUnionRange = 1024;  // key blocks per LDS pass of the union kerne
 // ---------------------------------------------------------------- union of a group
 
 // Per (bh, group): the ascending union of the kept key blocks of the group's kGroup
-// query blocks, with, per union entry, a kGroup-bit mask of the query blocks that keep
-// it. ulist: [BH][ng][Nb], umask: [BH][ng][Nb][kMaskWords], ucount: [BH][ng].
+// query blocks, and which query blocks keep each entry, as one bit row per query block
+// over the union positions. ulist: [BH][ng][Nb], ucount: [BH][ng],
+// umask: [BH][ng][nw][kGroup] with nw = ceil(Nb / 32): bit p % 32 of umask[..][p / 32][qb]
+// is set when query block qb keeps union entry p (one step's words are contiguous).
 __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __restrict__ idx, int Nb, int ksel,
                                                            int ngroups, int32_t* __restrict__ ulist,
                                                            uint32_t* __restrict__ umask,
                                                            int32_t* __restrict__ ucount) {
   __shared__ uint32_t s_flags[kUnionRange][kMaskWords];
+  __shared__ int32_t s_pos[kUnionRange];  // key block (in the range) of each new union entry
   __shared__ int s_tmp[8];
   const int bh = blockIdx.x / ngroups, grp = blockIdx.x % ngroups, t = threadIdx.x;
   const int q0 = grp * kGroup, nq = min(kGroup, Nb - q0);
   const size_t gbase = (size_t)bh * ngroups + grp;
+  const int nw = (Nb + 31) / 32;
+  uint32_t* mrow = umask + gbase * kGroup * nw;
+  for (int e = t; e < kGroup * nw; e += 256) mrow[e] = 0u;
   int count = 0;
   for (int r0 = 0; r0 < Nb; r0 += kUnionRange) {
     const int rl = min(kUnionRange, Nb - r0);
@@ -72,15 +78,41 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
       if (k < w) off += s_tmp[k];
       tot += s_tmp[k];
     }
-    int pos = count + off + incl - n;
+    int pos = off + incl - n;  // within this range
     for (int j = j0; j < j1; j++) {
       if (!any(j)) continue;
-      ulist[gbase * Nb + pos] = r0 + j;
-      uint4* dst = (uint4*)(umask + (gbase * Nb + pos) * kMaskWords);
-#pragma unroll
-      for (int x = 0; x < kMaskWords / 4; x++)
-        dst[x] = make_uint4(s_flags[j][4 * x], s_flags[j][4 * x + 1], s_flags[j][4 * x + 2], s_flags[j][4 * x + 3]);
+      ulist[gbase * Nb + count + pos] = r0 + j;
+      s_pos[pos] = j;
       pos++;
+    }
+    __syncthreads();
+    // bit rows: word wd of query block qb covers union positions 32 wd .. 32 wd + 31; the
+    // words at the range's ends are shared with the neighbouring ranges (atomic OR).
+    // Each half-wave takes one (wd, 32 query blocks) tile, a 32 x 32 bit transpose done
+    // with ballots: lane i holds the query-block word of position 32 wd + i, and ballot b
+    // gathers bit b (query block) over the 32 positions.
+    if (tot > 0) {
+      const int w0 = count >> 5, w1 = (count + tot - 1) >> 5, nwr = w1 - w0 + 1;
+      const int ntile = nwr * kMaskWords, i = lane & 31, hw = lane >> 5;
+      for (int base = 2 * w; base < ntile; base += 8) {  // 4 waves x 2 halves
+        const int tile = base + hw;
+        uint32_t word = 0u;
+        int wd = 0, qw = 0;
+        if (tile < ntile) {
+          wd = w0 + tile / kMaskWords;
+          qw = tile % kMaskWords;
+          const int p = 32 * wd + i - count;
+          if (p >= 0 && p < tot) word = s_flags[s_pos[p]][qw];
+        }
+        uint32_t mine = 0u;
+#pragma unroll
+        for (int b = 0; b < 32; b++) {
+          const unsigned long long m = __ballot((word >> b) & 1u);
+          if (i == b) mine = hw ? (uint32_t)(m >> 32) : (uint32_t)m;
+        }
+        const int qb = 32 * qw + i;
+        if (tile < ntile && mine && qb < nq) atomicOr(&mrow[(size_t)wd * kGroup + qb], mine);
+      }
     }
     count += tot;
     __syncthreads();
@@ -92,6 +124,7 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
 
 constexpr int kBp = 72;     // LDS row pitch (bf16) of a [state][64 columns] operand tile: 144 B
 constexpr int kMgSlots = 4;  // steps of 32 union entries in flight (registers, then LDS)
+constexpr int kUlChunk = 1024;  // union-list entries per LDS chunk
 typedef short v4s_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
 
@@ -113,8 +146,10 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
     const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
     uint16_t* __restrict__ hc) {
   __shared__ __attribute__((aligned(16))) uint16_t s_b[kMgSlots][32 * kBp];
-  __shared__ uint32_t s_m[kMgSlots][32][kMaskWords];
+  __shared__ uint32_t s_m[kMgSlots][kGroup];  // per step: the 32 union entries' bits of each query block
+  __shared__ v8s s_lut[256];                  // byte -> its 8 bits as bf16 0.0 / 1.0
   __shared__ __attribute__((aligned(16))) uint16_t s_out[kGroup / 2 * 64];
+  __shared__ int32_t s_ul[2][kUlChunk];  // union list, two chunks of kUlChunk entries
 
   const int per_bh = ngroups * 129 * 2;
   const int bh = blockIdx.x / per_bh, rem = blockIdx.x % per_bh;
@@ -122,7 +157,8 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
   const size_t gbase = (size_t)bh * ngroups + grp;
   const int U = ucount[gbase];
   const int32_t* ul = ulist + gbase * Nb;
-  const uint32_t* um = umask + gbase * Nb * kMaskWords;
+  const int nw = (Nb + 31) / 32;
+  const uint32_t* um = umask + gbase * kGroup * nw;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, kg = lane >> 4;
 
   v4f_ acc[4][4];
@@ -132,35 +168,41 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
     for (int n = 0; n < 4; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (U + 31) / 32;
+  // The union list goes through LDS in chunks of kUlChunk entries, each staged one step
+  // before the first state load that needs it, so that no state load waits on a
+  // dependent global load of its index.
+  auto fill_ul = [&](int chunk) {
+    for (int e = t; e < kUlChunk; e += 256) {
+      const int u = chunk * kUlChunk + e;
+      s_ul[chunk & 1][e] = u < U ? ul[u] : 0;
+    }
+  };
   // 32 states x 64 columns per step: thread t holds 16 B (8 columns) of state t/8, and
-  // one mask word (entry t/8, word t%8); stored row-major ([state][column]) into LDS the
-  // step before use. The MFMA B operand (8 consecutive states of one column) comes from
-  // transposing reads.
+  // the step's mask word of query block t; stored row-major ([state][column]) into LDS
+  // the step before use. The MFMA B operand (8 consecutive states of one column) comes
+  // from transposing reads.
   uint4 pre[kMgSlots];
   uint32_t pmask[kMgSlots];
   const size_t col0 = (size_t)c * kD + 64 * half + (t & 7) * 8;
   auto load = [&](int slot, int step) {
     const int u = step * 32 + (t >> 3);
     pre[slot] = make_uint4(0, 0, 0, 0);
-    pmask[slot] = 0u;
     if (u < U) {
-      pre[slot] = *(const uint4*)(hs + ((size_t)bh * Nb + ul[u]) * kStateElems + col0);
-      pmask[slot] = um[(size_t)u * kMaskWords + (t & 7)];
+      const int j = s_ul[(u / kUlChunk) & 1][u % kUlChunk];
+      pre[slot] = *(const uint4*)(hs + ((size_t)bh * Nb + j) * kStateElems + col0);
     }
+    pmask[slot] = um[(size_t)step * kGroup + t];
   };
   auto store = [&](int slot) {
     *(uint4*)(&s_b[slot][(t >> 3) * kBp + (t & 7) * 8]) = pre[slot];
-    s_m[slot][t >> 3][t & 7] = pmask[slot];
+    s_m[slot][t] = pmask[slot];
   };
   auto step_body = [&](int slot) {
-    // A operand: rows = query blocks 64w + 16m + l16, k = union entries 8kg .. 8kg+7
+    // A operand: rows = query blocks 64w + 16m + l16, k = union entries 8kg .. 8kg+7:
+    // byte kg of the query block's step word, expanded through the table
     v8s a[4];
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-      const int word = 2 * w + (m >> 1), bit = 16 * (m & 1) + l16;
-#pragma unroll
-      for (int x = 0; x < 8; x++) a[m][x] = ((s_m[slot][8 * kg + x][word] >> bit) & 1u) ? (short)0x3F80 : (short)0;
-    }
+    for (int m = 0; m < 4; m++) a[m] = s_lut[(s_m[slot][64 * w + 16 * m + l16] >> (8 * kg)) & 255u];
     // lane (kg, l16): states 8kg..8kg+7 of column 16n + l16, as two 4 x 16 transposes
     const int ta = l16 >> 2, tb = l16 & 3;
 #pragma unroll
@@ -174,6 +216,15 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[m]), b, acc[m][n], 0, 0, 0);
     }
   };
+  static_assert(kUlChunk % 32 == 0 && kUlChunk >= 32 * (kMgSlots + 1), "chunk holds whole steps");
+  {
+    v8s e;
+#pragma unroll
+    for (int x = 0; x < 8; x++) e[x] = ((t >> x) & 1) ? (short)0x3F80 : (short)0;  // bf16 1.0
+    s_lut[t] = e;
+  }
+  fill_ul(0);
+  __syncthreads();
 #pragma unroll
   for (int p = 0; p < kMgSlots; p++)
     if (p < nsteps) load(p, p);
@@ -187,6 +238,9 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
       const int step = s0 + ph;
       if (step < nsteps) {
         if (step + kMgSlots < nsteps) load(ph, step + kMgSlots);
+        // the next step loads step + kMgSlots + 1: stage its chunk now if it starts one
+        const int un = (step + kMgSlots + 1) * 32;
+        if (un < U && un % kUlChunk == 0) fill_ul(un / kUlChunk);
         step_body(ph);
         if (step + 1 < nsteps) store((ph + 1) % kMgSlots);
       }

@@ -100,11 +100,12 @@ def test_stage_parity(name):
                 want = sorted(set(np.concatenate([gidx[i] for i in rows]).tolist()))
                 cnt = int(g["ucount"][bh][grp])
                 assert cnt == len(want) and list(g["ulist"][bh][grp][:cnt]) == want
-                um = g["umask"][bh][grp][:cnt].view(np.uint32)
-                for u, j in enumerate(want):
-                    keepers = [i for i in rows if j in set(gidx[i].tolist())]
-                    got = [G * grp + 32 * wd + bb for wd in range(G // 32) for bb in range(32) if (um[u][wd] >> bb) & 1]
-                    assert got == keepers
+                um = g["umask"][bh][grp].view(np.uint32).T  # [G][ceil(Nb/32)]: bit p of row qb
+                for qi, i in enumerate(rows):
+                    kept_i = set(gidx[i].tolist())
+                    got = [p for p in range(32 * um.shape[1]) if (um[qi][p // 32] >> (p % 32)) & 1]
+                    assert got == [p for p, j in enumerate(want) if j in kept_i]
+                assert not um[len(rows):].any()
             # complement states: total minus the kept blocks (with the GPU's kept sets)
             for i in range(Nb):
                 keep = np.zeros(Nb, bool)
