@@ -443,23 +443,36 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
 
 int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
 
-hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
-                                    const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
-                                    void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
+hipError_t launch_linear_union(const void* idx, int BH, int Nb, int ksel, void* ulist, void* umask, void* ucount,
+                              hipStream_t st) {
   const int ng = linear_groups(Nb);
   hipLaunchKernelGGL(linear_union_kernel, dim3(BH * ng), dim3(256), 0, st, (const int32_t*)idx, Nb, ksel, ng,
                      (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot, const void* proj, int BH, int N,
+                                int Nb, const void* ulist, const void* umask, const void* ucount, void* hc, void* y,
+                                hipStream_t st) {
+  const int ng = linear_groups(Nb);
   hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
                      (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
                      Nb, ng, (uint16_t*)hc);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
   const int per_xcd = (groups + 7) / 8;
   hipLaunchKernelGGL(linear_out_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)hc, (const uint16_t*)proj, N, Nb, groups, per_xcd, (uint16_t*)y);
   return hipGetLastError();
+}
+
+hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
+                                    const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
+                                    void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
+  hipError_t e = launch_linear_union(idx, BH, Nb, ksel, ulist, umask, ucount, st);
+  if (e != hipSuccess) return e;
+  return launch_linear_masked(q, hs, htot, proj, BH, N, Nb, ulist, umask, ucount, hc, y, st);
 }
 
 }  // namespace sagesla

@@ -19,6 +19,48 @@ __device__ __forceinline__ uint32_t ord_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Scores of up to 8 query-block rows (qbar in LDS, fp64) against key blocks j0 + 256 q,
+// q < JT (JT <= 6): s = sum_c qbar[r][c] kbar[c][j] in channel order with fused multiply-adds,
+// divided by sqrt(d) (one rounding), and stored as order-preserving fp32 keys.
+template <int JT>
+__device__ __forceinline__ void score_pass(const double* __restrict__ kb, const double (*s_qb)[kD],
+                                           uint32_t* s_keys, int Nb, int nr, int j0) {
+  const double inv_sqrt_d = 1.0 / sqrt((double)kD);
+  double acc[JT][8];
+#pragma unroll
+  for (int q = 0; q < JT; q++)
+#pragma unroll
+    for (int r = 0; r < 8; r++) acc[q][r] = 0.0;
+#pragma unroll 2
+  for (int c = 0; c < kD; c += 2) {
+    double kv[JT][2];
+#pragma unroll
+    for (int q = 0; q < JT; q++) {
+      const int j = j0 + q * kSelThreads;
+      kv[q][0] = j < Nb ? kb[(size_t)c * Nb + j] : 0.0;
+      kv[q][1] = j < Nb ? kb[(size_t)(c + 1) * Nb + j] : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const double2 qv = *(const double2*)&s_qb[r][c];  // one 16-byte broadcast read
+#pragma unroll
+      for (int q = 0; q < JT; q++) {
+        acc[q][r] = __fma_rn(qv.x, kv[q][0], acc[q][r]);
+        acc[q][r] = __fma_rn(qv.y, kv[q][1], acc[q][r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < JT; q++) {
+    const int j = j0 + q * kSelThreads;
+    if (j < Nb) {
+#pragma unroll
+      for (int r = 0; r < 8; r++)
+        if (r < nr) s_keys[r * Nb + j] = ord_key((float)(acc[q][r] * inv_sqrt_d));
+    }
+  }
+}
+
 // R query blocks of one head per workgroup (4 waves). Dynamic LDS: keys [R][Nb] uint32.
 // Phase 1: all threads score the R rows against every key block (4 key blocks per
 // thread in flight). Phase 2: one wave per row selects, with a wave-private histogram
@@ -28,7 +70,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
                                                              int ksel, int R, int groups,
                                                              int32_t* __restrict__ idx) {
   extern __shared__ uint32_t s_keys[];  // [R][Nb]
-  __shared__ double s_qb[8][kD];
+  __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
   __shared__ uint32_t s_hist[4][256];
 
   const int bh = blockIdx.x / groups, g0 = (blockIdx.x % groups) * R;
@@ -38,39 +80,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
     s_qb[e / kD][e % kD] = qbar[((size_t)bh * Nb + g0 + e / kD) * kD + e % kD];
   __syncthreads();
 
-  // ---- phase 1: scores (fp64, channel order fixed), keys = order-preserving fp32 bits
-  const double inv_sqrt_d = 1.0 / sqrt((double)kD);
+  // ---- phase 1: scores (fp64, channel order fixed), keys = order-preserving fp32 bits.
+  // Thread t scores key blocks t + 256 q; the ceil(Nb / 256) blocks per thread are taken
+  // in the fewest balanced passes of at most 6.
   const double* kb = kbart + (size_t)bh * kD * Nb;
-  constexpr int JT = 4;
-  for (int j0 = t; j0 < Nb; j0 += kSelThreads * JT) {
-    double acc[JT][8];
-#pragma unroll
-    for (int q = 0; q < JT; q++)
-#pragma unroll
-      for (int r = 0; r < 8; r++) acc[q][r] = 0.0;
-#pragma unroll 4
-    for (int c = 0; c < kD; c++) {
-      double kv[JT];
-#pragma unroll
-      for (int q = 0; q < JT; q++) {
-        const int j = j0 + q * kSelThreads;
-        kv[q] = j < Nb ? kb[(size_t)c * Nb + j] : 0.0;
-      }
-#pragma unroll
-      for (int r = 0; r < 8; r++) {
-        const double qv = s_qb[r][c];
-#pragma unroll
-        for (int q = 0; q < JT; q++) acc[q][r] = __fma_rn(qv, kv[q], acc[q][r]);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < JT; q++) {
-      const int j = j0 + q * kSelThreads;
-      if (j < Nb) {
-#pragma unroll
-        for (int r = 0; r < 8; r++)
-          if (r < nr) s_keys[r * Nb + j] = ord_key((float)(acc[q][r] * inv_sqrt_d));
-      }
+  const int kpt = (Nb + kSelThreads - 1) / kSelThreads;
+  const int npass = (kpt + 5) / 6, jt = (kpt + npass - 1) / npass;
+  for (int q0 = 0; q0 < kpt; q0 += jt) {
+    const int n = min(jt, kpt - q0);
+    switch (n) {
+      case 1: score_pass<1>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
+      case 2: score_pass<2>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
+      case 3: score_pass<3>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
+      case 4: score_pass<4>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
+      case 5: score_pass<5>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
+      default: score_pass<6>(kb, s_qb, s_keys, Nb, nr, t + q0 * kSelThreads); break;
     }
   }
   __syncthreads();
