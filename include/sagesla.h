@@ -145,7 +145,9 @@ sagesla_status sagesla_linear_total(const void *hpart, int B, int H, int N, int 
 
 /* Linear branch: per group of 256 query blocks the union of their kept sets (ulist,
  * umask, ucount), the complement states hc = S_total - sum_kept S_j (a 0/1-mask product
- * on the matrix cores), and y = O_l W with O_l = phi(q) H^c / (phi(q) . z^c). */
+ * on the matrix cores), and y = O_l W with O_l = phi(q) H^c / (phi(q) . z^c). When more
+ * than half the blocks are kept (2 ksel > Nb) the lists and masks describe the blocks
+ * NOT kept and hc is their direct sum (no cancellation against the total). */
 sagesla_status sagesla_linear_complement(const void *q, const void *idx, const void *hs,
                                          const void *htot, const void *proj, int B, int H,
                                          int N, int d, int block, double topk, void *ulist,

@@ -27,8 +27,12 @@ constexpr int kUnionRange = 1024;  // key blocks per LDS pass of the union kerne
 // over the union positions. ulist: [BH][ng][Nb], ucount: [BH][ng],
 // umask: [BH][ng][nw][kGroup] with nw = ceil(Nb / 32): bit p % 32 of umask[..][p / 32][qb]
 // is set when query block qb keeps union entry p (one step's words are contiguous).
+// complement != 0 (more than half the blocks kept): the same for the blocks NOT kept,
+// so that the complement is summed directly instead of as total - kept (which would
+// cancel almost all of the total and leave the bf16 rounding of the kept states).
 __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __restrict__ idx, int Nb, int ksel,
-                                                           int ngroups, int32_t* __restrict__ ulist,
+                                                           int ngroups, int complement,
+                                                           int32_t* __restrict__ ulist,
                                                            uint32_t* __restrict__ umask,
                                                            int32_t* __restrict__ ucount) {
   __shared__ uint32_t s_flags[kUnionRange][kMaskWords];
@@ -54,10 +58,19 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
     __syncthreads();
     // compact the non-empty entries in ascending order: thread t owns a contiguous range
     const int per = (rl + 255) / 256, j0 = t * per, j1 = min(rl, j0 + per);
+    // membership bits of entry j for query-block word x: kept, or (complement) not kept
+    // by one of the group's nq query blocks
+    auto bits_of = [&](int j, int x) {
+      const uint32_t f = s_flags[j][x];
+      if (!complement) return f;
+      const int lo = 32 * x;
+      const uint32_t valid = nq >= lo + 32 ? 0xFFFFFFFFu : (nq <= lo ? 0u : (1u << (nq - lo)) - 1u);
+      return ~f & valid;
+    };
     auto any = [&](int j) {
       uint32_t o = 0u;
 #pragma unroll
-      for (int x = 0; x < kMaskWords; x++) o |= s_flags[j][x];
+      for (int x = 0; x < kMaskWords; x++) o |= bits_of(j, x);
       return o != 0u;
     };
     int n = 0;
@@ -102,7 +115,7 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
           wd = w0 + tile / kMaskWords;
           qw = tile % kMaskWords;
           const int p = 32 * wd + i - count;
-          if (p >= 0 && p < tot) word = s_flags[s_pos[p]][qw];
+          if (p >= 0 && p < tot) word = bits_of(s_pos[p], qw);
         }
         uint32_t mine = 0u;
 #pragma unroll
@@ -144,7 +157,7 @@ __device__ __forceinline__ v4s_ lds_read_tr16(const uint16_t* p) {
 __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
     const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
     const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
-    uint16_t* __restrict__ hc) {
+    int complement, uint16_t* __restrict__ hc) {
   __shared__ __attribute__((aligned(16))) uint16_t s_b[kMgSlots][32 * kBp];
   __shared__ uint32_t s_m[kMgSlots][kGroup];  // per step: the 32 union entries' bits of each query block
   __shared__ v8s s_lut[256];                  // byte -> its 8 bits as bf16 0.0 / 1.0
@@ -247,7 +260,8 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
       __syncthreads();
     }
   }
-  // hc = htot - M, staged through LDS (two halves of kGroup/2 query blocks) for 16-byte stores
+  // hc = htot - M (kept sets) or M (complement sets), staged through LDS (two halves of
+  // kGroup/2 query blocks) for 16-byte stores
   const float* ht = htot + (size_t)bh * kStateElems + c * kD + 64 * half;
   const int q0 = grp * kGroup;
 #pragma unroll
@@ -256,13 +270,14 @@ __global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
 #pragma unroll
       for (int n = 0; n < 4; n++) {
         const int col = 16 * n + l16;
-        const float tot = ht[col];
+        const float tot = complement ? 0.f : ht[col];
+        const float sgn = complement ? 1.f : -1.f;
 #pragma unroll
         for (int m = 0; m < 4; m++)
 #pragma unroll
           for (int v = 0; v < 4; v++) {
             const int qi = 64 * (w & 1) + 16 * m + 4 * kg + v;  // within the half
-            s_out[qi * 64 + col] = f32_to_bf16(tot - acc[m][n][v]);
+            s_out[qi * 64 + col] = f32_to_bf16(tot + sgn * acc[m][n][v]);
           }
       }
     }
@@ -443,21 +458,25 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
 
 int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
 
+// The complement is summed directly over the blocks not kept when those are fewer than
+// the kept ones (see linear_union_kernel).
+static int use_complement_sets(int Nb, int ksel) { return 2 * ksel > Nb; }
+
 hipError_t launch_linear_union(const void* idx, int BH, int Nb, int ksel, void* ulist, void* umask, void* ucount,
                               hipStream_t st) {
   const int ng = linear_groups(Nb);
   hipLaunchKernelGGL(linear_union_kernel, dim3(BH * ng), dim3(256), 0, st, (const int32_t*)idx, Nb, ksel, ng,
-                     (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
+                     use_complement_sets(Nb, ksel), (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
   return hipGetLastError();
 }
 
 hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot, const void* proj, int BH, int N,
-                                int Nb, const void* ulist, const void* umask, const void* ucount, void* hc, void* y,
-                                hipStream_t st) {
+                                int Nb, int ksel, const void* ulist, const void* umask, const void* ucount, void* hc,
+                                void* y, hipStream_t st) {
   const int ng = linear_groups(Nb);
   hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
                      (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
-                     Nb, ng, (uint16_t*)hc);
+                     Nb, ng, use_complement_sets(Nb, ksel), (uint16_t*)hc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
@@ -472,7 +491,7 @@ hipError_t launch_linear_complement(const void* q, const void* idx, const void* 
                                     void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
   hipError_t e = launch_linear_union(idx, BH, Nb, ksel, ulist, umask, ucount, st);
   if (e != hipSuccess) return e;
-  return launch_linear_masked(q, hs, htot, proj, BH, N, Nb, ulist, umask, ucount, hc, y, st);
+  return launch_linear_masked(q, hs, htot, proj, BH, N, Nb, ksel, ulist, umask, ucount, hc, y, st);
 }
 
 }  // namespace sagesla

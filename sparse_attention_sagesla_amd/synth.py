@@ -79,7 +79,7 @@ CONFIGS = {
 
 
 def scaled(cfg: Config, H: int | None = None, grid: tuple | None = None, seed: int | None = None,
-           topk: float | None = None, name: str | None = None) -> Config:
+           topk: float | None = None, name: str | None = None, linear: bool | None = None) -> Config:
     """A copy of ``cfg`` with fewer heads / a smaller grid (same recipe), for quick tests."""
     from dataclasses import replace
     kw = {}
@@ -91,6 +91,8 @@ def scaled(cfg: Config, H: int | None = None, grid: tuple | None = None, seed: i
         kw["seed"] = seed
     if topk is not None:
         kw["topk"] = topk
+    if linear is not None:
+        kw["linear"] = linear
     kw["name"] = name or (cfg.name + "-scaled")
     return replace(cfg, **kw)
 

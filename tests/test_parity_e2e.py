@@ -19,7 +19,12 @@ from _helpers import cos, mask_mismatch
 
 pytestmark = pytest.mark.gpu
 
-NAMES = ["wan1.3b-480p", "wan14b-480p", "wan14b-720p", "i2v-a14b-720p", "i2v-a14b-720p-dense"]
+NAMES = ["wan1.3b-480p", "wan14b-480p", "wan14b-720p", "i2v-a14b-720p", "i2v-a14b-720p-dense",
+         "long-sequence"]
+# one head of a 2^18-token sequence (4096 key blocks): several passes of the union and
+# selection kernels and union lists longer than one LDS chunk
+EXTRA = {"long-sequence": synth.scaled(synth.CONFIGS["wan14b-720p"], H=1, grid=(16, 64, 256), seed=41,
+                                       name="long-sequence")}
 
 
 def sample_blocks(Nb, seed):
@@ -31,7 +36,7 @@ def sample_blocks(Nb, seed):
 
 @pytest.mark.parametrize("name", NAMES)
 def test_full_size_sampled(name):
-    cfg = synth.CONFIGS[name]
+    cfg = EXTRA[name] if name in EXTRA else synth.CONFIGS[name]
     N, Nb = cfg.N, O.num_blocks(cfg.N)
     print("\n[case] %s: B=%d H=%d N=%d topk=%g" % (name, cfg.B, cfg.H, N, cfg.topk), flush=True)
     x = synth.make_inputs(cfg, device="cuda")

@@ -29,6 +29,12 @@ CASES = {
     "ksel-1": (synth.CONFIGS["wan1.3b-480p"], dict(H=2, grid=(2, 16, 40), topk=1e-6, seed=25)),
     # more query blocks than one complement group holds (300 blocks: groups of 256 + 44)
     "two-groups": (synth.CONFIGS["wan1.3b-480p"], dict(H=1, grid=(3, 10, 640), seed=26)),
+    # edge cases: one token; exactly one full block; a complement of a single block
+    # (ksel = Nb - 1); the linear branch off with sparse selection (no projection)
+    "single-token": (synth.CONFIGS["tiny"], dict(H=1, grid=(1, 1, 1), seed=28)),
+    "exact-block": (synth.CONFIGS["tiny"], dict(H=1, grid=(1, 1, 64), seed=29)),
+    "one-block-linear": (synth.CONFIGS["wan1.3b-480p"], dict(H=1, grid=(1, 4, 80), topk=0.8, seed=30)),
+    "linear-off": (synth.CONFIGS["wan1.3b-480p"], dict(H=2, grid=(2, 8, 40), topk=0.2, seed=31, linear=False)),
 }
 
 
@@ -94,17 +100,20 @@ def test_stage_parity(name):
             assert np.max(np.abs(g["htot"][bh] - tot)) <= 1e-5 * np.max(np.abs(tot))
             # union of each group's kept sets, with the per-query-block masks
             gidx = g["idx"][bh]
+            # (the blocks NOT kept when more than half are kept)
             G = S.GROUP
+            comp = 2 * ksel > Nb
+            member = [(set(range(Nb)) - set(gidx[i].tolist())) if comp else set(gidx[i].tolist())
+                      for i in range(Nb)]
             for grp in range((Nb + G - 1) // G):
                 rows = range(G * grp, min(Nb, G * grp + G))
-                want = sorted(set(np.concatenate([gidx[i] for i in rows]).tolist()))
+                want = sorted(set().union(*(member[i] for i in rows)))
                 cnt = int(g["ucount"][bh][grp])
                 assert cnt == len(want) and list(g["ulist"][bh][grp][:cnt]) == want
                 um = g["umask"][bh][grp].view(np.uint32).T  # [G][ceil(Nb/32)]: bit p of row qb
                 for qi, i in enumerate(rows):
-                    kept_i = set(gidx[i].tolist())
                     got = [p for p in range(32 * um.shape[1]) if (um[qi][p // 32] >> (p % 32)) & 1]
-                    assert got == [p for p, j in enumerate(want) if j in kept_i]
+                    assert got == [p for p, j in enumerate(want) if j in member[i]]
                 assert not um[len(rows):].any()
             # complement states: total minus the kept blocks (with the GPU's kept sets)
             for i in range(Nb):
