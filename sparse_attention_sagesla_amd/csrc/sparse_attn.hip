@@ -38,8 +38,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Per-wave state of the online softmax for 32 query rows (one per lane pair l, l^32).
 struct RowState {
-  float m, l;   // running max and running sum of the FP8 weights
+  float m, l;   // running max; sum of the FP8 weights (filled in at the end)
   v16f acc[4];  // O^T accumulators (4 tiles of 32 channels)
+  v4f lacc;     // running row sums on the matrix cores: lanes 0..15, element 0 (query l), 1 (query l + 16)
 };
 
 // Online softmax of one 64-key tile (S^T accumulators) -> FP8 probabilities in the
@@ -70,7 +71,10 @@ __device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a,
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
 #pragma unroll
     for (int d = 0; d < 4; d++) st.acc[d] *= alpha;
-    st.l *= alpha;
+    // lane j < 16 holds the sums of queries j (element 0) and j + 16 (element 1)
+    const float alpha_hi = __shfl(alpha, (__lane_id() & 15) + 16);
+    st.lacc[0] *= alpha;
+    st.lacc[1] *= alpha_hi;
   }
   st.m = mn;
   // 448 p = 2^fma(S, a, log2(448) - m'). For the row maximum the fused product may land
@@ -146,11 +150,18 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   RowState st;
   st.m = -INFINITY;
   st.l = 0.f;
+  st.lacc = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int d = 0; d < 4; d++) st.acc[d] = (v16f){};
 
-  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                    0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // Row sums on v_mfma_f32_16x16x128_f8f6f4 with P8 as its B operand: lane l's 32 bytes
+  // are column l % 16 over keys 32 (l / 16) .., and lane l holds query l % 32. The A
+  // operand (lane l: row l % 16 over keys 32 (l / 16) ..) is e4m3 1.0 in row 0 over the
+  // key ranges of lanes 0..15 and 32..47 (queries 0..15) and in row 1 over those of lanes
+  // 16..31 and 48..63 (queries 16..31), zero elsewhere: result rows 0 and 1 are the sums.
+  const int lr = l & 15, lq = (l >> 4) & 1;
+  const int one8 = ((lr == 0 && lq == 0) || (lr == 1 && lq == 1)) ? 0x38383838 : 0;
+  const v8i lsel = {one8, one8, one8, one8, one8, one8, one8, one8};
 
   // one kept block: tile in (ck, cv), next block's DMA into (nk, nv)
   auto step = [&](int u, const uint8_t* ck, const uint8_t* cv, uint8_t* nk, uint8_t* nv) {
@@ -185,10 +196,8 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
 #pragma unroll
     for (int d = 0; d < 4; d++)
       st.acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[d], pb, st.acc[d], 0, 0, 0, 0, 0, 0);
-    // this block's row sums of the FP8 weights on the matrix cores (every element of
-    // the tile holds the sum for the lane's query)
-    const v16f lblk = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, (v16f){}, 0, 0, 0, 0, 0, 0);
-    st.l += lblk[0];
+    // this block's row sums of the FP8 weights, accumulated on the matrix cores
+    st.lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(lsel, pb, st.lacc, 0, 0, 0, 0, 0, 0);
   };
 
   int u = 0;
@@ -198,6 +207,11 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   }
   if (u < ksel) step(u, s_k0, s_v0, s_k1, s_v1);
 
+  {
+    // query r's sum: lane r & 15, element 0 for r < 16, element 1 otherwise
+    const float l0 = __shfl(st.lacc[0], r & 15), l1 = __shfl(st.lacc[1], r & 15);
+    st.l = r < 16 ? l0 : l1;
+  }
   const float inv_l = 1.0f / st.l;
   const int qrow = i * kBlk + 32 * w + r;
   if (qrow < N) {
