@@ -44,17 +44,8 @@ struct RowState {
 };
 
 // Online softmax of one 64-key tile (S^T accumulators) -> FP8 probabilities in the
-// B-operand layout of O^T = V8^T P8^T.
-// MASK: the tile is the partial last block; keys at or past nvalid take no part.
-template <bool MASK>
-__device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a, int g, int nvalid) {
-  if (MASK) {
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-      for (int v = 0; v < 16; v++)
-        if (key_of_slot(g, tt, v) >= nvalid) S[tt][v] = INT_MIN;
-  }
+// B-operand layout of O^T = V8^T P8^T. Keys masked out hold INT_MIN.
+__device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a) {
   int mx = INT_MIN;
 #pragma unroll
   for (int tt = 0; tt < 2; tt++)
@@ -90,7 +81,6 @@ __device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a,
       for (int e = 0; e < 4; e++) {
         const int sv = S[tt][4 * v4 + e];
         p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, a, bias));
-        if (MASK && sv == INT_MIN) p[e] = 0.f;
       }
       int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
@@ -191,8 +181,31 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
       for (int s = 0; s < 4; s++) S[tt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[tt][s], qb[s], S[tt], 0, 0, 0);
     }
     const float a = (sqi * sk[hb + j]) * c0;
-    const v8i pb = (j == Nb - 1 && nlast < kBlk) ? softmax_tile<true>(st, S, a, g, nlast)
-                                                 : softmax_tile<false>(st, S, a, g, kBlk);
+    // The partial last block: keys at or past nlast take no part. Their scores are set
+    // to INT_MIN before the softmax (out of the row maximum) and their FP8 weights to
+    // zero after it. (One softmax body for both cases: a second copy of it doubles the
+    // loop's register demand.)
+    const bool partial = j == Nb - 1 && nlast < kBlk;
+    if (partial) {
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int v = 0; v < 16; v++)
+          if (key_of_slot(g, tt, v) >= nlast) S[tt][v] = INT_MIN;
+    }
+    v8i pb = softmax_tile(st, S, a);
+    if (partial) {
+#pragma unroll
+      for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; v4++) {
+          uint32_t keep = 0u;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            if (key_of_slot(g, tt, 4 * v4 + e) < nlast) keep |= 0xFFu << (8 * e);
+          pb[4 * tt + v4] &= (int)keep;
+        }
+    }
 #pragma unroll
     for (int d = 0; d < 4; d++)
       st.acc[d] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[d], pb, st.acc[d], 0, 0, 0, 0, 0, 0);

@@ -193,3 +193,25 @@ def test_batch_of_two():
         for h in range(2):
             r = O.sagesla_head(bits["q"][b, h], bits["k"][b, h], bits["v"][b, h], w, cfg.topk)
             assert cos(o[b, h], r["out"][:cfg.N]) >= 0.9995
+
+
+@pytest.mark.parametrize("grid", [(1, 1, 37), (4, 20, 33)])
+def test_small_scores_partial_block(grid):
+    """Q and K scaled by 2^-10: the logit scale a = s_q s_k / sqrt(d) log2(e) falls near
+    1e-10, where a masked key's INT_MIN score no longer underflows the exponent on its own.
+    The keys past N in the partial last block must still take no part. (A power-of-two
+    factor leaves the pooled means, the scores' order and the INT8 codes unchanged.)"""
+    cfg = synth.scaled(synth.CONFIGS["wan14b-720p"], H=2, grid=grid, seed=32)
+    print("\n[case] small scores N=%d" % cfg.N, flush=True)
+    x = synth.make_inputs(cfg, device="cuda")
+    for n in ("q", "k"):
+        x[n] = x[n] * 2.0 ** -10
+    out = S.fwd(x["q"], x["k"], x["v"], x["proj"], topk=cfg.topk)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy()
+    bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
+    w = synth.bf16_bits(x["proj"])
+    for h in range(cfg.H):
+        r = O.sagesla_head(bits["q"][0, h], bits["k"][0, h], bits["v"][0, h], w, cfg.topk, quant=True)
+        assert cos(o[0, h], r["out"][:cfg.N]) >= 0.9995
+        assert np.max(np.abs(o[0, h] - r["out"][:cfg.N])) <= 2e-2
