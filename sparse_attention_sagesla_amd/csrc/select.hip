@@ -31,14 +31,31 @@ __device__ __forceinline__ void score_pass(const double* __restrict__ kb, const 
   for (int q = 0; q < JT; q++)
 #pragma unroll
     for (int r = 0; r < 8; r++) acc[q][r] = 0.0;
+  // The next channel pair's values are loaded while this pair's products run. Key
+  // blocks past Nb read block Nb - 1 (their scores are not stored), so that every load
+  // is unconditional.
+  const double* kp[JT];
+#pragma unroll
+  for (int q = 0; q < JT; q++) kp[q] = kb + min(j0 + q * kSelThreads, Nb - 1);
+  double kn[JT][2];
+#pragma unroll
+  for (int q = 0; q < JT; q++) {
+    kn[q][0] = kp[q][0];
+    kn[q][1] = kp[q][(size_t)Nb];
+  }
 #pragma unroll 2
   for (int c = 0; c < kD; c += 2) {
     double kv[JT][2];
 #pragma unroll
     for (int q = 0; q < JT; q++) {
-      const int j = j0 + q * kSelThreads;
-      kv[q][0] = j < Nb ? kb[(size_t)c * Nb + j] : 0.0;
-      kv[q][1] = j < Nb ? kb[(size_t)(c + 1) * Nb + j] : 0.0;
+      kv[q][0] = kn[q][0];
+      kv[q][1] = kn[q][1];
+    }
+    const int cn = c + 2 < kD ? c + 2 : c;
+#pragma unroll
+    for (int q = 0; q < JT; q++) {
+      kn[q][0] = kp[q][(size_t)cn * Nb];
+      kn[q][1] = kp[q][(size_t)(cn + 1) * Nb];
     }
 #pragma unroll
     for (int r = 0; r < 8; r++) {
