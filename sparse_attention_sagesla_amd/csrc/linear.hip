@@ -311,23 +311,25 @@ __device__ __forceinline__ v8bf tile_col8(const uint16_t* tile, int a0, int c0, 
 struct OutLoads {
   uint4 q[4];    // raw q: rows t/16 + 16 mm, channels 8 (t%16) .. +7
   v8bf sa[8];    // S^c rows 32 w + l%32, k-steps s: the A operands of num^T
-  float zc;      // z^c[t] (t < 128)
+  uint16_t zc;   // z^c[t % 128] (bf16; used by t < 128)
 };
 
 __device__ __forceinline__ void out_load(OutLoads& L, const uint16_t* q, const uint16_t* hc, int bh, int i, int N,
                                          int Nb, int t, int w, int lane) {
+  // Every load is unconditional (rows past the block's end repeat its last row; their
+  // results are never stored), so that the compiler's wait counts stay exact and the
+  // loads of the next block overlap this one's work.
   const int n = block_len(i, N), rg = t >> 4, ch = t & 15;
 #pragma unroll
   for (int mm = 0; mm < 4; mm++) {
-    const int row = rg + 16 * mm;
-    L.q[mm] = make_uint4(0, 0, 0, 0);
-    if (row < n) L.q[mm] = *(const uint4*)(q + ((size_t)bh * N + (size_t)i * kBlk + row) * kD + ch * 8);
+    const int row = min(rg + 16 * mm, n - 1);
+    L.q[mm] = *(const uint4*)(q + ((size_t)bh * N + (size_t)i * kBlk + row) * kD + ch * 8);
   }
   const uint16_t* S = hc + ((size_t)bh * Nb + i) * kStateElems;
   const int c = 32 * w + (lane & 31), g = lane >> 5;
 #pragma unroll
   for (int s = 0; s < 8; s++) L.sa[s] = *(const v8bf*)(S + c * kD + 16 * s + 8 * g);
-  L.zc = t < kD ? bf16_to_f32(S[kD * kD + t]) : 0.f;
+  L.zc = S[kD * kD + (t & (kD - 1))];
 }
 
 // One workgroup (256 threads, 4 waves) per kOutQB consecutive query blocks of one head:
@@ -353,17 +355,26 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, r = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-  OutLoads cur, nxt;
-  out_load(cur, q, hc, bh, i0, N, Nb, t, w, lane);
-  for (int e = t; e < kD * 16; e += 256) {
-    const int a = e >> 4, c8 = (e & 15) * 8;
-    *(uint4*)(s_w + a * kLs + c8) = *(const uint4*)(proj + a * kD + c8);
+  OutLoads la, lb;
+  out_load(la, q, hc, bh, i0, N, Nb, t, w, lane);
+  {
+    // W_proj: all of this thread's loads in flight before its stores
+    uint4 wv[kD * 16 / 256];
+#pragma unroll
+    for (int k = 0; k < kD * 16 / 256; k++) {
+      const int e = t + 256 * k, a = e >> 4, c8 = (e & 15) * 8;
+      wv[k] = *(const uint4*)(proj + a * kD + c8);
+    }
+#pragma unroll
+    for (int k = 0; k < kD * 16 / 256; k++) {
+      const int e = t + 256 * k, a = e >> 4, c8 = (e & 15) * 8;
+      *(uint4*)(s_w + a * kLs + c8) = wv[k];
+    }
   }
-  for (int i = i0; i < i1; i++) {
-    if (i + 1 < i1) out_load(nxt, q, hc, bh, i + 1, N, Nb, t, w, lane);
+  auto process = [&](const OutLoads& cur, int i) {
     const int n = block_len(i, N);
     __syncthreads();  // the previous block is done with s_a, s_zc, s_den
-    if (t < kD) s_zc[t] = cur.zc;
+    if (t < kD) s_zc[t] = bf16_to_f32(cur.zc);
     __syncthreads();
     // phi(q) rows (16 lanes per row) -> s_a; den = phi(q) . z^c in fp32
     {
@@ -452,7 +463,16 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
         }
       }
     }
-    cur = nxt;
+  };
+  // two load sets in turn: the next block's loads fly while this one is processed, and no
+  // register whose load is in flight is copied
+  for (int i = i0; i < i1; i += 2) {
+    if (i + 1 < i1) out_load(lb, q, hc, bh, i + 1, N, Nb, t, w, lane);
+    process(la, i);
+    if (i + 1 < i1) {
+      if (i + 2 < i1) out_load(la, q, hc, bh, i + 2, N, Nb, t, w, lane);
+      process(lb, i + 1);
+    }
   }
 }
 
