@@ -31,32 +31,22 @@ __device__ __forceinline__ void score_pass(const double* __restrict__ kb, const 
   for (int q = 0; q < JT; q++)
 #pragma unroll
     for (int r = 0; r < 8; r++) acc[q][r] = 0.0;
-  // The next channel pair's values are loaded while this pair's products run. Key
-  // blocks past Nb read block Nb - 1 (their scores are not stored), so that every load
-  // is unconditional.
+  // Key blocks past Nb read block Nb - 1 (their scores are not stored), so that every
+  // load is unconditional.
   const double* kp[JT];
 #pragma unroll
   for (int q = 0; q < JT; q++) kp[q] = kb + min(j0 + q * kSelThreads, Nb - 1);
-  double kn[JT][2];
+  // Two channel pairs in flight, in register sets A and B used in turn (a register whose
+  // load is in flight is never copied, which would make the compiler wait for it).
+  double ka[JT][2], kc[JT][2];
 #pragma unroll
   for (int q = 0; q < JT; q++) {
-    kn[q][0] = kp[q][0];
-    kn[q][1] = kp[q][(size_t)Nb];
+    ka[q][0] = kp[q][0];
+    ka[q][1] = kp[q][(size_t)Nb];
+    kc[q][0] = kp[q][(size_t)2 * Nb];
+    kc[q][1] = kp[q][(size_t)3 * Nb];
   }
-#pragma unroll 2
-  for (int c = 0; c < kD; c += 2) {
-    double kv[JT][2];
-#pragma unroll
-    for (int q = 0; q < JT; q++) {
-      kv[q][0] = kn[q][0];
-      kv[q][1] = kn[q][1];
-    }
-    const int cn = c + 2 < kD ? c + 2 : c;
-#pragma unroll
-    for (int q = 0; q < JT; q++) {
-      kn[q][0] = kp[q][(size_t)cn * Nb];
-      kn[q][1] = kp[q][(size_t)(cn + 1) * Nb];
-    }
+  auto fma_pair = [&](const double (&kv)[JT][2], int c) {
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const double2 qv = *(const double2*)&s_qb[r][c];  // one 16-byte broadcast read
@@ -65,6 +55,22 @@ __device__ __forceinline__ void score_pass(const double* __restrict__ kb, const 
         acc[q][r] = __fma_rn(qv.x, kv[q][0], acc[q][r]);
         acc[q][r] = __fma_rn(qv.y, kv[q][1], acc[q][r]);
       }
+    }
+  };
+  for (int c = 0; c < kD; c += 4) {
+    fma_pair(ka, c);
+    const int ca = c + 4 < kD ? c + 4 : c;  // (the last refills reload rows already read)
+#pragma unroll
+    for (int q = 0; q < JT; q++) {
+      ka[q][0] = kp[q][(size_t)ca * Nb];
+      ka[q][1] = kp[q][(size_t)(ca + 1) * Nb];
+    }
+    fma_pair(kc, c + 2);
+    const int cc = c + 6 < kD ? c + 6 : c + 2;
+#pragma unroll
+    for (int q = 0; q < JT; q++) {
+      kc[q][0] = kp[q][(size_t)cc * Nb];
+      kc[q][1] = kp[q][(size_t)(cc + 1) * Nb];
     }
   }
 #pragma unroll
