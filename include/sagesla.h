@@ -161,6 +161,48 @@ sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k
                                    const void *idx, const void *y, int B, int H, int N, int d,
                                    int block, double topk, void *out, sagesla_stream_t stream);
 
+/* ------------------------------------------------------------------ W8A8 linear layer
+ *
+ * y = x W^T (+ bias) with 8-bit weights and activations, the layer computed in the INT8
+ * domain (TurboDiffusion explainer, news.qq.com, "Third key": both weights and activations
+ * of the linear layers are quantized to 8-bit integers; the weights offline in 128 x 128
+ * blocks that each share one scale factor, the activations dynamically at inference).
+ * Activation grouping (not given there): one scale per token and 128-channel block.
+ *
+ * Quantization of a group G (weight block or activation token-block), in fp32:
+ *   amax = max |x| over G;  s = amax / 127;  code = clamp(rne(x * (127 / amax)), -127, 127);
+ *   amax = 0 gives s = 0 and zero codes.
+ * Product:  y[m][n] = sum_kb sx[kb][m] sw[n/128][kb] (sum_{k in kb} x8[m][k] w8[n][k]) (+ bias[n]),
+ *   the integer sums exact (int32), scaling and the sum over blocks in fp32, y rounded to bf16.
+ *
+ * Shapes: x bf16 [M][K], W bf16 [N][K] (row-major, as a torch Linear weight), bias bf16 [N]
+ * or NULL, y bf16 [M][N]. K a multiple of 128 (<= 65536), N a multiple of 256 (<= 65536),
+ * 1 <= M <= 2^24. Rows are padded to Mp = 256 * ceil(M / 256).
+ *
+ * Code layout of x8 and w8: tiles of 32 rows x 128 channels (4096 bytes) in MFMA operand
+ * order, byte (s*64 + lane)*16 + e <-> row 32*tile + lane % 32 and channel
+ * 128*kb + 64*(lane / 32) + 16*s + e, stored block-major: tile (kb, rt) at byte
+ * (kb * RT + rt) * 4096 with RT = Mp / 32 (x8) or N / 32 (w8). Scales: sx fp32 [K/128][Mp]
+ * (rows past M: 0), sw fp32 [N/128][K/128]. All buffers are the caller's (16-byte aligned
+ * device memory, sizes from sagesla_w8a8_sizes); calls enqueue on the stream and return.
+ * Errors: SAGESLA_ERR_INVALID_ARGUMENT for shapes or pointers out of these bounds,
+ * SAGESLA_ERR_UNSUPPORTED off gfx950, SAGESLA_ERR_HIP for a failed launch. */
+sagesla_status sagesla_w8a8_sizes(int M, int N, int K, size_t *x8_bytes, size_t *sx_bytes,
+                                  size_t *w8_bytes, size_t *sw_bytes);
+
+/* Weight codes w8 and block scales sw of W (done once per weight). */
+sagesla_status sagesla_w8a8_quant_weight(const void *w, int N, int K, void *w8, void *sw,
+                                         sagesla_stream_t stream);
+
+/* Activation codes x8 and scales sx of x (each call). */
+sagesla_status sagesla_w8a8_quant_act(const void *x, int M, int K, void *x8, void *sx,
+                                      sagesla_stream_t stream);
+
+/* The block-scaled INT8 product y = x W^T (+ bias) from the codes and scales. */
+sagesla_status sagesla_w8a8_gemm(const void *x8, const void *sx, const void *w8, const void *sw,
+                                 const void *bias, int M, int N, int K, void *y,
+                                 sagesla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -6,7 +6,9 @@ tensors into it. The library is loaded on first use; there is no CPU fallback.
 """
 from . import synth  # noqa: F401  (seeded synthetic inputs)
 from ._lib import (GROUP, SageSLAError, alloc_workspace, fwd, ksel, lib, status_string,  # noqa: F401
-                   workspace_layout, workspace_size, workspace_views)
+                   w8a8_gemm, w8a8_linear, w8a8_quant_act, w8a8_quant_weight, w8a8_sizes, workspace_layout,
+                   workspace_size, workspace_views)
 
 __all__ = ["fwd", "ksel", "workspace_size", "workspace_layout", "workspace_views", "alloc_workspace",
-           "SageSLAError", "status_string", "lib", "synth"]
+           "SageSLAError", "status_string", "lib", "synth", "w8a8_sizes", "w8a8_quant_weight", "w8a8_quant_act",
+           "w8a8_gemm", "w8a8_linear"]

@@ -23,7 +23,8 @@ GROUP = 256  # query blocks per group of the linear-branch complement (union lis
 
 EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_workspace_size",
            "sagesla_workspace_layout", "sagesla_fwd", "sagesla_pool", "sagesla_head_stats", "sagesla_select",
-           "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn"]
+           "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
+           "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm"]
 
 _lib = None
 
@@ -57,6 +58,10 @@ def lib():
             "sagesla_linear_total": (i32, [P] + dims + [i32, P, P]),
             "sagesla_linear_complement": (i32, [P] * 5 + dims + [i32, f64] + [P] * 5 + [P]),
             "sagesla_sparse_attn": (i32, [P] * 8 + dims + [i32, f64, P, P]),
+            "sagesla_w8a8_sizes": (i32, [i32, i32, i32] + [C.POINTER(sz)] * 4),
+            "sagesla_w8a8_quant_weight": (i32, [P, i32, i32, P, P, P]),
+            "sagesla_w8a8_quant_act": (i32, [P, i32, i32, P, P, P]),
+            "sagesla_w8a8_gemm": (i32, [P] * 5 + [i32, i32, i32, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -170,3 +175,50 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
             continue
         out[name] = ws[off:off + nbytes].view(dt).view(shape)
     return out
+
+
+# ---------------------------------------------------------------- W8A8 linear layer
+
+def w8a8_sizes(M: int, N: int, K: int) -> dict:
+    """Bytes of the activation codes/scales and weight codes/scales (see include/sagesla.h)."""
+    out = [C.c_size_t() for _ in range(4)]
+    _check(lib().sagesla_w8a8_sizes(M, N, K, *[C.byref(o) for o in out]), "sagesla_w8a8_sizes")
+    return dict(zip(["x8", "sx", "w8", "sw"], [o.value for o in out]))
+
+
+def w8a8_quant_weight(w, stream=None):
+    """bf16 [N][K] weight -> (w8 uint8 codes, sw fp32 [N/128][K/128])."""
+    N, K = w.shape
+    sz = w8a8_sizes(1, N, K)
+    w8 = torch.empty(sz["w8"], dtype=torch.uint8, device=w.device)
+    sw = torch.empty((N // 128, K // 128), dtype=torch.float32, device=w.device)
+    _check(lib().sagesla_w8a8_quant_weight(_ptr(w), N, K, _ptr(w8), _ptr(sw), _stream(stream)),
+           "sagesla_w8a8_quant_weight")
+    return w8, sw
+
+
+def w8a8_quant_act(x, stream=None):
+    """bf16 [M][K] activations -> (x8 uint8 codes, sx fp32 [K/128][Mp])."""
+    M, K = x.shape
+    sz = w8a8_sizes(M, 256, K)
+    x8 = torch.empty(sz["x8"], dtype=torch.uint8, device=x.device)
+    sx = torch.empty((K // 128, sz["sx"] // (4 * (K // 128))), dtype=torch.float32, device=x.device)
+    _check(lib().sagesla_w8a8_quant_act(_ptr(x), M, K, _ptr(x8), _ptr(sx), _stream(stream)),
+           "sagesla_w8a8_quant_act")
+    return x8, sx
+
+
+def w8a8_gemm(x8, sx, w8, sw, M, N, K, bias=None, out=None, stream=None):
+    """y bf16 [M][N] from the codes and scales."""
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x8.device)
+    _check(lib().sagesla_w8a8_gemm(_ptr(x8), _ptr(sx), _ptr(w8), _ptr(sw), _ptr(bias), M, N, K, _ptr(out),
+                                   _stream(stream)), "sagesla_w8a8_gemm")
+    return out
+
+
+def w8a8_linear(x, w8, sw, N, bias=None, stream=None):
+    """The layer: quantize x, then the block-scaled INT8 product with the quantized weight."""
+    M, K = x.shape
+    x8, sx = w8a8_quant_act(x, stream)
+    return w8a8_gemm(x8, sx, w8, sw, M, N, K, bias=bias, stream=stream)

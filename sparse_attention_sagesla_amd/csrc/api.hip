@@ -21,6 +21,11 @@ hipError_t launch_linear_complement(const void*, const void*, const void*, const
                                     int, int, void*, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
                               const void*, const void*, int, int, int, int, void*, hipStream_t);
+int w8a8_row_tiles(int M);
+hipError_t launch_w8a8_quant_act(const void*, int, int, void*, void*, hipStream_t);
+hipError_t launch_w8a8_quant_weight(const void*, int, int, void*, void*, hipStream_t);
+hipError_t launch_w8a8_gemm(const void*, const void*, const void*, const void*, const void*, int, int, int, void*,
+                            hipStream_t);
 }  // namespace sagesla
 
 using namespace sagesla;
@@ -315,6 +320,53 @@ sagesla_status sagesla_sparse_attn(const void* q8, const void* sq, const void* k
   if ((s = check_device()) != SAGESLA_OK) return s;
   return from_hip(launch_sparse_attn(q8, sq, k8, sk, v8, vamax, idx, y, gm.BH, gm.N, gm.Nb, gm.ksel, out,
                                      (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- W8A8 linear layer
+
+static sagesla_status w8a8_check(int M, int N, int K) {
+  if (M < 1 || M > (1 << 24) || K < 128 || K % 128 != 0 || K > (1 << 16) || N < 256 || N % 256 != 0 ||
+      N > (1 << 16))
+    return SAGESLA_ERR_INVALID_ARGUMENT;
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_w8a8_sizes(int M, int N, int K, size_t* x8_bytes, size_t* sx_bytes, size_t* w8_bytes,
+                                  size_t* sw_bytes) {
+  sagesla_status s = w8a8_check(M, N, K);
+  if (s != SAGESLA_OK) return s;
+  const size_t Mp = (size_t)w8a8_row_tiles(M) * 32, KB = K / 128;
+  if (x8_bytes) *x8_bytes = Mp * K;
+  if (sx_bytes) *sx_bytes = KB * Mp * 4;
+  if (w8_bytes) *w8_bytes = (size_t)N * K;
+  if (sw_bytes) *sw_bytes = (size_t)(N / 128) * KB * 4;
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_w8a8_quant_weight(const void* w, int N, int K, void* w8, void* sw, sagesla_stream_t stream) {
+  sagesla_status s = w8a8_check(1, N, K);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({w, w8, sw})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_w8a8_quant_weight(w, N, K, w8, sw, (hipStream_t)stream));
+}
+
+sagesla_status sagesla_w8a8_quant_act(const void* x, int M, int K, void* x8, void* sx, sagesla_stream_t stream) {
+  sagesla_status s = w8a8_check(M, 256, K);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({x, x8, sx})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_w8a8_quant_act(x, M, K, x8, sx, (hipStream_t)stream));
+}
+
+sagesla_status sagesla_w8a8_gemm(const void* x8, const void* sx, const void* w8, const void* sw, const void* bias,
+                                 int M, int N, int K, void* y, sagesla_stream_t stream) {
+  sagesla_status s = w8a8_check(M, N, K);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({x8, sx, w8, sw, y})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(bias)) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_w8a8_gemm(x8, sx, w8, sw, bias, M, N, K, y, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -197,3 +197,25 @@ def make_inputs(cfg: Config, device="cpu"):
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw uint16 bit patterns of a bf16 tensor (host copy), for passing to C code."""
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def make_linear_inputs(M: int, K: int, N: int, seed: int, device="cpu", bias: bool = True):
+    """Inputs of one linear layer of the transformer: dict(x bf16 [M][K], w bf16 [N][K],
+    bias bf16 [N] or None), row-major as a torch Linear takes them.
+
+    x: N(0, 1) entries times a per-token magnitude exp(N(0, 1/4)), and K/64 outlier
+    channels (every 64th) scaled by 8, the structure that makes per-block activation scales
+    matter; w: N(0, 1/K) (unit output variance per unit input); bias: N(0, 0.02^2).
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.randn((M, K), generator=gen, device=device, dtype=torch.float32)
+    x *= torch.exp(0.5 * torch.randn((M, 1), generator=gen, device=device, dtype=torch.float32))
+    x[:, ::64] *= 8.0
+    x = x.to(torch.bfloat16)
+    w = (torch.randn((N, K), generator=gen, device=device, dtype=torch.float32) / math.sqrt(K)).to(torch.bfloat16)
+    b = None
+    if bias:
+        b = (0.02 * torch.randn((N,), generator=gen, device=device, dtype=torch.float32)).to(torch.bfloat16)
+    return {"x": x, "w": w, "bias": b}

@@ -68,3 +68,13 @@ def cos(a, b):
     if na == 0 and nb == 0:
         return 1.0
     return float(a @ b / (na * nb))
+
+
+def decode_w8a8_tiles(buf, RT, K):
+    """Block-major 32 x 128 INT8 code tiles -> [32*RT][K] rows.
+
+    Tile (kb, rt) sits at byte (kb*RT + rt)*4096; byte (s*64 + lane)*16 + e of a tile holds
+    row 32rt + lane%32, channel 128kb + 64(lane/32) + 16s + e."""
+    KB = K // 128
+    a = np.asarray(buf).view(np.int8)[: KB * RT * 4096].reshape(KB, RT, 4, 2, 32, 16)  # kb, rt, s, g, r, e
+    return a.transpose(1, 4, 0, 3, 2, 5).reshape(RT * 32, K)

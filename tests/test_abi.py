@@ -126,3 +126,18 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         S.fwd(q, q, q)
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 256, 128), (1, 128, 128), (1, 384, 128), (1, 256, 100), (1, 256, 0),
+                                   ((1 << 24) + 1, 256, 128), (1, 256, 1 << 17)])
+def test_w8a8_sizes_rejects(M, N, K):
+    out = [C.c_size_t() for _ in range(4)]
+    st = S.lib().sagesla_w8a8_sizes(M, N, K, *[C.byref(o) for o in out])
+    assert st == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_w8a8_sizes():
+    sz = S.w8a8_sizes(300, 512, 384)
+    assert sz == {"x8": 512 * 384, "sx": 3 * 512 * 4, "w8": 512 * 384, "sw": 4 * 3 * 4}
+    sz = S.w8a8_sizes(75600, 5120, 5120)
+    assert sz["x8"] == 75776 * 5120 and sz["sx"] == 40 * 75776 * 4
