@@ -106,12 +106,18 @@ __global__ __launch_bounds__(256) void w8a8_quant_weight_kernel(const uint16_t* 
 }
 
 // y tile of 256 rows x 256 columns per workgroup (8 waves, 2 per SIMD, 1 workgroup per
-// CU): wave (wm, wn) owns rows 64*wm .. +63 (two 32-row tiles) and columns 128*wn .. +127
-// (four 32-column tiles, one 128-column weight block). Per 128-channel block kb: the 8
-// x-tiles, 8 w-tiles and the 256 activation scales go by DMA into a two-stage LDS ring,
-// one block ahead; each (column tile, row tile) pair takes four INT8 32x32x32 MFMAs into
-// an int32 tile D[n][m] (lane = row m, 16 columns n per lane), which is added to the fp32
-// accumulator (in VGPRs: the VALU updates it) scaled by s_x[m][kb] s_w[nblock][kb].
+// CU): wave (wm, wn) owns rows 64*wm .. +63 and columns 128*wn .. +127 (one 128-column
+// weight block). Per 128-channel block kb: the 8 x-tiles, 8 w-tiles and the 256 activation
+// scales go by DMA into a two-stage LDS ring, one block ahead. The wave's product is 8 x 4
+// sub-tiles of 16 columns x 16 rows, each two INT8 16x16x64 MFMAs into an int32 tile
+// D[n][m] (lane: row m = lane%16, columns 4*(lane/16) .. +3), added to the fp32 accumulator
+// (in VGPRs: the VALU updates it) scaled by s_x[m][kb] s_w[nblock][kb].
+//
+// Operand chunks of a 16-row sub-tile for one 64-channel step t: lane 16g + r reads the
+// 16-byte chunk (s = 2t + g/2, lane' = 32(g%2) + 16*half + r) of the 32-row code tile, a
+// chunk of row r of that half. The chunks cover each row's 128 channels once over t and g,
+// and the x and w operands use the same assignment, so each MFMA pair sums the block's
+// products (the order of the K terms is immaterial to an exact integer sum).
 __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict__ x8, const float* __restrict__ sx,
                                                         const int8_t* __restrict__ w8, const float* __restrict__ sw,
                                                         const uint16_t* __restrict__ bias, int M, int N, int KB,
@@ -151,56 +157,77 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
     __builtin_amdgcn_global_load_lds((const void*)(ss + (uint32_t)ls), (lds_ptr_w8)(ds + 64 * (w & 3)), 4, 0, 0);
   };
 
-  // accumulator of column tile a, row tile b at acc[2 * a + b]
-  float acc[8][16];
+  // accumulator of column sub-tile j (16 columns), row sub-tile h (16 rows) at acc[j][h]
+  float acc[8][4][4];
 #pragma unroll
-  for (int i = 0; i < 8; i++)
+  for (int j = 0; j < 8; j++)
 #pragma unroll
-    for (int v = 0; v < 16; v++) acc[i][v] = 0.f;
+    for (int h = 0; h < 4; h++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) acc[j][h][v] = 0.f;
 
-  // this lane's byte offsets of its operand chunks (kept opaque per block, so that the
-  // compiler adds the tile and step offsets as immediates instead of holding one address
-  // per stage, tile and step)
-  int xo = 2 * wm * kW8Tile + l * 16, wo = 4 * wn * kW8Tile + l * 16, so = 64 * wm + (l & 31);
-  // The eight tiles go in a pipeline: the MFMAs of tile i are issued before tile i-1 is
-  // scaled into its accumulator. The empty asm statements keep that order (the compiler
-  // would otherwise issue all eight MFMA chains first and hold eight int32 tiles): tile
-  // i+1's operands pass through an asm placed after tile i-1's accumulator has been
-  // written, so at most two int32 tiles are live.
+  // this lane's byte offset within a code tile (see above), and its operand bases (kept
+  // opaque per block, so that the compiler adds the sub-tile and step offsets as immediates
+  // instead of holding one address per stage, sub-tile and step)
+  const int g = l >> 4, r = l & 15;
+  const int lane_off = ((g >> 1) * 64 + 32 * (g & 1) + r) * 16;
+  int xo = 2 * wm * kW8Tile + lane_off, wo = 4 * wn * kW8Tile + lane_off, so = 64 * wm + r;
+  // The eight column groups go in a pipeline: the MFMAs of group j (four independent
+  // two-MFMA chains, one per row sub-tile) are issued before group j-1 is scaled into its
+  // accumulators, and the w operands of group j+1 are read from LDS meanwhile. The empty
+  // asm statements keep that order (the compiler would otherwise issue every MFMA first and
+  // hold all the int32 tiles): group j+1's operands pass through an asm placed after group
+  // j-1's accumulators have been written, so at most two groups of int32 tiles are live.
   auto compute = [&](const int8_t* cx, const int8_t* cw, const float* cs, int kb) {
-    asm volatile("" : "+v"(xo), "+v"(so));
+    asm volatile("" : "+v"(xo), "+v"(so), "+v"(wo));
     const float swv = sw[(size_t)nblk * KB + kb];
-    v4i xb[2][4];
-    float sc[2];
+    v4i xb[4][2];
+    float sc[4];
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
+    for (int h = 0; h < 4; h++) {
 #pragma unroll
-      for (int s = 0; s < 4; s++) xb[b][s] = *(const v4i*)(cx + xo + b * kW8Tile + s * 1024);
-      sc[b] = cs[so + 32 * b] * swv;
+      for (int t = 0; t < 2; t++) xb[h][t] = *(const v4i*)(cx + xo + (h >> 1) * kW8Tile + (h & 1) * 256 + t * 2048);
+      sc[h] = cs[so + 16 * h] * swv;
     }
-    auto scale_in = [&](const v16i& d, int i) {
+    auto w_op = [&](v4i* wa, int j) {
 #pragma unroll
-      for (int v = 0; v < 16; v++) acc[i][v] = __builtin_fmaf((float)d[v], sc[i & 1], acc[i][v]);
-#pragma unroll
-      for (int v = 0; v < 16; v++) asm volatile("" : "+v"(acc[i][v]));
+      for (int t = 0; t < 2; t++) wa[t] = *(const v4i*)(cw + wo + (j >> 1) * kW8Tile + (j & 1) * 256 + t * 2048);
     };
-    v4i wa[4];
-    v16i dp;
+    auto scale_in = [&](const v4i* d, int j) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-      const int a = i >> 1, b = i & 1;
-      if (b == 0) {
-        asm volatile("" : "+v"(wo), "+v"(xb[0][0]));
+      for (int h = 0; h < 4; h++)
 #pragma unroll
-        for (int s = 0; s < 4; s++) wa[s] = *(const v4i*)(cw + wo + a * kW8Tile + s * 1024);
-      } else {
-        asm volatile("" : "+v"(xb[1][0]));
+        for (int v = 0; v < 4; v++) acc[j][h][v] = __builtin_fmaf((float)d[h][v], sc[h], acc[j][h][v]);
+#pragma unroll
+      for (int h = 0; h < 4; h++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) asm volatile("" : "+v"(acc[j][h][v]));
+    };
+    v4i wa[2], wn_[2], dp[4];
+    w_op(wa, 0);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      asm volatile("" : "+v"(xb[0][0]));
+      if (j + 1 < 8) w_op(wn_, j + 1);
+      v4i d[4];
+#pragma unroll
+      for (int h = 0; h < 4; h++) d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[0], xb[h][0], (v4i){}, 0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 4; h++) d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[1], xb[h][1], d[h], 0, 0, 0);
+      if (j > 0) {
+        scale_in(dp, j - 1);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
       }
-      v16i d = (v16i){};
 #pragma unroll
-      for (int s = 0; s < 4; s++) d = __builtin_amdgcn_mfma_i32_32x32x32_i8(wa[s], xb[b][s], d, 0, 0, 0);
-      if (i > 0) scale_in(dp, i - 1);
-      dp = d;
+      for (int h = 0; h < 4; h++) dp[h] = d[h];
+      if (j + 1 < 8) {
+        wa[0] = wn_[0];
+        wa[1] = wn_[1];
+      }
     }
     scale_in(dp, 7);
   };
@@ -219,26 +246,28 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
     }
   }
 
-  // D[n][m]: lane%32 = row m within its tile, element v = column 8*(v/4) + 4*(lane/32) + v%4
-  const int m_lo = 256 * tm + 64 * wm + (l & 31);
+  // D[n][m] of sub-tile (j, h): lane 16g + r holds row m = 16h + r, columns 16j + 4g .. +3.
+  // The bias values go into registers before the first store: loads and stores share one
+  // completion counter, so a load issued after stores would wait for all of them.
+  const int m_lo = 256 * tm + 64 * wm + r;
+  const int n_lo = 256 * tn + 128 * wn + 4 * g;
+  uint2 bv[8];
 #pragma unroll
-  for (int a = 0; a < 4; a++) {
-    const int n0 = 256 * tn + 128 * wn + 32 * a + 4 * (l >> 5);
+  for (int j = 0; j < 8; j++) bv[j] = bias ? *(const uint2*)(bias + n_lo + 16 * j) : make_uint2(0u, 0u);
+  // (one wait for all of them here, rather than one per guarded row group after stores)
 #pragma unroll
-    for (int b = 0; b < 2; b++) {
-      const int m = m_lo + 32 * b;
-      if (m < M) {
+  for (int j = 0; j < 8; j++) asm volatile("" : "+v"(bv[j].x), "+v"(bv[j].y));
 #pragma unroll
-        for (int v4 = 0; v4 < 4; v4++) {
-          const int n = n0 + 8 * v4;
-          float o[4];
+  for (int h = 0; h < 4; h++) {
+    const int m = m_lo + 16 * h;
+    if (m < M) {
 #pragma unroll
-          for (int e = 0; e < 4; e++) o[e] = acc[2 * a + b][4 * v4 + e] + (bias ? bf16_to_f32(bias[n + e]) : 0.f);
-          uint2 pk;
-          pk.x = pack_bf16x2(o[0], o[1]);
-          pk.y = pack_bf16x2(o[2], o[3]);
-          *(uint2*)(y + (size_t)m * N + n) = pk;
-        }
+      for (int j = 0; j < 8; j++) {
+        const float* o = acc[j][h];
+        uint2 pk;
+        pk.x = pack_bf16x2(o[0] + __uint_as_float(bv[j].x << 16), o[1] + __uint_as_float(bv[j].x & 0xFFFF0000u));
+        pk.y = pack_bf16x2(o[2] + __uint_as_float(bv[j].y << 16), o[3] + __uint_as_float(bv[j].y & 0xFFFF0000u));
+        *(uint2*)(y + (size_t)m * N + n_lo + 16 * j) = pk;
       }
     }
   }
