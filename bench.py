@@ -9,7 +9,9 @@ checked identical to sagesla_fwd's), with HIP events between the stages, so that
 kernel's average duration is measured live.
 
 Prints one JSON line. Default workload: the Wan2.1-14B-720P attention layer shape
-(B=1, H=40, N=75600, d=128, topk=0.1).
+(B=1, H=40, N=75600, d=128, topk=0.1). The line also carries a "w8a8" object: the W8A8
+linear layer (activation quantization + block-scaled INT8 product) on a 5120 -> 5120
+projection over the same 75,600 tokens, with torch's bf16 linear timed beside it.
 """
 import argparse
 import hashlib
@@ -35,6 +37,8 @@ def parse():
     ap.add_argument("--config", default="wan14b-720p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=200, help="query blocks in the oracle sample")
+    ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 linear-layer measurement")
+    ap.add_argument("--w8a8-shape", default="75600,5120,5120", help="M,K,N of the W8A8 linear layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MiB (a kernel of known "
                          "traffic that calibrates hardware byte counters under a profiler)")
@@ -203,7 +207,117 @@ def main():
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks)
+    if not args.no_w8a8:
+        res["w8a8"] = w8a8_measure(args)
     print(json.dumps(res), flush=True)
+
+
+def w8a8_measure(args):
+    """The W8A8 linear layer y = x W^T + b at one shape (default: a 5120 -> 5120 projection of
+    the Wan2.1-14B transformer over the 75,600 tokens of a 720p clip). The weight is quantized
+    once, outside the timed region; one step is the layer: activation quantization and the
+    block-scaled INT8 product. HIP events around each kernel on the launch stream give the
+    per-kernel averages; torch's bf16 linear on the same inputs is timed beside it."""
+    import sparse_attention_sagesla_amd as S
+    from sparse_attention_sagesla_amd import synth
+    M, K, N = (int(t) for t in args.w8a8_shape.split(","))
+    dev = torch.device("cuda:0")
+    inp = synth.make_linear_inputs(M, K, N, seed=7, device=dev, bias=True)
+    xx, w, b = inp["x"], inp["w"], inp["bias"]
+    w8, sw = S.w8a8_quant_weight(w)
+    sz = S.w8a8_sizes(M, N, K)
+    KB, Mp = K // 128, sz["sx"] // (4 * (K // 128))
+    x8 = torch.empty(sz["x8"], dtype=torch.uint8, device=dev)
+    sx = torch.empty((KB, Mp), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    L = S.lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def qa():
+        st = L.sagesla_w8a8_quant_act(xx.data_ptr(), M, K, x8.data_ptr(), sx.data_ptr(), sp)
+        if st != 0:
+            raise RuntimeError("sagesla_w8a8_quant_act: " + S.status_string(st))
+
+    def gm():
+        st = L.sagesla_w8a8_gemm(x8.data_ptr(), sx.data_ptr(), w8.data_ptr(), sw.data_ptr(), b.data_ptr(), M, N, K,
+                                 y.data_ptr(), sp)
+        if st != 0:
+            raise RuntimeError("sagesla_w8a8_gemm: " + S.status_string(st))
+
+    for _ in range(args.warmup):
+        qa()
+        gm()
+    steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
+        qa()
+        ev[s_][1].record(stream)
+        gm()
+        ev[s_][2].record(stream)
+    torch.cuda.synchronize()
+    ms_q = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_g = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    ms_layer = sum(e[0].elapsed_time(e[2]) for e in ev) / steps
+
+    # torch's bf16 linear (hipBLASLt) on the same inputs, for context
+    for _ in range(args.warmup):
+        torch.nn.functional.linear(xx, w, b)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        torch.nn.functional.linear(xx, w, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_bf16 = e0.elapsed_time(e1) / steps
+
+    ops = 2.0 * M * N * K
+    tops = ops / (ms_g * 1e-3) / 1e12
+    qa_bytes = 2.0 * M * K + float(Mp) * K + 4.0 * KB * Mp  # bf16 in, codes and scales out
+    qa_gbs = qa_bytes / (ms_q * 1e-3) / 1e9
+    res = {
+        "workload": "linear layer y = x W^T + b, M=%d tokens, K=%d -> N=%d (Wan2.1-14B projection, 720p)" % (M, K, N),
+        "dtype": "int8 (MFMA, 128x128 weight blocks, per token x 128-channel activation scales), fp32 scaling",
+        "ms_layer": round(ms_layer, 4),
+        "ms_quant_act": round(ms_q, 4),
+        "ms_gemm": round(ms_g, 4),
+        "tops_layer": round(ops / (ms_layer * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_INT8_FP8_TOPS, "unit": "TOP/s",
+                     "frac": round(tops / PEAK_INT8_FP8_TOPS, 4), "traffic": None, "kernel": "w8a8_gemm_kernel",
+                     "work_per_launch_ops": ops},
+        "quant_act_roofline": {"bound": "hbm", "achieved": round(qa_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(qa_gbs / PEAK_HBM_GBS, 4), "kernel": "w8a8_quant_act_kernel",
+                               "bytes_per_launch": qa_bytes},
+        "torch_bf16_linear_ms": round(ms_bf16, 4),
+        "speedup_vs_torch_bf16": round(ms_bf16 / ms_layer, 3),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = w8a8_cpu_baseline(xx, w, b, M, K, N)
+    return res
+
+
+def w8a8_cpu_baseline(xx, w, b, M, K, N, rows=16):
+    """The W8A8 oracle, as it is, on `rows` tokens (quantization and product), extrapolated to
+    M tokens; the weight quantization (once per weight) is reported apart."""
+    import oracle.w8a8 as OW
+    from sparse_attention_sagesla_amd import synth
+    sel = torch.linspace(0, M - 1, rows, device=xx.device).long()
+    xr, wb, bb = synth.bf16_bits(xx[sel]), synth.bf16_bits(w), synth.bf16_bits(b)
+    t0 = time.perf_counter()
+    qw, swo = OW.quant_weight(wb)
+    t_w = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    qx, sxo = OW.quant_act(xr)
+    OW.gemm(qx, sxo, qw, swo, bb)
+    t_r = (time.perf_counter() - t0) / rows
+    return {"value": round(M * t_r * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+            "sample": "%d of %d tokens (quantization + product), %.4f s per token, extrapolated; weight "
+                      "quantization %.2f s once, not included; single thread" % (rows, M, t_r, t_w),
+            "measured_s": round(t_w + rows * t_r, 2)}
 
 
 def cpu_baseline(cfg, x, nblocks):

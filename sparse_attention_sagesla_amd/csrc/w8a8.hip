@@ -159,6 +159,12 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
 
   // accumulator of column sub-tile j (16 columns), row sub-tile h (16 rows) at acc[j][h]
   float acc[8][4][4];
+  // The int32 tiles start from the bits of 1.5 * 2^23 (float), so the MFMA's integer sum
+  // leaves the bits of the float 1.5 * 2^23 + dot (|dot| <= 127 * 127 * 128 < 2^22 keeps it
+  // in [2^23, 2^24), where floats are the integers): one exact subtraction then gives
+  // float(dot), in place of the slower int-to-float conversion.
+  const v4i magic = (v4i){0x4B400000, 0x4B400000, 0x4B400000, 0x4B400000};
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
 #pragma unroll
   for (int j = 0; j < 8; j++)
 #pragma unroll
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
 #pragma unroll
       for (int h = 0; h < 4; h++)
 #pragma unroll
-        for (int v = 0; v < 4; v++) acc[j][h][v] = __builtin_fmaf((float)d[h][v], sc[h], acc[j][h][v]);
+        for (int v = 0; v < 4; v++) acc[j][h][v] = __builtin_fmaf(__int_as_float(d[h][v]) - kMagic, sc[h], acc[j][h][v]);
 #pragma unroll
       for (int h = 0; h < 4; h++)
 #pragma unroll
@@ -211,7 +217,7 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
       if (j + 1 < 8) w_op(wn_, j + 1);
       v4i d[4];
 #pragma unroll
-      for (int h = 0; h < 4; h++) d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[0], xb[h][0], (v4i){}, 0, 0, 0);
+      for (int h = 0; h < 4; h++) d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[0], xb[h][0], magic, 0, 0, 0);
 #pragma unroll
       for (int h = 0; h < 4; h++) d[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wa[1], xb[h][1], d[h], 0, 0, 0);
       if (j > 0) {
