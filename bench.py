@@ -276,6 +276,17 @@ def w8a8_measure(args):
 
     ops = 2.0 * M * N * K
     tops = ops / (ms_g * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "w8a8_gemm_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            # counters taken on an older kernel source, or another shape, do not describe this one
+            if tj.get("source_sha256_16") == src_hash(tj["sources"]) and "M=%d tokens, K=%d -> N=%d" % (
+                    M, K, N) in tj.get("workload", ""):
+                traffic = tj.get("bytes_per_launch")
+        except Exception:
+            traffic = None
     qa_bytes = 2.0 * M * K + float(Mp) * K + 4.0 * KB * Mp  # bf16 in, codes and scales out
     qa_gbs = qa_bytes / (ms_q * 1e-3) / 1e9
     res = {
@@ -286,7 +297,7 @@ def w8a8_measure(args):
         "ms_gemm": round(ms_g, 4),
         "tops_layer": round(ops / (ms_layer * 1e-3) / 1e12, 1),
         "roofline": {"bound": "mfma", "achieved": round(tops, 1), "peak": PEAK_INT8_FP8_TOPS, "unit": "TOP/s",
-                     "frac": round(tops / PEAK_INT8_FP8_TOPS, 4), "traffic": None, "kernel": "w8a8_gemm_kernel",
+                     "frac": round(tops / PEAK_INT8_FP8_TOPS, 4), "traffic": traffic, "kernel": "w8a8_gemm_kernel",
                      "work_per_launch_ops": ops},
         "quant_act_roofline": {"bound": "hbm", "achieved": round(qa_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(qa_gbs / PEAK_HBM_GBS, 4), "kernel": "w8a8_quant_act_kernel",

@@ -132,8 +132,13 @@ __global__ __launch_bounds__(512) void w8a8_gemm_kernel(const int8_t* __restrict
 
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= tiles) return;
-  // column tiles fastest: the workgroups that run together on an XCD share their x rows
-  const int tm = tile / tiles_n, tn = tile % tiles_n;
+  // tiles in groups of 8 row tiles: consecutive tiles run through the group's row tiles for
+  // one column tile, so that the 32 workgroups resident on an XCD read 8 x slices and 4 w
+  // slices per block (the L2 then serves most operand reads; the whole weight, 26 MB for a
+  // 5120 x 5120 layer, would otherwise be fetched again for every row tile)
+  const int TM = tiles / tiles_n, grp = tile / (8 * tiles_n), gi = tile % (8 * tiles_n);
+  const int gm = min(8, TM - grp * 8);
+  const int tm = grp * 8 + gi % gm, tn = gi / gm;
   const int t = threadIdx.x, l = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), wm = w & 3, wn = w >> 2;
   const int nblk = 2 * tn + wn;  // this wave's 128-column weight block
