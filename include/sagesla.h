@@ -161,6 +161,60 @@ sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k
                                    const void *idx, const void *y, int B, int H, int N, int d,
                                    int block, double topk, void *out, sagesla_stream_t stream);
 
+/* ------------------------------------------------------------------ SLA training path
+ *
+ * Trainable sparse-linear attention, unquantized: SLA is fine-tuned so that the model
+ * learns which connections matter, and SageSLA replaces it only at inference (news.qq.com
+ * explainer, "First key: attention" and "From training to deployment"). Per (batch, head),
+ * with the same pooling, selection and linear branch as above:
+ *   O_s = softmax(Q K_J^T / sqrt(d)) V_J over the tokens J of the kept key blocks, in bf16
+ *   products with fp32 accumulation and an fp32 online softmax;  O = O_s + O_l W.
+ * The backward takes the kept sets as fixed (the selection is piecewise constant) and
+ * returns dQ, dK, dV of L = sum(dO * O):
+ *   dS = P * (dP - D), dP = dO V^T, D = rowsum(dO * O_s);  dQ = dS K / sqrt(d),
+ *   dK = dS^T Q / sqrt(d), dV = P^T dO  (sparse part).
+ *
+ * The training workspace holds the forward regions (SAGESLA_WS_*, same meaning) and
+ * these; sagesla_sla_bwd reads what sagesla_sla_fwd left there for the same inputs. */
+typedef enum {
+    SAGESLA_SLA_WS_LSE = SAGESLA_WS_COUNT, /* fp32 [BH][N] row log-sum-exp of the scores
+                                              s/sqrt(d), base 2: log2 sum_j 2^(s_ij log2(e)/sqrt(d)) */
+    SAGESLA_SLA_WS_OS,    /* bf16 [BH][N][d]     O_s                                      */
+    SAGESLA_SLA_WS_KT,    /* bf16 [BH][Nb][8192] K token-reduction tiles (below)          */
+    SAGESLA_SLA_WS_VT,    /* bf16 [BH][Nb][8192] V token-reduction tiles                  */
+    SAGESLA_SLA_WS_QT,    /* bf16 [BH][Nb][8192] Q token-reduction tiles (backward)       */
+    SAGESLA_SLA_WS_DOT,   /* bf16 [BH][Nb][8192] dO token-reduction tiles (backward)      */
+    SAGESLA_SLA_WS_DSUM,  /* fp32 [BH][N]        D = rowsum(dO * O_s) (backward)          */
+    SAGESLA_SLA_WS_MASK,  /* u32 [BH][Nb][ceil(Nb/32)] bit i of row j: query block i keeps j */
+    SAGESLA_SLA_WS_COUNT
+} sagesla_sla_ws_region;
+/* Token-reduction tiles of a [N][d] tensor X, per 64-token block: element
+ * ((tt*4 + ct)*2 + t)*512 + l*8 + e holds X[32*tt + 16*t + 8*(e/4) + 4*g + e%4][32*ct + r]
+ * (tt, t in 0..1, ct in 0..3, e in 0..7; tokens past N are 0). */
+
+/* Bytes of the training workspace (linear = 0 when proj will be NULL). Host only. */
+sagesla_status sagesla_sla_workspace_size(int B, int H, int N, int d, int block, double topk,
+                                          int linear, size_t *bytes);
+
+/* Byte offsets of the SAGESLA_WS_* and SAGESLA_SLA_WS_* regions. Host only. */
+sagesla_status sagesla_sla_workspace_layout(int B, int H, int N, int d, int block, double topk,
+                                            int linear, size_t offsets[SAGESLA_SLA_WS_COUNT]);
+
+/* SLA forward (unquantized): out bf16 [B,H,N,d] = O_s (+ O_l W when proj != NULL and
+ * ksel < Nb); leaves lse, O_s and the kept sets in the workspace for the backward. */
+sagesla_status sagesla_sla_fwd(const void *q, const void *k, const void *v, const void *proj,
+                               int B, int H, int N, int d, double topk, int block, void *out,
+                               void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
+
+/* SLA backward: dq, dk, dv fp32 [B,H,N,d] (overwritten) from dout bf16 [B,H,N,d] and the
+ * workspace of the sagesla_sla_fwd call on the same q, k, v, proj, sizes and topk.
+ * This version differentiates the sparse part: proj must be NULL (else
+ * SAGESLA_ERR_UNSUPPORTED) and dproj must be NULL. */
+sagesla_status sagesla_sla_bwd(const void *q, const void *k, const void *v, const void *proj,
+                               const void *dout, int B, int H, int N, int d, double topk,
+                               int block, void *dq, void *dk, void *dv, void *dproj,
+                               void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
+
 /* ------------------------------------------------------------------ W8A8 linear layer
  *
  * y = x W^T (+ bias) with 8-bit weights and activations, the layer computed in the INT8

@@ -24,7 +24,10 @@ GROUP = 256  # query blocks per group of the linear-branch complement (union lis
 EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_workspace_size",
            "sagesla_workspace_layout", "sagesla_fwd", "sagesla_pool", "sagesla_head_stats", "sagesla_select",
            "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
-           "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm"]
+           "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
+           "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd"]
+SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask"]
+SLA_WS_COUNT = len(SLA_WS_REGIONS)
 
 _lib = None
 
@@ -62,6 +65,10 @@ def lib():
             "sagesla_w8a8_quant_weight": (i32, [P, i32, i32, P, P, P]),
             "sagesla_w8a8_quant_act": (i32, [P, i32, i32, P, P, P]),
             "sagesla_w8a8_gemm": (i32, [P] * 5 + [i32, i32, i32, P, P]),
+            "sagesla_sla_workspace_size": (i32, dims + [i32, f64, i32, C.POINTER(sz)]),
+            "sagesla_sla_workspace_layout": (i32, dims + [i32, f64, i32, C.POINTER(sz * SLA_WS_COUNT)]),
+            "sagesla_sla_fwd": (i32, [P, P, P, P] + dims + [f64, i32, P, P, sz, P]),
+            "sagesla_sla_bwd": (i32, [P] * 5 + dims + [f64, i32] + [P] * 5 + [sz, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -222,3 +229,73 @@ def w8a8_linear(x, w8, sw, N, bias=None, stream=None):
     M, K = x.shape
     x8, sx = w8a8_quant_act(x, stream)
     return w8a8_gemm(x8, sx, w8, sw, M, N, K, bias=bias, stream=stream)
+
+
+# ---------------------------------------------------------------- SLA training path
+
+def sla_workspace_size(B, H, N, d=128, block=64, topk=0.1, linear=True) -> int:
+    out = C.c_size_t()
+    _check(lib().sagesla_sla_workspace_size(B, H, N, d, block, float(topk), int(bool(linear)), C.byref(out)),
+           "sagesla_sla_workspace_size")
+    return out.value
+
+
+def sla_workspace_layout(B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict:
+    arr = (C.c_size_t * SLA_WS_COUNT)()
+    _check(lib().sagesla_sla_workspace_layout(B, H, N, d, block, float(topk), int(bool(linear)), C.byref(arr)),
+           "sagesla_sla_workspace_layout")
+    return {name: arr[i] for i, name in enumerate(SLA_WS_REGIONS)}
+
+
+def sla_fwd(q, k, v, proj=None, topk=0.1, block=64, out=None, workspace=None, stream=None):
+    """Unquantized SLA forward. Returns (out bf16 [B, H, N, d], workspace); the workspace
+    holds what sla_bwd needs."""
+    B, H, N, d = _shape(q)
+    for x in (k, v):
+        if _shape(x) != q.shape:
+            raise ValueError("q, k, v shapes differ")
+    if proj is not None and (proj.shape != (d, d) or proj.dtype != torch.bfloat16 or not proj.is_contiguous()):
+        raise ValueError("proj must be a contiguous bf16 [d, d] tensor")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(sla_workspace_size(B, H, N, d, block, topk, proj is not None), dtype=torch.uint8,
+                                device=q.device)
+    _check(lib().sagesla_sla_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(proj), B, H, N, d, float(topk), block, _ptr(out),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)), "sagesla_sla_fwd")
+    return out, workspace
+
+
+def sla_bwd(q, k, v, dout, workspace, proj=None, topk=0.1, block=64, dq=None, dk=None, dv=None, dproj=None,
+            stream=None):
+    """SLA backward from the workspace of sla_fwd on the same inputs. Returns (dq, dk, dv)
+    fp32 [B, H, N, d] (and dproj fp32 [d, d] when proj is given)."""
+    B, H, N, d = _shape(q)
+    if _shape(dout) != q.shape:
+        raise ValueError("dout shape differs")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dq is None else dq
+    dk = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(q.shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    if proj is not None and dproj is None:
+        dproj = torch.empty((d, d), dtype=torch.float32, device=q.device)
+    _check(lib().sagesla_sla_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(proj), _ptr(dout), B, H, N, d, float(topk), block,
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dproj), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "sagesla_sla_bwd")
+    return (dq, dk, dv) if proj is None else (dq, dk, dv, dproj)
+
+
+def sla_workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict:
+    """Typed views of the training intermediates (idx, lse, os, dsum, mask, y)."""
+    lay = sla_workspace_layout(B, H, N, d, block, topk, linear)
+    BH, Nb = B * H, (N + block - 1) // block
+    spec = {"idx": (torch.int32, (BH, Nb, ksel(N, topk, block))), "lse": (torch.float32, (BH, N)),
+            "os": (torch.bfloat16, (BH, N, d)), "dsum": (torch.float32, (BH, N)),
+            "mask": (torch.int32, (BH, Nb, (Nb + 31) // 32)), "y": (torch.bfloat16, (BH, N, d))}
+    out = {}
+    for name, (dt, shape) in spec.items():
+        off = lay[name]
+        nbytes = torch.Size(shape).numel() * torch.empty((), dtype=dt).element_size()
+        if off + nbytes <= ws.numel():
+            out[name] = ws[off:off + nbytes].view(dt).view(shape)
+    return out
+

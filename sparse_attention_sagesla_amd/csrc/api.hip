@@ -21,6 +21,14 @@ hipError_t launch_linear_complement(const void*, const void*, const void*, const
                                     int, int, void*, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
                               const void*, const void*, int, int, int, int, void*, hipStream_t);
+hipError_t launch_sla_relayout(const void*, int, int, int, void*, hipStream_t);
+hipError_t launch_sla_kept_mask(const void*, int, int, int, void*, hipStream_t);
+hipError_t launch_sla_fwd(const void*, const void*, const void*, const void*, const void*, int, int, int, int, void*,
+                          void*, void*, hipStream_t);
+hipError_t launch_sla_bwd_dq(const void*, const void*, const void*, const void*, const void*, const void*, const void*,
+                             const void*, int, int, int, int, void*, void*, hipStream_t);
+hipError_t launch_sla_bwd_dkdv(const void*, const void*, const void*, const void*, const void*, const void*,
+                               const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
 int w8a8_row_tiles(int M);
 hipError_t launch_w8a8_quant_act(const void*, int, int, void*, void*, hipStream_t);
 hipError_t launch_w8a8_quant_weight(const void*, int, int, void*, void*, hipStream_t);
@@ -367,6 +375,146 @@ sagesla_status sagesla_w8a8_gemm(const void* x8, const void* sx, const void* w8,
   if ((s = check_opt_ptr(bias)) != SAGESLA_OK) return s;
   if ((s = check_device()) != SAGESLA_OK) return s;
   return from_hip(launch_w8a8_gemm(x8, sx, w8, sw, bias, M, N, K, y, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------- SLA training path
+
+}  // extern "C"
+
+namespace {
+
+// The forward regions, then the training regions, each 256-byte aligned.
+void sla_layout(const Geom& gm, bool linear, size_t off[SAGESLA_SLA_WS_COUNT], size_t* total) {
+  size_t base;
+  layout(gm, linear, off, &base);
+  const size_t BH = gm.BH, N = gm.N, Nb = gm.Nb, D = kD, nw = (gm.Nb + 31) / 32;
+  const size_t tiles = BH * Nb * (size_t)kBlk * kD * 2;
+  size_t sz[SAGESLA_SLA_WS_COUNT] = {};
+  sz[SAGESLA_SLA_WS_LSE] = BH * N * 4;
+  sz[SAGESLA_SLA_WS_OS] = BH * N * D * 2;
+  sz[SAGESLA_SLA_WS_KT] = tiles;
+  sz[SAGESLA_SLA_WS_VT] = tiles;
+  sz[SAGESLA_SLA_WS_QT] = tiles;
+  sz[SAGESLA_SLA_WS_DOT] = tiles;
+  sz[SAGESLA_SLA_WS_DSUM] = BH * N * 4;
+  sz[SAGESLA_SLA_WS_MASK] = BH * Nb * nw * 4;
+  size_t o = align256(base);
+  for (int r = SAGESLA_WS_COUNT; r < SAGESLA_SLA_WS_COUNT; r++) {
+    off[r] = o;
+    o += align256(sz[r]);
+  }
+  *total = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+sagesla_status sagesla_sla_workspace_size(int B, int H, int N, int d, int block, double topk, int linear,
+                                          size_t* bytes) {
+  Geom gm;
+  if (!bytes) return SAGESLA_ERR_INVALID_ARGUMENT;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  size_t off[SAGESLA_SLA_WS_COUNT];
+  sla_layout(gm, linear != 0 && gm.ksel < gm.Nb, off, bytes);
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_sla_workspace_layout(int B, int H, int N, int d, int block, double topk, int linear,
+                                            size_t offsets[SAGESLA_SLA_WS_COUNT]) {
+  Geom gm;
+  if (!offsets) return SAGESLA_ERR_INVALID_ARGUMENT;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  size_t total;
+  sla_layout(gm, linear != 0 && gm.ksel < gm.Nb, offsets, &total);
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_sla_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
+                               int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
+                               sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, out, workspace})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
+  const bool linear = proj != nullptr && gm.ksel < gm.Nb;
+  size_t off[SAGESLA_SLA_WS_COUNT], total;
+  sla_layout(gm, linear, off, &total);
+  if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto P = [&](int r) { return (void*)(ws + off[r]); };
+  hipError_t e;
+  if ((e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART),
+                       P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), st)) !=
+      hipSuccess)
+    return from_hip(e);
+  if ((e = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_IDX),
+                         st)) != hipSuccess)
+    return from_hip(e);
+  if (linear) {
+    // the linear states come with the K/V quantization pass (its codes go unused here)
+    if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb,
+                               P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
+      return from_hip(e);
+    if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_K8),
+                             P(SAGESLA_WS_SK), P(SAGESLA_WS_V8), P(SAGESLA_WS_HS), P(SAGESLA_WS_HPART), st)) !=
+        hipSuccess)
+      return from_hip(e);
+    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st)) != hipSuccess)
+      return from_hip(e);
+    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj, gm.BH,
+                                      gm.N, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
+                                      P(SAGESLA_WS_UCOUNT), P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
+      return from_hip(e);
+  }
+  if ((e = launch_sla_relayout(v, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_VT), st)) != hipSuccess) return from_hip(e);
+  e = launch_sla_fwd(q, k, P(SAGESLA_SLA_WS_VT), P(SAGESLA_WS_IDX), linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH,
+                     gm.N, gm.Nb, gm.ksel, out, P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE), st);
+  return from_hip(e);
+}
+
+sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, const void* proj, const void* dout,
+                               int B, int H, int N, int d, double topk, int block, void* dq, void* dk, void* dv,
+                               void* dproj, void* workspace, size_t workspace_bytes, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, dout, dq, dk, dv, workspace})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(dproj)) != SAGESLA_OK) return s;
+  if (proj != nullptr || dproj != nullptr) return SAGESLA_ERR_UNSUPPORTED;
+  size_t off[SAGESLA_SLA_WS_COUNT], total;
+  sla_layout(gm, false, off, &total);
+  if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto P = [&](int r) { return (void*)(ws + off[r]); };
+  hipError_t e;
+  if ((e = launch_sla_relayout(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_KT), st)) != hipSuccess) return from_hip(e);
+  if ((e = launch_sla_relayout(q, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_QT), st)) != hipSuccess) return from_hip(e);
+  if ((e = launch_sla_relayout(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_DOT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_kept_mask(P(SAGESLA_WS_IDX), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_MASK), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_bwd_dq(q, k, v, P(SAGESLA_SLA_WS_KT), dout, P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE),
+                             P(SAGESLA_WS_IDX), gm.BH, gm.N, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_DSUM), dq, st)) !=
+      hipSuccess)
+    return from_hip(e);
+  e = launch_sla_bwd_dkdv(q, k, v, P(SAGESLA_SLA_WS_QT), dout, P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE),
+                          P(SAGESLA_SLA_WS_DSUM), P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st);
+  return from_hip(e);
 }
 
 }  // extern "C"
