@@ -170,22 +170,35 @@ sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k
  *   O_s = softmax(Q K_J^T / sqrt(d)) V_J over the tokens J of the kept key blocks, in bf16
  *   products with fp32 accumulation and an fp32 online softmax;  O = O_s + O_l W.
  * The backward takes the kept sets as fixed (the selection is piecewise constant) and
- * returns dQ, dK, dV of L = sum(dO * O):
- *   dS = P * (dP - D), dP = dO V^T, D = rowsum(dO * O_s);  dQ = dS K / sqrt(d),
- *   dK = dS^T Q / sqrt(d), dV = P^T dO  (sparse part).
+ * returns dQ, dK, dV (and dW) of L = sum(dO * O):
+ *   sparse part: dS = P * (dP - D), dP = dO V^T, D = rowsum(dO * O_s);
+ *     dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d), dV = P^T dO;
+ *   linear part (u = phi(q) H^c, s = phi(q) . z^c, O_l = u / s): dO_l = dO W^T,
+ *     du = dO_l / s, ds = -(dO_l . O_l) / s, dphi(q) = du H^c^T + ds z^c, and through the
+ *     channel softmax to dQ; the complement gradients dH^c_i = sum phi(q)^T du, dz^c_i =
+ *     sum phi(q) ds pass to every key block the query block leaves out, then through
+ *     H_j = phi(K_j)^T V_j and z_j to dK and dV; dW = sum O_l^T dO.
+ * On the GPU the key blocks' gradients are formed as the total minus the query blocks that
+ * keep them (or as the direct sum when 2 ksel > Nb), on the same masked product as the
+ * forward's complement.
  *
  * The training workspace holds the forward regions (SAGESLA_WS_*, same meaning) and
  * these; sagesla_sla_bwd reads what sagesla_sla_fwd left there for the same inputs. */
 typedef enum {
     SAGESLA_SLA_WS_LSE = SAGESLA_WS_COUNT, /* fp32 [BH][N] row log-sum-exp of the scores
                                               s/sqrt(d), base 2: log2 sum_j 2^(s_ij log2(e)/sqrt(d)) */
-    SAGESLA_SLA_WS_OS,    /* bf16 [BH][N][d]     O_s                                      */
+    SAGESLA_SLA_WS_OS,    /* fp32 [BH][N][d]     O_s                                      */
     SAGESLA_SLA_WS_KT,    /* bf16 [BH][Nb][8192] K token-reduction tiles (below)          */
     SAGESLA_SLA_WS_VT,    /* bf16 [BH][Nb][8192] V token-reduction tiles                  */
     SAGESLA_SLA_WS_QT,    /* bf16 [BH][Nb][8192] Q token-reduction tiles (backward)       */
     SAGESLA_SLA_WS_DOT,   /* bf16 [BH][Nb][8192] dO token-reduction tiles (backward)      */
     SAGESLA_SLA_WS_DSUM,  /* fp32 [BH][N]        D = rowsum(dO * O_s) (backward)          */
     SAGESLA_SLA_WS_MASK,  /* u32 [BH][Nb][ceil(Nb/32)] bit i of row j: query block i keeps j */
+    SAGESLA_SLA_WS_PHQ,   /* bf16 [BH][N][d] phi(q)                          (linear)   */
+    SAGESLA_SLA_WS_DU,    /* bf16 [BH][N][d] du = dO_l / s                   (linear)   */
+    SAGESLA_SLA_WS_OL,    /* bf16 [BH][N][d] O_l                             (linear)   */
+    SAGESLA_SLA_WS_DS,    /* fp32 [BH][N]    ds = -(dO_l . O_l) / s          (linear)   */
+    SAGESLA_SLA_WS_DWP,   /* fp32 [512][d][d] partial sums of dW             (linear)   */
     SAGESLA_SLA_WS_COUNT
 } sagesla_sla_ws_region;
 /* Token-reduction tiles of a [N][d] tensor X, per 64-token block: element
@@ -207,9 +220,9 @@ sagesla_status sagesla_sla_fwd(const void *q, const void *k, const void *v, cons
                                void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
 
 /* SLA backward: dq, dk, dv fp32 [B,H,N,d] (overwritten) from dout bf16 [B,H,N,d] and the
- * workspace of the sagesla_sla_fwd call on the same q, k, v, proj, sizes and topk.
- * This version differentiates the sparse part: proj must be NULL (else
- * SAGESLA_ERR_UNSUPPORTED) and dproj must be NULL. */
+ * workspace of the sagesla_sla_fwd call on the same q, k, v, proj, sizes and topk (its
+ * forward regions are overwritten). dproj: fp32 [d, d] (overwritten), required exactly
+ * when proj != NULL; it is the sum over all batches and heads. */
 sagesla_status sagesla_sla_bwd(const void *q, const void *k, const void *v, const void *proj,
                                const void *dout, int B, int H, int N, int d, double topk,
                                int block, void *dq, void *dk, void *dv, void *dproj,

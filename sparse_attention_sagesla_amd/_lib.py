@@ -26,7 +26,7 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
            "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd"]
-SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask"]
+SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask", "phq", "du", "ol", "ds", "dwp"]
 SLA_WS_COUNT = len(SLA_WS_REGIONS)
 
 _lib = None
@@ -289,7 +289,7 @@ def sla_workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> 
     lay = sla_workspace_layout(B, H, N, d, block, topk, linear)
     BH, Nb = B * H, (N + block - 1) // block
     spec = {"idx": (torch.int32, (BH, Nb, ksel(N, topk, block))), "lse": (torch.float32, (BH, N)),
-            "os": (torch.bfloat16, (BH, N, d)), "dsum": (torch.float32, (BH, N)),
+            "os": (torch.float32, (BH, N, d)), "dsum": (torch.float32, (BH, N)),
             "mask": (torch.int32, (BH, Nb, (Nb + 31) // 32)), "y": (torch.bfloat16, (BH, N, d))}
     out = {}
     for name, (dt, shape) in spec.items():

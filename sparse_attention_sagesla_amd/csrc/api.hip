@@ -29,6 +29,16 @@ hipError_t launch_sla_bwd_dq(const void*, const void*, const void*, const void*,
                              const void*, int, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_sla_bwd_dkdv(const void*, const void*, const void*, const void*, const void*, const void*,
                                const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
+hipError_t launch_sla_lin_bwd_q(const void*, const void*, const void*, const void*, int, int, int, void*, void*, void*,
+                                void*, void*, hipStream_t);
+hipError_t launch_sla_lin_dhc(const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
+hipError_t launch_sla_union_t(const void*, int, int, int, void*, void*, void*, hipStream_t);
+hipError_t launch_linear_mask_gemm(const void*, const void*, const void*, const void*, const void*, int, int, int,
+                                   void*, hipStream_t);
+hipError_t launch_sla_lin_bwd_k(const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
+hipError_t launch_sla_dw(const void*, const void*, int, void*, void*, hipStream_t);
+int sla_dw_parts();
+hipError_t launch_sla_zero(void*, size_t, hipStream_t);
 int w8a8_row_tiles(int M);
 hipError_t launch_w8a8_quant_act(const void*, int, int, void*, void*, hipStream_t);
 hipError_t launch_w8a8_quant_weight(const void*, int, int, void*, void*, hipStream_t);
@@ -391,13 +401,20 @@ void sla_layout(const Geom& gm, bool linear, size_t off[SAGESLA_SLA_WS_COUNT], s
   const size_t tiles = BH * Nb * (size_t)kBlk * kD * 2;
   size_t sz[SAGESLA_SLA_WS_COUNT] = {};
   sz[SAGESLA_SLA_WS_LSE] = BH * N * 4;
-  sz[SAGESLA_SLA_WS_OS] = BH * N * D * 2;
+  sz[SAGESLA_SLA_WS_OS] = BH * N * D * 4;
   sz[SAGESLA_SLA_WS_KT] = tiles;
   sz[SAGESLA_SLA_WS_VT] = tiles;
   sz[SAGESLA_SLA_WS_QT] = tiles;
   sz[SAGESLA_SLA_WS_DOT] = tiles;
   sz[SAGESLA_SLA_WS_DSUM] = BH * N * 4;
   sz[SAGESLA_SLA_WS_MASK] = BH * Nb * nw * 4;
+  if (linear) {
+    sz[SAGESLA_SLA_WS_PHQ] = BH * N * D * 2;
+    sz[SAGESLA_SLA_WS_DU] = BH * N * D * 2;
+    sz[SAGESLA_SLA_WS_OL] = BH * N * D * 2;
+    sz[SAGESLA_SLA_WS_DS] = BH * N * 4;
+    sz[SAGESLA_SLA_WS_DWP] = (size_t)sla_dw_parts() * D * D * 4;
+  }
   size_t o = align256(base);
   for (int r = SAGESLA_WS_COUNT; r < SAGESLA_SLA_WS_COUNT; r++) {
     off[r] = o;
@@ -492,9 +509,10 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
   if ((s = check_ptrs({q, k, v, dout, dq, dk, dv, workspace})) != SAGESLA_OK) return s;
   if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
   if ((s = check_opt_ptr(dproj)) != SAGESLA_OK) return s;
-  if (proj != nullptr || dproj != nullptr) return SAGESLA_ERR_UNSUPPORTED;
+  if ((proj == nullptr) != (dproj == nullptr)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  const bool linear = proj != nullptr && gm.ksel < gm.Nb;
   size_t off[SAGESLA_SLA_WS_COUNT], total;
-  sla_layout(gm, false, off, &total);
+  sla_layout(gm, linear, off, &total);
   if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
   if ((s = check_device()) != SAGESLA_OK) return s;
 
@@ -502,6 +520,7 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
   char* ws = (char*)workspace;
   auto P = [&](int r) { return (void*)(ws + off[r]); };
   hipError_t e;
+  // sparse part: dq, dk, dv written
   if ((e = launch_sla_relayout(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_KT), st)) != hipSuccess) return from_hip(e);
   if ((e = launch_sla_relayout(q, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_QT), st)) != hipSuccess) return from_hip(e);
   if ((e = launch_sla_relayout(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_DOT), st)) != hipSuccess)
@@ -512,8 +531,39 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
                              P(SAGESLA_WS_IDX), gm.BH, gm.N, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_DSUM), dq, st)) !=
       hipSuccess)
     return from_hip(e);
-  e = launch_sla_bwd_dkdv(q, k, v, P(SAGESLA_SLA_WS_QT), dout, P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE),
-                          P(SAGESLA_SLA_WS_DSUM), P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st);
+  if ((e = launch_sla_bwd_dkdv(q, k, v, P(SAGESLA_SLA_WS_QT), dout, P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE),
+                               P(SAGESLA_SLA_WS_DSUM), P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st)) !=
+      hipSuccess)
+    return from_hip(e);
+  if (proj == nullptr) return SAGESLA_OK;
+  if (!linear) {  // every block kept: no linear part, dW = 0
+    return from_hip(launch_sla_zero(dproj, (size_t)kD * kD, st));
+  }
+  // linear part: added into dq, dk, dv; the token-reduction tiles of phi(q), du and O_l
+  // reuse the K, Q and V tile regions, the state gradients the forward's state regions
+  if ((e = launch_sla_lin_bwd_q(q, dout, P(SAGESLA_WS_HC), proj, gm.BH, gm.N, gm.Nb, dq, P(SAGESLA_SLA_WS_PHQ),
+                                P(SAGESLA_SLA_WS_DU), P(SAGESLA_SLA_WS_DS), P(SAGESLA_SLA_WS_OL), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_relayout(P(SAGESLA_SLA_WS_PHQ), gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_KT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_relayout(P(SAGESLA_SLA_WS_DU), gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_QT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_relayout(P(SAGESLA_SLA_WS_OL), gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_VT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_lin_dhc(P(SAGESLA_SLA_WS_KT), P(SAGESLA_SLA_WS_QT), P(SAGESLA_SLA_WS_DS), gm.BH, gm.N, gm.Nb,
+                              P(SAGESLA_WS_HS), P(SAGESLA_WS_HPART), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_union_t(P(SAGESLA_SLA_WS_MASK), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST),
+                              P(SAGESLA_WS_UMASK), P(SAGESLA_WS_UCOUNT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_linear_mask_gemm(P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
+                                   P(SAGESLA_WS_UCOUNT), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_HC), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_lin_bwd_k(k, v, P(SAGESLA_WS_HC), gm.BH, gm.N, gm.Nb, dk, dv, st)) != hipSuccess)
+    return from_hip(e);
+  e = launch_sla_dw(P(SAGESLA_SLA_WS_VT), P(SAGESLA_SLA_WS_DOT), gm.BH * gm.Nb, P(SAGESLA_SLA_WS_DWP), dproj, st);
   return from_hip(e);
 }
 

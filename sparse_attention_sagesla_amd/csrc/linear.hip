@@ -506,6 +506,17 @@ hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot,
   return hipGetLastError();
 }
 
+// The masked complement product alone, on lists built elsewhere (the backward passes
+// state gradients through it with the kept relation transposed).
+hipError_t launch_linear_mask_gemm(const void* hs, const void* htot, const void* ulist, const void* umask,
+                                   const void* ucount, int BH, int Nb, int ksel, void* hc, hipStream_t st) {
+  const int ng = linear_groups(Nb);
+  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
+                     (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
+                     Nb, ng, use_complement_sets(Nb, ksel), (uint16_t*)hc);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
                                     const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
                                     void* umask, void* ucount, void* hc, void* y, hipStream_t st) {

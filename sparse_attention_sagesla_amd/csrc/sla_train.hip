@@ -41,6 +41,14 @@ __device__ __forceinline__ v8bf pack8(const float* x) {
   return __builtin_bit_cast(v8bf, r);
 }
 
+// registers o .. o+7 of an accumulator as a bf16 operand
+__device__ __forceinline__ v8bf pack8v(const v16f& x, int o) {
+  float t[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) t[e] = x[o + e];
+  return pack8(t);
+}
+
 __device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -97,12 +105,13 @@ __global__ __launch_bounds__(256) void sla_kept_mask_kernel(const int* __restric
 // ------------------------------------------------------------------ forward
 // One workgroup (2 waves) per (head, query block); wave w owns query rows 32w .. +31, one
 // per lane column. Per kept key block: S^T = K Q^T (two 32-key tiles), online softmax in
-// the base-2 domain, O^T += V^T P^T. Epilogue: O_s (bf16), lse, and out = O_s + y.
+// the base-2 domain, O^T += V^T P^T. Epilogue: O_s (fp32, for the backward's D), lse, and
+// out = O_s + y (bf16).
 __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ vt, const int* __restrict__ idx,
                                                       const uint16_t* __restrict__ y, int BH, int N, int Nb, int ksel,
                                                       int per_xcd, uint16_t* __restrict__ out,
-                                                      uint16_t* __restrict__ os, float* __restrict__ lse) {
+                                                      float* __restrict__ os, float* __restrict__ lse) {
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, i = tile % Nb;
@@ -187,10 +196,10 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
       float a[4];
 #pragma unroll
       for (int e = 0; e < 4; e++) a[e] = o[ct][4 * v4 + e] * inv;
+      *(float4*)(os + rowoff + ch) = make_float4(a[0], a[1], a[2], a[3]);
       uint2 pk;
       pk.x = pack_bf16x2(a[0], a[1]);
       pk.y = pack_bf16x2(a[2], a[3]);
-      *(uint2*)(os + rowoff + ch) = pk;
       if (y) {
         const uint2 yy = *(const uint2*)(y + rowoff + ch);
         a[0] += __uint_as_float(yy.x << 16);
@@ -210,7 +219,7 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
 // 32-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T.
 __global__ __launch_bounds__(128) void sla_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                          const uint16_t* __restrict__ v, const uint16_t* __restrict__ kt_,
-                                                         const uint16_t* __restrict__ dout, const uint16_t* __restrict__ os,
+                                                         const uint16_t* __restrict__ dout, const float* __restrict__ os,
                                                          const float* __restrict__ lse, const int* __restrict__ idx,
                                                          int BH, int N, int Nb, int ksel, int per_xcd,
                                                          float* __restrict__ dsum, float* __restrict__ dq) {
@@ -231,9 +240,10 @@ __global__ __launch_bounds__(128) void sla_bwd_dq_kernel(const uint16_t* __restr
     qop[s] = qvalid ? ld8(q + e) : (v8bf){};
     dop[s] = qvalid ? ld8(dout + e) : (v8bf){};
     if (qvalid) {
-      const v8bf ov = ld8(os + e);
+      const float4 o0 = *(const float4*)(os + e), o1 = *(const float4*)(os + e + 4);
+      const float ov[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
 #pragma unroll
-      for (int x = 0; x < 8; x++) dpart += (float)dop[s][x] * (float)ov[x];
+      for (int x = 0; x < 8; x++) dpart += (float)dop[s][x] * ov[x];
     }
   }
   const float D = dpart + __shfl_xor(dpart, 32);
@@ -388,6 +398,454 @@ __global__ __launch_bounds__(128) void sla_bwd_dkdv_kernel(const uint16_t* __res
     }
 }
 
+// ------------------------------------------------------------------ backward: linear part
+// With phi = softmax over the channels, per query row: u = phi(q) H^c, s = phi(q) . z^c,
+// O_l = u / s, y = O_l W. Given dO:
+//   dO_l = dO W^T;  du = dO_l / s;  ds = -(dO_l . O_l) / s;
+//   dphi(q) = du H^c^T + ds z^c;  dq_l = phi (dphi - phi . dphi);
+//   dH^c_i = sum_{rows of i} phi(q)^T du,  dz^c_i = sum phi(q) ds;
+//   dH_j = sum of dH^c_i over the query blocks i that leave j out (likewise dz_j);
+//   dphi(k_t) = dH_j v_t + dz_j,  dv_l = phi(k_t) dH_j,  dk_l = phi (dphi - phi . dphi);
+//   dW = sum over rows of O_l^T dO.
+// State layouts: the forward's S^c = [H^c^T ; z^c] (row c < 128 holds H^c[.][c], row 128
+// z^c); the gradients dH^c_i and dH_j are stored as R = [dH ; dz] (row a < 128 holds
+// dH[a][.], row 128 dz), which the masked complement product treats alike.
+
+constexpr int kSp = 136;  // LDS row pitch (bf16) of a staged 129 x 128 state
+
+__device__ __forceinline__ void stage_state(uint16_t (*dst)[kSp], const uint16_t* src, int t, int nthr) {
+  for (int c = t; c < 129 * 16; c += nthr) {
+    const int row = c >> 4, col = (c & 15) * 8;
+    *(v4i*)&dst[row][col] = *(const v4i*)(src + row * kD + col);
+  }
+}
+
+// 8 bf16 of column `col` at rows r(e) = base + 8(e/4) + e%4 (e = 0..7) of a staged tile:
+// the token-reduction slot order of a 32x32 accumulator, with rows as the reduced index.
+__device__ __forceinline__ v8bf lds_col8(const uint16_t (*tile)[kSp], int base, int col) {
+  v8s x;
+#pragma unroll
+  for (int e = 0; e < 8; e++) x[e] = (short)tile[base + 8 * (e >> 2) + (e & 3)][col];
+  return __builtin_bit_cast(v8bf, x);
+}
+
+// Per (head, query block), lanes = query rows (2 waves x 32). Adds dq_l into dq and writes
+// phi(q), du, O_l (bf16, row-major) and ds (fp32) for the state gradients and dW.
+__global__ __launch_bounds__(128) void sla_lin_bwd_q_kernel(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ dout,
+                                                            const uint16_t* __restrict__ hc,
+                                                            const uint16_t* __restrict__ proj, int BH, int N, int Nb,
+                                                            int per_xcd, float* __restrict__ dq,
+                                                            uint16_t* __restrict__ phq_o, uint16_t* __restrict__ du_o,
+                                                            float* __restrict__ ds_o, uint16_t* __restrict__ ol_o) {
+  __shared__ __attribute__((aligned(16))) uint16_t sS[129][kSp];
+  const int tile = xcd_tile(blockIdx.x, per_xcd);
+  if (tile >= BH * Nb) return;
+  const int bh = tile / Nb, i = tile % Nb;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  const int qi = kBlk * i + 32 * w + r;
+  const bool qvalid = qi < N;
+  const size_t rowoff = ((size_t)bh * N + (qvalid ? qi : 0)) * kD;
+  stage_state(sS, hc + ((size_t)bh * Nb + i) * kStateElems, threadIdx.x, 128);
+
+  // phi(q) in the operand order (channels 16s + 8g .. +7), and the row's softmax stats
+  float x[64];
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    const v8bf a = qvalid ? ld8(q + rowoff + 16 * s + 8 * g) : (v8bf){};
+#pragma unroll
+    for (int e = 0; e < 8; e++) x[8 * s + e] = (float)a[e];
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 64; e++) mx = fmaxf(mx, x[e]);
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 64; e++) {
+    x[e] = __expf(x[e] - mx);
+    sum += x[e];
+  }
+  sum += __shfl_xor(sum, 32);
+  const float isum = 1.f / sum;
+  v8bf phb[8];
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+    float t8[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) t8[e] = x[8 * s + e] * isum;
+    phb[s] = pack8(t8);
+    if (qvalid) *(v8bf*)(phq_o + rowoff + 16 * s + 8 * g) = phb[s];
+  }
+  __syncthreads();
+
+  // u^T = S^c phi^T and dO_l^T = W dO^T (lanes = rows, registers = channels c)
+  v16f u[4], dl[4];
+  float zpart = 0.f;
+#pragma unroll
+  for (int s = 0; s < 8; s++) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) zpart += bf16_to_f32(sS[128][16 * s + 8 * g + e]) * (float)phb[s][e];
+  }
+  const float sden = zpart + __shfl_xor(zpart, 32);
+  v8bf dob[8];
+#pragma unroll
+  for (int s = 0; s < 8; s++) dob[s] = qvalid ? ld8(dout + rowoff + 16 * s + 8 * g) : (v8bf){};
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++) {
+    u[ct] = (v16f){};
+    dl[ct] = (v16f){};
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      u[ct] = mfma(*(const v8bf*)&sS[32 * ct + r][16 * s + 8 * g], phb[s], u[ct]);
+      dl[ct] = mfma(ld8(proj + (32 * ct + r) * kD + 16 * s + 8 * g), dob[s], dl[ct]);
+    }
+  }
+  const float is = 1.f / sden;
+  float dpart = 0.f;
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+      u[ct][v] *= is;  // O_l
+      dpart += dl[ct][v] * u[ct][v];
+    }
+  const float dsv = -(dpart + __shfl_xor(dpart, 32)) * is;
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) dl[ct][v] *= is;  // du
+  if (qvalid) {
+    if (g == 0) ds_o[(size_t)bh * N + qi] = dsv;
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; v4++) {
+        const int ch = 32 * ct + 8 * v4 + 4 * g;
+        uint2 a, b;
+        a.x = pack_bf16x2(u[ct][4 * v4], u[ct][4 * v4 + 1]);
+        a.y = pack_bf16x2(u[ct][4 * v4 + 2], u[ct][4 * v4 + 3]);
+        b.x = pack_bf16x2(dl[ct][4 * v4], dl[ct][4 * v4 + 1]);
+        b.y = pack_bf16x2(dl[ct][4 * v4 + 2], dl[ct][4 * v4 + 3]);
+        *(uint2*)(ol_o + rowoff + ch) = a;
+        *(uint2*)(du_o + rowoff + ch) = b;
+      }
+  }
+
+  // dphi^T[a][q] = sum_c H^c[a][c] du[q][c] + ds z^c[a]: A = S^c read down its columns,
+  // B = du in the accumulator's own register order
+  v16f dp[4];
+#pragma unroll
+  for (int at = 0; at < 4; at++) {
+    dp[at] = (v16f){};
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+        dp[at] = mfma(lds_col8(sS, 32 * ct + 16 * t + 4 * g, 32 * at + r), pack8v(dl[ct], 8 * t), dp[at]);
+  }
+  // phi(q) at the accumulator's channels a = 32at + 8(v/4) + 4g + v%4, then dq_l
+  float ph[4][16], dot = 0.f;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; v4++) {
+      const int ch = 32 * at + 8 * v4 + 4 * g;
+      const uint2 raw = qvalid ? *(const uint2*)(q + rowoff + ch) : make_uint2(0u, 0u);
+      const float f[4] = {__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xFFFF0000u),
+                          __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int v = 4 * v4 + e;
+        ph[at][v] = __expf(f[e] - mx) * isum;
+        dp[at][v] += dsv * bf16_to_f32(sS[128][ch + e]);
+        dot += ph[at][v] * dp[at][v];
+      }
+    }
+  dot += __shfl_xor(dot, 32);
+  if (!qvalid) return;
+  float* drow = dq + rowoff;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; v4++) {
+      const int ch = 32 * at + 8 * v4 + 4 * g;
+      float4 o = *(float4*)(drow + ch);
+      o.x += ph[at][4 * v4] * (dp[at][4 * v4] - dot);
+      o.y += ph[at][4 * v4 + 1] * (dp[at][4 * v4 + 1] - dot);
+      o.z += ph[at][4 * v4 + 2] * (dp[at][4 * v4 + 2] - dot);
+      o.w += ph[at][4 * v4 + 3] * (dp[at][4 * v4 + 3] - dot);
+      *(float4*)(drow + ch) = o;
+    }
+}
+
+// Per (head, 16 consecutive query blocks): R_i = [dH^c_i ; dz^c_i] (bf16) for each block and
+// their fp32 sum (the chunk's partial of the total). Wave w owns channels a = 32w .. +31:
+// D[c][a] = sum_t du[t][c] phi[t][a] on the token-reduction tiles of du and phi; the ds
+// row enters as a fifth tile whose only non-zero row is c = 0.
+__global__ __launch_bounds__(256) void sla_lin_dhc_kernel(const uint16_t* __restrict__ phqt,
+                                                          const uint16_t* __restrict__ dut,
+                                                          const float* __restrict__ ds, int BH, int N, int Nb,
+                                                          uint16_t* __restrict__ rs, float* __restrict__ rpart) {
+  const int nc = (Nb + kChunk - 1) / kChunk;
+  const int bh = blockIdx.x / nc, chunk = blockIdx.x % nc;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  v16f cs[5];
+#pragma unroll
+  for (int ct = 0; ct < 5; ct++) cs[ct] = (v16f){};
+  const int i0 = chunk * kChunk, i1 = min(Nb, i0 + kChunk);
+  for (int i = i0; i < i1; i++) {
+    const size_t tb = ((size_t)bh * Nb + i) * kTrTile + l * 8;
+    v16f acc[5];
+#pragma unroll
+    for (int ct = 0; ct < 5; ct++) acc[ct] = (v16f){};
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const v8bf b = ld8(phqt + tb + ((tt * 4 + w) * 2 + t) * 512);
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(ld8(dut + tb + ((tt * 4 + ct) * 2 + t) * 512), b, acc[ct]);
+        float dv8[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int tok = kBlk * i + 32 * tt + 16 * t + 8 * (e >> 2) + 4 * g + (e & 3);
+          dv8[e] = (r == 0 && tok < N) ? ds[(size_t)bh * N + tok] : 0.f;
+        }
+        acc[4] = mfma(pack8(dv8), b, acc[4]);
+      }
+    // D[c][a]: lane = a (32w + r), registers = c rows 32ct + 8(v/4) + 4g + v%4
+    uint16_t* R = rs + ((size_t)bh * Nb + i) * kStateElems;
+    const int a = 32 * w + r;
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int c = 32 * ct + 8 * (v >> 2) + 4 * g + (v & 3);
+        R[a * kD + c] = f32_to_bf16(acc[ct][v]);
+        cs[ct][v] += acc[ct][v];
+      }
+    if (g == 0) R[kD * kD + a] = f32_to_bf16(acc[4][0]);
+    cs[4][0] += acc[4][0];
+  }
+  float* P = rpart + ((size_t)bh * nc + chunk) * kStateElems;
+  const int a = 32 * w + r;
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) P[a * kD + 32 * ct + 8 * (v >> 2) + 4 * g + (v & 3)] = cs[ct][v];
+  if (g == 0) P[kD * kD + a] = cs[4][0];
+}
+
+// Per (bh, group of kGroup key blocks): the ascending union of the query blocks that keep
+// any key block of the group (or, complement != 0, that leave it out), and one bit row per
+// key block over the union positions, in the layout of the forward's union lists, from the
+// transposed kept mask.
+__global__ __launch_bounds__(256) void sla_union_t_kernel(const uint32_t* __restrict__ mask, int Nb, int nw, int ng,
+                                                          int complement, int32_t* __restrict__ ulist,
+                                                          uint32_t* __restrict__ umask, int32_t* __restrict__ ucount) {
+  extern __shared__ uint32_t sh[];  // U[nw], base[nw + 1]
+  uint32_t* U = sh;
+  uint32_t* base = sh + nw;
+  const int bh = blockIdx.x / ng, grp = blockIdx.x % ng;
+  const int t = threadIdx.x, j = grp * kGroup + t;
+  const bool jv = j < Nb;
+  const uint32_t* row = mask + ((size_t)bh * Nb + (jv ? j : 0)) * nw;
+  auto bits_of = [&](int wi) -> uint32_t {
+    uint32_t b = jv ? row[wi] : 0u;
+    if (complement && jv) {
+      b = ~b;
+      const int lo = 32 * wi;
+      if (lo + 32 > Nb) b &= (Nb - lo) >= 32 ? 0xFFFFFFFFu : ((1u << (Nb - lo)) - 1u);
+    }
+    return b;
+  };
+  for (int wi = t; wi < nw; wi += 256) U[wi] = 0u;
+  __syncthreads();
+  for (int wi = 0; wi < nw; wi++) {
+    const uint32_t b = bits_of(wi);
+    if (b) atomicOr(&U[wi], b);
+  }
+  __syncthreads();
+  if (t == 0) {
+    uint32_t acc = 0;
+    for (int wi = 0; wi < nw; wi++) {
+      base[wi] = acc;
+      acc += __popc(U[wi]);
+    }
+    base[nw] = acc;
+    ucount[(size_t)bh * ng + grp] = (int32_t)acc;
+  }
+  __syncthreads();
+  int32_t* ul = ulist + ((size_t)bh * ng + grp) * Nb;
+  for (int wi = t; wi < nw; wi += 256) {
+    uint32_t b = U[wi];
+    int p = (int)base[wi];
+    while (b) {
+      ul[p++] = 32 * wi + __builtin_ctz(b);
+      b &= b - 1;
+    }
+  }
+  // this key block's bit row over the union positions, one 32-position word at a time
+  uint32_t* um = umask + ((size_t)bh * ng + grp) * (size_t)nw * kGroup;
+  const int total = (int)base[nw];
+  uint32_t word = 0u;
+  int p = 0;
+  for (int wi = 0; wi < nw; wi++) {
+    uint32_t b = U[wi];
+    const uint32_t mine = bits_of(wi);
+    while (b) {
+      const uint32_t low = b & (0u - b);
+      if (mine & low) word |= 1u << (p & 31);
+      b &= b - 1;
+      if ((++p & 31) == 0) {
+        um[(size_t)((p >> 5) - 1) * kGroup + t] = word;
+        word = 0u;
+      }
+    }
+  }
+  if (p & 31) um[(size_t)(p >> 5) * kGroup + t] = word;
+  for (int pw = (total + 31) / 32; pw < nw; pw++) um[(size_t)pw * kGroup + t] = 0u;
+}
+
+// Per (head, key block), lanes = keys (2 waves x 32): adds dk_l and dv_l from R_j = [dH_j ; dz_j].
+__global__ __launch_bounds__(128) void sla_lin_bwd_k_kernel(const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v,
+                                                            const uint16_t* __restrict__ rj, int BH, int N, int Nb,
+                                                            int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
+  __shared__ __attribute__((aligned(16))) uint16_t sR[129][kSp];
+  const int tile = xcd_tile(blockIdx.x, per_xcd);
+  if (tile >= BH * Nb) return;
+  const int bh = tile / Nb, j = tile % Nb;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  const int kj = kBlk * j + 32 * w + r;
+  const bool kvalid = kj < N;
+  const size_t rowoff = ((size_t)bh * N + (kvalid ? kj : 0)) * kD;
+  stage_state(sR, rj + ((size_t)bh * Nb + j) * kStateElems, threadIdx.x, 128);
+  v8bf vb[8];
+#pragma unroll
+  for (int s = 0; s < 8; s++) vb[s] = kvalid ? ld8(v + rowoff + 16 * s + 8 * g) : (v8bf){};
+  // phi(k) at the accumulator's channels a = 32at + 8(v/4) + 4g + v%4
+  float ph[4][16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; v4++) {
+      const uint2 raw = kvalid ? *(const uint2*)(k + rowoff + 32 * at + 8 * v4 + 4 * g) : make_uint2(0u, 0u);
+      ph[at][4 * v4] = __uint_as_float(raw.x << 16);
+      ph[at][4 * v4 + 1] = __uint_as_float(raw.x & 0xFFFF0000u);
+      ph[at][4 * v4 + 2] = __uint_as_float(raw.y << 16);
+      ph[at][4 * v4 + 3] = __uint_as_float(raw.y & 0xFFFF0000u);
+#pragma unroll
+      for (int e = 0; e < 4; e++) mx = fmaxf(mx, ph[at][4 * v4 + e]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  float sum = 0.f;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int x = 0; x < 16; x++) {
+      ph[at][x] = __expf(ph[at][x] - mx);
+      sum += ph[at][x];
+    }
+  sum += __shfl_xor(sum, 32);
+  const float isum = 1.f / sum;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int x = 0; x < 16; x++) ph[at][x] *= isum;
+  __syncthreads();
+
+  // dphi^T[a][t] = sum_c dH[a][c] v[t][c] + dz[a]
+  v16f dp[4];
+  float dot = 0.f;
+#pragma unroll
+  for (int at = 0; at < 4; at++) {
+    dp[at] = (v16f){};
+#pragma unroll
+    for (int s = 0; s < 8; s++) dp[at] = mfma(*(const v8bf*)&sR[32 * at + r][16 * s + 8 * g], vb[s], dp[at]);
+#pragma unroll
+    for (int x = 0; x < 16; x++) {
+      dp[at][x] += bf16_to_f32(sR[128][32 * at + 8 * (x >> 2) + 4 * g + (x & 3)]);
+      dot += ph[at][x] * dp[at][x];
+    }
+  }
+  dot += __shfl_xor(dot, 32);
+  // dv_l^T[c][t] = sum_a dH[a][c] phi[t][a]: A = R read down its columns, B = phi in the
+  // accumulator's register order
+  v16f dva[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++) {
+    dva[ct] = (v16f){};
+#pragma unroll
+    for (int at = 0; at < 4; at++)
+#pragma unroll
+      for (int t = 0; t < 2; t++)
+        dva[ct] = mfma(lds_col8(sR, 32 * at + 16 * t + 4 * g, 32 * ct + r), pack8(&ph[at][8 * t]), dva[ct]);
+  }
+  if (!kvalid) return;
+  float* krow = dk + rowoff;
+  float* vrow = dv + rowoff;
+#pragma unroll
+  for (int at = 0; at < 4; at++)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; v4++) {
+      const int ch = 32 * at + 8 * v4 + 4 * g;
+      float4 o = *(float4*)(krow + ch);
+      o.x += ph[at][4 * v4] * (dp[at][4 * v4] - dot);
+      o.y += ph[at][4 * v4 + 1] * (dp[at][4 * v4 + 1] - dot);
+      o.z += ph[at][4 * v4 + 2] * (dp[at][4 * v4 + 2] - dot);
+      o.w += ph[at][4 * v4 + 3] * (dp[at][4 * v4 + 3] - dot);
+      *(float4*)(krow + ch) = o;
+      float4 p = *(float4*)(vrow + ch);
+      p.x += dva[at][4 * v4];
+      p.y += dva[at][4 * v4 + 1];
+      p.z += dva[at][4 * v4 + 2];
+      p.w += dva[at][4 * v4 + 3];
+      *(float4*)(vrow + ch) = p;
+    }
+}
+
+// dW partial sums: workgroup p adds O_l^T dO over its share of the (head, block) pairs;
+// wave w owns rows c = 32w .. +31 of dW. Then one pass adds the partials.
+constexpr int kDwParts = 512;
+
+__global__ __launch_bounds__(256) void sla_dw_partial_kernel(const uint16_t* __restrict__ olt,
+                                                             const uint16_t* __restrict__ dot_, int nblocks,
+                                                             float* __restrict__ part) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  const int per = (nblocks + kDwParts - 1) / kDwParts;
+  const int b0 = blockIdx.x * per, b1 = min(nblocks, b0 + per);
+  v16f acc[4];
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++) acc[ct] = (v16f){};
+  for (int b = b0; b < b1; b++) {
+    const size_t tb = (size_t)b * kTrTile + l * 8;
+#pragma unroll
+    for (int tt = 0; tt < 2; tt++)
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        const v8bf a = ld8(olt + tb + ((tt * 4 + w) * 2 + t) * 512);
+#pragma unroll
+        for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(a, ld8(dot_ + tb + ((tt * 4 + ct) * 2 + t) * 512), acc[ct]);
+      }
+  }
+  // D[c][c']: row c = 32w + 8(v/4) + 4g + v%4, column c' = 32ct + r
+  float* P = part + (size_t)blockIdx.x * kD * kD;
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) P[(32 * w + 8 * (v >> 2) + 4 * g + (v & 3)) * kD + 32 * ct + r] = acc[ct][v];
+}
+
+__global__ __launch_bounds__(256) void sla_dw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw) {
+  const int e = blockIdx.x * 256 + threadIdx.x;  // kD * kD elements
+  float s = 0.f;
+  for (int p = 0; p < kDwParts; p++) s += part[(size_t)p * kD * kD + e];
+  dw[e] = s;
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_sla_relayout(const void* x, int BH, int N, int Nb, void* xt, hipStream_t st) {
   hipLaunchKernelGGL(sla_relayout_kernel, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)x, N, Nb, (uint16_t*)xt);
@@ -410,7 +868,7 @@ hipError_t launch_sla_fwd(const void* q, const void* k, const void* vt, const vo
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sla_fwd_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)vt, (const int*)idx, (const uint16_t*)y, BH, N, Nb, ksel, per_xcd,
-                     (uint16_t*)out, (uint16_t*)os, (float*)lse);
+                     (uint16_t*)out, (float*)os, (float*)lse);
   return hipGetLastError();
 }
 
@@ -419,7 +877,7 @@ hipError_t launch_sla_bwd_dq(const void* q, const void* k, const void* v, const 
                              void* dsum, void* dq, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sla_bwd_dq_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)kt, (const uint16_t*)dout, (const uint16_t*)os,
+                     (const uint16_t*)v, (const uint16_t*)kt, (const uint16_t*)dout, (const float*)os,
                      (const float*)lse, (const int*)idx, BH, N, Nb, ksel, per_xcd, (float*)dsum, (float*)dq);
   return hipGetLastError();
 }
@@ -435,4 +893,54 @@ hipError_t launch_sla_bwd_dkdv(const void* q, const void* k, const void* v, cons
   return hipGetLastError();
 }
 
+hipError_t launch_sla_lin_bwd_q(const void* q, const void* dout, const void* hc, const void* proj, int BH, int N,
+                                int Nb, void* dq, void* phq, void* du, void* ds, void* ol, hipStream_t st) {
+  const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL(sla_lin_bwd_q_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)dout, (const uint16_t*)hc, (const uint16_t*)proj, BH, N, Nb, per_xcd,
+                     (float*)dq, (uint16_t*)phq, (uint16_t*)du, (float*)ds, (uint16_t*)ol);
+  return hipGetLastError();
+}
+
+hipError_t launch_sla_lin_dhc(const void* phqt, const void* dut, const void* ds, int BH, int N, int Nb, void* rs,
+                              void* rpart, hipStream_t st) {
+  const int nc = (Nb + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(sla_lin_dhc_kernel, dim3(BH * nc), dim3(256), 0, st, (const uint16_t*)phqt,
+                     (const uint16_t*)dut, (const float*)ds, BH, N, Nb, (uint16_t*)rs, (float*)rpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_sla_union_t(const void* mask, int BH, int Nb, int ksel, void* ulist, void* umask, void* ucount,
+                              hipStream_t st) {
+  const int nw = (Nb + 31) / 32, ng = (Nb + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(sla_union_t_kernel, dim3(BH * ng), dim3(256), (2 * nw + 1) * sizeof(uint32_t), st,
+                     (const uint32_t*)mask, Nb, nw, ng, 2 * ksel > Nb ? 1 : 0, (int32_t*)ulist, (uint32_t*)umask,
+                     (int32_t*)ucount);
+  return hipGetLastError();
+}
+
+hipError_t launch_sla_lin_bwd_k(const void* k, const void* v, const void* rj, int BH, int N, int Nb, void* dk,
+                                void* dv, hipStream_t st) {
+  const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
+  hipLaunchKernelGGL(sla_lin_bwd_k_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)k,
+                     (const uint16_t*)v, (const uint16_t*)rj, BH, N, Nb, per_xcd, (float*)dk, (float*)dv);
+  return hipGetLastError();
+}
+
+hipError_t launch_sla_dw(const void* olt, const void* dot, int nblocks, void* part, void* dw, hipStream_t st) {
+  hipLaunchKernelGGL(sla_dw_partial_kernel, dim3(kDwParts), dim3(256), 0, st, (const uint16_t*)olt,
+                     (const uint16_t*)dot, nblocks, (float*)part);
+  hipLaunchKernelGGL(sla_dw_reduce_kernel, dim3(kD * kD / 256), dim3(256), 0, st, (const float*)part, (float*)dw);
+  return hipGetLastError();
+}
+
+int sla_dw_parts() { return kDwParts; }
+
+hipError_t launch_sla_zero(void* p, size_t words, hipStream_t st) {
+  const int blocks = (int)((words + 255) / 256 < 65536 ? (words + 255) / 256 : 65536);
+  hipLaunchKernelGGL(sla_fill_kernel, dim3(blocks), dim3(256), 0, st, (uint32_t*)p, words);
+  return hipGetLastError();
+}
+
 }  // namespace sagesla
+
