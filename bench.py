@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-blocks", type=int, default=200, help="query blocks in the oracle sample")
     ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 linear-layer measurement")
+    ap.add_argument("--no-sla-train", action="store_true", help="skip the SLA training-path measurement")
     ap.add_argument("--w8a8-shape", default="75600,5120,5120", help="M,K,N of the W8A8 linear layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MiB (a kernel of known "
@@ -209,7 +210,75 @@ def main():
         res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks)
     if not args.no_w8a8:
         res["w8a8"] = w8a8_measure(args)
+    if not args.no_sla_train:
+        res["sla_train"] = sla_train_measure(args, cfg, x)
     print(json.dumps(res), flush=True)
+
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+
+def sla_train_measure(args, cfg, x):
+    """The trainable SLA path on the same inputs: the unquantized forward (saving what the
+    backward needs) and the backward (dQ, dK, dV, dW) from a seeded dO, each timed with HIP
+    events on the launch stream over the same number of steps."""
+    import sparse_attention_sagesla_amd as S
+    B, H, N, d, topk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.topk
+    q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
+    dev = q.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 77)
+    dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ws = torch.empty(S.sla_workspace_size(B, H, N, d, 64, topk, proj is not None), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+    dproj = torch.empty((d, d), dtype=torch.float32, device=dev) if proj is not None else None
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        S.sla_fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)
+
+    def bwd():
+        S.sla_bwd(q, k, v, dout, ws, proj=proj, topk=topk, dq=grads[0], dk=grads[1], dv=grads[2], dproj=dproj)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    steps = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for s_ in range(steps):
+        ev[s_][0].record(stream)
+        fwd()
+        ev[s_][1].record(stream)
+        bwd()
+        ev[s_][2].record(stream)
+    torch.cuda.synchronize()
+    ms_f = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    ms_b = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    # executed products from the actual kept lists: forward QK^T and PV, backward S, dP, dQ
+    # (query side) and S, dP, dV, dK (key side), each 2 n_i n_j d flops per kept pair
+    idx = S.sla_workspace_views(ws, B, H, N, topk=topk, linear=proj is not None)["idx"].long()
+    Nb = (N + 63) // 64
+    nlen = torch.full((Nb,), 64, dtype=torch.int64, device=dev)
+    nlen[-1] = N - 64 * (Nb - 1)
+    pair_tok = float((nlen[idx].sum(-1) * nlen[None, :]).sum().item())
+    f_fwd, f_bwd = 4.0 * d * pair_tok, 14.0 * d * pair_tok
+    tf_f, tf_b = f_fwd / (ms_f * 1e-3) / 1e12, f_bwd / (ms_b * 1e-3) / 1e12
+    return {
+        "workload": "%s: B=%d H=%d N=%d d=%d topk=%g, linear branch %s; one step = forward + backward" % (
+            cfg.name, B, H, N, d, topk, "on" if proj is not None else "off"),
+        "dtype": "bf16 (MFMA), fp32 softmax and accumulation; gradients fp32",
+        "ms_fwd": round(ms_f, 4),
+        "ms_bwd": round(ms_b, 4),
+        "ms_step": round(ms_f + ms_b, 4),
+        "fwd_sparse_tflops": round(tf_f, 1),
+        "bwd_sparse_tflops": round(tf_b, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf_b, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "backward pass (sparse products; the linear part's time included)",
+                     "work_per_launch_flops": f_bwd},
+    }
 
 
 def w8a8_measure(args):
