@@ -142,3 +142,81 @@ def sla_backward(q, k, v, w, idx, dout, blk=64):
     return dict(dq=dq_s + dq_l, dk=dk_s + dk_l, dv=dv_s + dv_l, dw=dw, dq_s=dq_s, dk_s=dk_s, dv_s=dv_s,
                 dq_l=dq_l, dk_l=dk_l, dv_l=dv_l, lse=fw["lse"], out=fw["out"], out_s=fw["out_s"],
                 out_l=fw["out_l"])
+
+
+def sla_backward_rows(q, k, v, w, idx, dout, qblocks, kblocks, blk=64):
+    """The same gradients as sla_backward, for the rows of some blocks only: dq on the query
+    blocks `qblocks`, dk and dv on the key blocks `kblocks` (for inputs too long to
+    differentiate whole). The sparse part needs, per key block, every query block that keeps
+    it; the linear part needs the complement-state gradients of every query block, which
+    are cheap (one 128 x 128 product each). Returns dict(dq, dk, dv) of {block: rows}."""
+    q, k, v, dout = (np.asarray(a, np.float64) for a in (q, k, v, dout))
+    N, d = q.shape
+    Nb, sl = _blocks(N, blk)
+    scale = 1.0 / np.sqrt(d)
+
+    def sparse_rows(i):
+        cols = _kept_tokens(idx[i], sl)
+        s = q[sl[i]] @ k[cols].T * scale
+        m = s.max(axis=1, keepdims=True)
+        p = np.exp(s - m)
+        p /= p.sum(axis=1, keepdims=True)
+        o_s = p @ v[cols]
+        do = dout[sl[i]]
+        dp = do @ v[cols].T
+        D = (do * o_s).sum(axis=1)
+        return cols, p, p * (dp - D[:, None])
+
+    dq = {i: np.zeros((sl[i].stop - sl[i].start, d)) for i in qblocks}
+    dk = {j: np.zeros((sl[j].stop - sl[j].start, d)) for j in kblocks}
+    dv = {j: np.zeros((sl[j].stop - sl[j].start, d)) for j in kblocks}
+    for i in qblocks:
+        cols, p, ds = sparse_rows(i)
+        dq[i] += ds @ k[cols] * scale
+    keepers = {j: [i for i in range(Nb) if j in set(int(t) for t in idx[i])] for j in kblocks}
+    for j in kblocks:
+        for i in keepers[j]:
+            cols, p, ds = sparse_rows(i)
+            at = np.flatnonzero((cols >= sl[j].start) & (cols < sl[j].stop))
+            dv[j] += p[:, at].T @ dout[sl[i]]
+            dk[j] += ds[:, at].T @ q[sl[i]] * scale
+
+    if w is not None:
+        w = np.asarray(w, np.float64)
+        phq, phk = _softmax_rows(q), _softmax_rows(k)
+        H = np.stack([phk[sl[j]].T @ v[sl[j]] for j in range(Nb)])
+        z = np.stack([phk[sl[j]].sum(axis=0) for j in range(Nb)])
+        dH, dz = np.zeros_like(H), np.zeros_like(z)
+        # C[i][j] = 1 when query block i leaves key block j out: every complement sum at
+        # once as one product with the 0/1 matrix (the same sums over the blocks not kept)
+        C = np.ones((Nb, Nb))
+        for i in range(Nb):
+            C[i, np.asarray(idx[i], int)] = 0.0
+        Hc_all = (C @ H.reshape(Nb, -1)).reshape(H.shape)
+        zc_all = C @ z
+        for i in range(Nb):
+            if not C[i].any():
+                continue
+            Hc, zc = Hc_all[i], zc_all[i]
+            u = phq[sl[i]] @ Hc
+            s = phq[sl[i]] @ zc
+            ol = u / s[:, None]
+            dol = dout[sl[i]] @ w.T
+            du = dol / s[:, None]
+            dsv = -(dol * ol).sum(axis=1) / s
+            if i in dq:
+                dph = du @ Hc.T + dsv[:, None] * zc[None, :]
+                p_ = phq[sl[i]]
+                dq[i] += p_ * (dph - (p_ * dph).sum(axis=1, keepdims=True))
+            dHc = phq[sl[i]].T @ du
+            dzc = phq[sl[i]].T @ dsv
+            for j in kblocks:
+                if C[i, j]:
+                    dH[j] += dHc
+                    dz[j] += dzc
+        for j in kblocks:
+            p_ = phk[sl[j]]
+            dph = v[sl[j]] @ dH[j].T + dz[j][None, :]
+            dk[j] += p_ * (dph - (p_ * dph).sum(axis=1, keepdims=True))
+            dv[j] += p_ @ dH[j]
+    return dict(dq=dq, dk=dk, dv=dv)

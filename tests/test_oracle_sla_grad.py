@@ -131,3 +131,19 @@ def test_linear_off_when_all_blocks_kept():
     idx = np.tile(np.arange(3, dtype=np.int32), (3, 1))
     g = G.sla_backward(q, k, v, w, idx, dout, blk)
     assert not g["dq_l"].any() and not g["dk_l"].any() and not g["dv_l"].any() and not g["dw"].any()
+
+
+@pytest.mark.parametrize("linear", [False, True])
+def test_rows_match_whole_backward(linear):
+    """The row-sampled gradients equal the whole backward's rows (same formulas, taken a
+    block at a time)."""
+    N, d, blk = 300, 16, 32
+    q, k, v, w, dout, idx = make(N, d, 11, 3, blk, linear=linear)
+    g = G.sla_backward(q, k, v, w, idx, dout, blk)
+    qb, kb = [0, 4, 9], [1, 5, 9]
+    r = G.sla_backward_rows(q, k, v, w, idx, dout, qb, kb, blk)
+    for i in qb:
+        assert np.allclose(r["dq"][i], g["dq"][i * blk:min(N, (i + 1) * blk)], rtol=1e-10, atol=1e-12)
+    for j in kb:
+        assert np.allclose(r["dk"][j], g["dk"][j * blk:min(N, (j + 1) * blk)], rtol=1e-10, atol=1e-12)
+        assert np.allclose(r["dv"][j], g["dv"][j * blk:min(N, (j + 1) * blk)], rtol=1e-10, atol=1e-12)
