@@ -23,6 +23,7 @@ hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*
                               const void*, const void*, int, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_relayout(const void*, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_kept_mask(const void*, int, int, int, void*, hipStream_t);
+hipError_t launch_sla_relayout_hd(const void*, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_fwd(const void*, const void*, const void*, const void*, const void*, int, int, int, int, void*,
                           void*, void*, hipStream_t);
 hipError_t launch_sla_bwd_dq(const void*, const void*, const void*, const void*, const void*, const void*, const void*,
@@ -494,7 +495,10 @@ sagesla_status sagesla_sla_fwd(const void* q, const void* k, const void* v, cons
       return from_hip(e);
   }
   if ((e = launch_sla_relayout(v, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_VT), st)) != hipSuccess) return from_hip(e);
-  e = launch_sla_fwd(q, k, P(SAGESLA_SLA_WS_VT), P(SAGESLA_WS_IDX), linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH,
+  // K in head-dim-reduction tiles (in the K tile region, which the backward rewrites)
+  if ((e = launch_sla_relayout_hd(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_KT), st)) != hipSuccess)
+    return from_hip(e);
+  e = launch_sla_fwd(q, P(SAGESLA_SLA_WS_KT), P(SAGESLA_SLA_WS_VT), P(SAGESLA_WS_IDX), linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH,
                      gm.N, gm.Nb, gm.ksel, out, P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE), st);
   return from_hip(e);
 }

@@ -86,6 +86,25 @@ __global__ __launch_bounds__(256) void sla_relayout_kernel(const uint16_t* __res
   }
 }
 
+// X [BH][N][128] bf16 -> "head-dim-reduction tiles" [BH][Nb][kTrTile]: chunk (tt*8 + s)*64 + l
+// holds X[32tt + r][16s + 8g .. +7], the operand order of products that reduce over the head
+// dimension, so that one operand is one lane-contiguous 1 KiB read (tokens past N are 0).
+__global__ __launch_bounds__(256) void sla_relayout_hd_kernel(const uint16_t* __restrict__ x, int N, int Nb,
+                                                              uint16_t* __restrict__ xh) {
+  const int bh = blockIdx.x / Nb, blk = blockIdx.x % Nb, t = threadIdx.x;
+  const int n = block_len(blk, N);
+  const uint16_t* src = x + ((size_t)bh * N + (size_t)blk * kBlk) * kD;
+  uint16_t* dst = xh + ((size_t)bh * Nb + blk) * kTrTile;
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int c = t + 256 * k;  // chunk (tt*8 + s)*64 + l
+    const int l = c & 63, s = (c >> 6) & 7, tt = c >> 9, row = 32 * tt + (l & 31), col = 16 * s + 8 * (l >> 5);
+    v4i val = (v4i){0, 0, 0, 0};
+    if (row < n) val = *(const v4i*)(src + (size_t)row * kD + col);
+    *(v4i*)(dst + (size_t)c * 8) = val;
+  }
+}
+
 // ------------------------------------------------------------------ transposed kept sets
 // mask[bh][j][i / 32] bit i % 32 set when query block i keeps key block j.
 __global__ __launch_bounds__(256) void sla_fill_kernel(uint32_t* __restrict__ p, size_t n) {
@@ -104,14 +123,21 @@ __global__ __launch_bounds__(256) void sla_kept_mask_kernel(const int* __restric
 
 // ------------------------------------------------------------------ forward
 // One workgroup (2 waves) per (head, query block); wave w owns query rows 32w .. +31, one
-// per lane column. Per kept key block: S^T = K Q^T (two 32-key tiles), online softmax in
-// the base-2 domain, O^T += V^T P^T. Epilogue: O_s (fp32, for the backward's D), lse, and
-// out = O_s + y (bf16).
+// per lane column. The kept key blocks' K (head-dim-reduction tiles) and V (token-reduction
+// tiles) arrive by DMA in a two-stage LDS ring, one block ahead, and both waves read them
+// there. Per block: S^T = K Q^T (two 32-key tiles), online softmax in the base-2 domain,
+// O^T += V^T P^T. Epilogue: O_s (fp32, for the backward's D), lse, and out = O_s + y (bf16).
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ vt, const int* __restrict__ idx,
                                                       const uint16_t* __restrict__ y, int BH, int N, int Nb, int ksel,
                                                       int per_xcd, uint16_t* __restrict__ out,
                                                       float* __restrict__ os, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV1[kTrTile];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, i = tile % Nb;
@@ -119,7 +145,6 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
   const int qi = kBlk * i + 32 * w + r;
   const bool qvalid = qi < N;
   const uint16_t* Qh = q + (size_t)bh * N * kD;
-  const uint16_t* Kh = k + (size_t)bh * N * kD;
   const float c = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
 
   v8bf qop[8];
@@ -133,17 +158,25 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
   for (int ct = 0; ct < 4; ct++) o[ct] = (v16f){};
 
   const int* irow = idx + ((size_t)bh * Nb + i) * ksel;
-  for (int kk = 0; kk < ksel; kk++) {
-    const int j = irow[kk];
+  // each wave copies half of each 16 KiB tile: 8 DMAs of 1 KiB (16 bytes per lane)
+  auto issue = [&](uint16_t* dk_, uint16_t* dv_, int j) {
+    const uint16_t* ks = k + ((size_t)bh * Nb + j) * kTrTile + (w * 8 * 64 + l) * 8;
+    const uint16_t* vs = vt + ((size_t)bh * Nb + j) * kTrTile + (w * 8 * 64 + l) * 8;
+#pragma unroll
+    for (int cc = 0; cc < 8; cc++)
+      __builtin_amdgcn_global_load_lds((const void*)(ks + cc * 512), (lds_ptr_t)(dk_ + (w * 8 + cc) * 512), 16, 0, 0);
+#pragma unroll
+    for (int cc = 0; cc < 8; cc++)
+      __builtin_amdgcn_global_load_lds((const void*)(vs + cc * 512), (lds_ptr_t)(dv_ + (w * 8 + cc) * 512), 16, 0, 0);
+  };
+  auto compute = [&](const uint16_t* ck, const uint16_t* cv, int j) {
     const int nj = block_len(j, N);
     float sc[2][16];
 #pragma unroll
     for (int kt = 0; kt < 2; kt++) {
-      const int kr = 32 * kt + r;
-      const uint16_t* krow = Kh + ((size_t)j * kBlk + kr) * kD + 8 * g;
       v16f acc = (v16f){};
 #pragma unroll
-      for (int s = 0; s < 8; s++) acc = mfma(kr < nj ? ld8(krow + 16 * s) : (v8bf){}, qop[s], acc);
+      for (int s = 0; s < 8; s++) acc = mfma(*(const v8bf*)(ck + ((kt * 8 + s) * 64 + l) * 8), qop[s], acc);
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int key = 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
@@ -173,15 +206,29 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
     for (int ct = 0; ct < 4; ct++)
 #pragma unroll
       for (int v = 0; v < 16; v++) o[ct][v] *= alpha;
-    const uint16_t* vb = vt + ((size_t)bh * Nb + j) * kTrTile + l * 8;
 #pragma unroll
     for (int kt = 0; kt < 2; kt++)
 #pragma unroll
       for (int t = 0; t < 2; t++) {
         const v8bf pb = pack8(&sc[kt][8 * t]);
 #pragma unroll
-        for (int ct = 0; ct < 4; ct++) o[ct] = mfma(ld8(vb + ((kt * 4 + ct) * 2 + t) * 512), pb, o[ct]);
+        for (int ct = 0; ct < 4; ct++)
+          o[ct] = mfma(*(const v8bf*)(cv + ((((kt * 4 + ct) * 2 + t) * 64) + l) * 8), pb, o[ct]);
       }
+  };
+
+  issue(sK0, sV0, irow[0]);
+  for (int kk = 0; kk < ksel; kk += 2) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs of block kk have landed
+    __syncthreads();                // and the other wave's; all reads of the other stage are done
+    if (kk + 1 < ksel) issue(sK1, sV1, irow[kk + 1]);
+    compute(sK0, sV0, irow[kk]);
+    if (kk + 1 < ksel) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kk + 2 < ksel) issue(sK0, sV0, irow[kk + 2]);
+      compute(sK1, sV1, irow[kk + 1]);
+    }
   }
 
   if (!qvalid) return;
@@ -849,6 +896,12 @@ __global__ __launch_bounds__(256) void sla_dw_reduce_kernel(const float* __restr
 // ------------------------------------------------------------------ launchers
 hipError_t launch_sla_relayout(const void* x, int BH, int N, int Nb, void* xt, hipStream_t st) {
   hipLaunchKernelGGL(sla_relayout_kernel, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)x, N, Nb, (uint16_t*)xt);
+  return hipGetLastError();
+}
+
+hipError_t launch_sla_relayout_hd(const void* x, int BH, int N, int Nb, void* xh, hipStream_t st) {
+  hipLaunchKernelGGL(sla_relayout_hd_kernel, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)x, N, Nb,
+                     (uint16_t*)xh);
   return hipGetLastError();
 }
 
