@@ -194,6 +194,8 @@ typedef enum {
     SAGESLA_SLA_WS_DOT,   /* bf16 [BH][Nb][8192] dO token-reduction tiles (backward)      */
     SAGESLA_SLA_WS_DSUM,  /* fp32 [BH][N]        D = rowsum(dO * O_s) (backward)          */
     SAGESLA_SLA_WS_MASK,  /* u32 [BH][Nb][ceil(Nb/32)] bit i of row j: query block i keeps j */
+    SAGESLA_SLA_WS_H0,    /* bf16 [BH][Nb][8192] head-dim-reduction tiles (below) of K, then of Q */
+    SAGESLA_SLA_WS_H1,    /* bf16 [BH][Nb][8192] head-dim-reduction tiles of dO (backward) */
     SAGESLA_SLA_WS_PHQ,   /* bf16 [BH][N][d] phi(q)                          (linear)   */
     SAGESLA_SLA_WS_DU,    /* bf16 [BH][N][d] du = dO_l / s                   (linear)   */
     SAGESLA_SLA_WS_OL,    /* bf16 [BH][N][d] O_l                             (linear)   */
@@ -203,7 +205,10 @@ typedef enum {
 } sagesla_sla_ws_region;
 /* Token-reduction tiles of a [N][d] tensor X, per 64-token block: element
  * ((tt*4 + ct)*2 + t)*512 + l*8 + e holds X[32*tt + 16*t + 8*(e/4) + 4*g + e%4][32*ct + r]
- * (tt, t in 0..1, ct in 0..3, e in 0..7; tokens past N are 0). */
+ * (tt, t in 0..1, ct in 0..3, e in 0..7; tokens past N are 0). Head-dim-reduction tiles:
+ * element (tt*8 + s)*512 + l*8 + e holds X[32*tt + r][16*s + 8*g + e] (s in 0..7). The
+ * forward leaves K's head-dim-reduction tiles in SAGESLA_SLA_WS_KT and the backward
+ * rewrites the tile regions. */
 
 /* Bytes of the training workspace (linear = 0 when proj will be NULL). Host only. */
 sagesla_status sagesla_sla_workspace_size(int B, int H, int N, int d, int block, double topk,

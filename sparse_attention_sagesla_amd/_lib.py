@@ -26,7 +26,7 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
            "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd"]
-SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask", "phq", "du", "ol", "ds", "dwp"]
+SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask", "h0", "h1", "phq", "du", "ol", "ds", "dwp"]
 SLA_WS_COUNT = len(SLA_WS_REGIONS)
 
 _lib = None

@@ -409,6 +409,8 @@ void sla_layout(const Geom& gm, bool linear, size_t off[SAGESLA_SLA_WS_COUNT], s
   sz[SAGESLA_SLA_WS_DOT] = tiles;
   sz[SAGESLA_SLA_WS_DSUM] = BH * N * 4;
   sz[SAGESLA_SLA_WS_MASK] = BH * Nb * nw * 4;
+  sz[SAGESLA_SLA_WS_H0] = tiles;
+  sz[SAGESLA_SLA_WS_H1] = tiles;
   if (linear) {
     sz[SAGESLA_SLA_WS_PHQ] = BH * N * D * 2;
     sz[SAGESLA_SLA_WS_DU] = BH * N * D * 2;
@@ -531,13 +533,25 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
     return from_hip(e);
   if ((e = launch_sla_kept_mask(P(SAGESLA_WS_IDX), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_MASK), st)) != hipSuccess)
     return from_hip(e);
-  if ((e = launch_sla_bwd_dq(q, k, v, P(SAGESLA_SLA_WS_KT), dout, P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE),
+  // dQ: K and V in head-dim-reduction tiles (V's in the V tile region), K in token-reduction tiles
+  if ((e = launch_sla_relayout_hd(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H0), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_relayout_hd(v, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_VT), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_bwd_dq(q, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_VT), P(SAGESLA_SLA_WS_KT), dout,
+                             P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE),
                              P(SAGESLA_WS_IDX), gm.BH, gm.N, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_DSUM), dq, st)) !=
       hipSuccess)
     return from_hip(e);
-  if ((e = launch_sla_bwd_dkdv(q, k, v, P(SAGESLA_SLA_WS_QT), dout, P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE),
-                               P(SAGESLA_SLA_WS_DSUM), P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st)) !=
-      hipSuccess)
+  // dK, dV: Q and dO in head-dim-reduction tiles (Q's in H0, which K's no longer need) and
+  // token-reduction tiles
+  if ((e = launch_sla_relayout_hd(q, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H0), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_relayout_hd(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H1), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_sla_bwd_dkdv(k, v, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_H1), P(SAGESLA_SLA_WS_QT),
+                               P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE), P(SAGESLA_SLA_WS_DSUM),
+                               P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st)) != hipSuccess)
     return from_hip(e);
   if (proj == nullptr) return SAGESLA_OK;
   if (!linear) {  // every block kept: no linear part, dW = 0

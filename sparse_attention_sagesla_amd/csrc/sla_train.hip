@@ -261,20 +261,31 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ backward: dQ (and D)
-// One workgroup (2 waves) per (head, query block), lanes = query rows as in the forward.
-// D = rowsum(dO * O_s) first (stored for the dK/dV pass), then per kept key block and
-// 32-key tile: S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T.
-__global__ __launch_bounds__(128) void sla_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                         const uint16_t* __restrict__ v, const uint16_t* __restrict__ kt_,
+// One workgroup (4 waves) per (head, query block). Wave (kt, qh) takes query rows 32qh .. +31
+// (one per lane column) against key tile kt (keys 32kt .. +31) of every kept block; P comes
+// from the saved lse, so the two key tiles need no exchange until the end, where their dQ
+// partial sums are added through LDS. D = rowsum(dO * O_s) first (stored for the dK/dV
+// pass). The kept blocks' K and V (head-dim-reduction tiles) and K (token-reduction tiles)
+// arrive by DMA in a two-stage LDS ring, one block ahead. Per block and wave:
+// S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T.
+__global__ __launch_bounds__(256) void sla_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh,
+                                                         const uint16_t* __restrict__ vh, const uint16_t* __restrict__ kt_,
                                                          const uint16_t* __restrict__ dout, const float* __restrict__ os,
                                                          const float* __restrict__ lse, const int* __restrict__ idx,
                                                          int BH, int N, int Nb, int ksel, int per_xcd,
                                                          float* __restrict__ dsum, float* __restrict__ dq) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sA0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sC0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sC1[kTrTile];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, i = tile % Nb;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
-  const int qi = kBlk * i + 32 * w + r;
+  const int kt = w >> 1, qh = w & 1;
+  const int qi = kBlk * i + 32 * qh + r;
   const bool qvalid = qi < N;
   const size_t hoff = (size_t)bh * N * kD;
   const float c = kLog2e * 0.08838834764831845f;
@@ -295,45 +306,78 @@ __global__ __launch_bounds__(128) void sla_bwd_dq_kernel(const uint16_t* __restr
   }
   const float D = dpart + __shfl_xor(dpart, 32);
   const float L = qvalid ? lse[(size_t)bh * N + qi] : 0.f;
-  if (qvalid && g == 0) dsum[(size_t)bh * N + qi] = D;
+  if (qvalid && g == 0 && kt == 0) dsum[(size_t)bh * N + qi] = D;
 
   v16f acc[4];
 #pragma unroll
   for (int ct = 0; ct < 4; ct++) acc[ct] = (v16f){};
 
   const int* irow = idx + ((size_t)bh * Nb + i) * ksel;
-  for (int kk = 0; kk < ksel; kk++) {
-    const int j = irow[kk];
+  // each wave copies a quarter of each 16 KiB tile: 4 DMAs of 1 KiB
+  auto issue = [&](uint16_t* da, uint16_t* db, uint16_t* dc, int j) {
+    const size_t to = ((size_t)bh * Nb + j) * kTrTile + (w * 4 * 64 + l) * 8;
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {
+      __builtin_amdgcn_global_load_lds((const void*)(kh + to + cc * 512), (lds_ptr_t)(da + (w * 4 + cc) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vh + to + cc * 512), (lds_ptr_t)(db + (w * 4 + cc) * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(kt_ + to + cc * 512), (lds_ptr_t)(dc + (w * 4 + cc) * 512), 16, 0, 0);
+    }
+  };
+  auto compute = [&](const uint16_t* ca, const uint16_t* cb, const uint16_t* cc_, int j) {
     const int nj = block_len(j, N);
-    const uint16_t* kb = kt_ + ((size_t)bh * Nb + j) * kTrTile + l * 8;
+    v16f s_ = (v16f){}, dp = (v16f){};
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++) {
-      const int kr = 32 * kt + r;
-      const size_t roff = hoff + ((size_t)j * kBlk + kr) * kD + 8 * g;
-      v16f s_ = (v16f){}, dp = (v16f){};
+    for (int s = 0; s < 8; s++) {
+      const int off = ((kt * 8 + s) * 64 + l) * 8;
+      s_ = mfma(*(const v8bf*)(ca + off), qop[s], s_);
+      dp = mfma(*(const v8bf*)(cb + off), dop[s], dp);
+    }
+    float ds[16];
 #pragma unroll
-      for (int s = 0; s < 8; s++) {
-        const bool kv = kr < nj;
-        s_ = mfma(kv ? ld8(k + roff + 16 * s) : (v8bf){}, qop[s], s_);
-        dp = mfma(kv ? ld8(v + roff + 16 * s) : (v8bf){}, dop[s], dp);
-      }
-      float ds[16];
+    for (int x = 0; x < 16; x++) {
+      const int key = 32 * kt + 8 * (x >> 2) + 4 * g + (x & 3);
+      const float p = (key < nj && qvalid) ? exp2f(s_[x] * c - L) : 0.f;
+      ds[x] = p * (dp[x] - D);
+    }
 #pragma unroll
-      for (int x = 0; x < 16; x++) {
-        const int key = 32 * kt + 8 * (x >> 2) + 4 * g + (x & 3);
-        const float p = (key < nj && qvalid) ? exp2f(s_[x] * c - L) : 0.f;
-        ds[x] = p * (dp[x] - D);
-      }
+    for (int t = 0; t < 2; t++) {
+      const v8bf bq = pack8(&ds[8 * t]);
 #pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const v8bf b = pack8(&ds[8 * t]);
-#pragma unroll
-        for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(ld8(kb + ((kt * 4 + ct) * 2 + t) * 512), b, acc[ct]);
-      }
+      for (int ct = 0; ct < 4; ct++)
+        acc[ct] = mfma(*(const v8bf*)(cc_ + ((((kt * 4 + ct) * 2 + t) * 64) + l) * 8), bq, acc[ct]);
+    }
+  };
+
+  issue(sA0, sB0, sC0, irow[0]);
+  for (int kk = 0; kk < ksel; kk += 2) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (kk + 1 < ksel) issue(sA1, sB1, sC1, irow[kk + 1]);
+    compute(sA0, sB0, sC0, irow[kk]);
+    if (kk + 1 < ksel) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (kk + 2 < ksel) issue(sA0, sB0, sC0, irow[kk + 2]);
+      compute(sA1, sB1, sC1, irow[kk + 1]);
     }
   }
 
-  if (!qvalid) return;
+  // the key-tile-1 waves hand their partial sums to the key-tile-0 waves through LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* red = qh ? (float*)sB0 : (float*)sA0;  // 16 KiB per query half
+  if (kt == 1) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) red[(ct * 16 + v) * 64 + l] = acc[ct][v];
+  }
+  __syncthreads();
+  if (kt == 1 || !qvalid) return;
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+    for (int v = 0; v < 16; v++) acc[ct][v] += red[(ct * 16 + v) * 64 + l];
   const float sc = 0.08838834764831845f;  // 1 / sqrt(128)
   float* drow = dq + hoff + (size_t)qi * kD;
 #pragma unroll
@@ -347,23 +391,44 @@ __global__ __launch_bounds__(128) void sla_bwd_dq_kernel(const uint16_t* __restr
 }
 
 // ------------------------------------------------------------------ backward: dK, dV
-// One workgroup (2 waves) per (head, key block j); wave w owns keys 32w .. +31, one per
-// lane column. The query blocks that keep j come from the transposed mask, ascending. Per
-// 32-query tile: S = Q K^T, dP = dO V^T (lanes = keys, registers = queries), P and dS from
-// the saved lse and D, then dV^T += dO^T P and dK^T += Q^T dS on the token-reduction tiles
-// of dO and Q. The wave's K and V operands stay in registers.
-__global__ __launch_bounds__(128) void sla_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                           const uint16_t* __restrict__ v, const uint16_t* __restrict__ qt_,
-                                                           const uint16_t* __restrict__ dout,
-                                                           const uint16_t* __restrict__ dot_, const float* __restrict__ lse,
-                                                           const float* __restrict__ dsum, const uint32_t* __restrict__ mask,
-                                                           int BH, int N, int Nb, int nw, int per_xcd,
-                                                           float* __restrict__ dk, float* __restrict__ dv) {
+// One workgroup (8 waves, 2 per SIMD) per (head, key block j). Wave (role, kh, qt) takes keys
+// 32kh .. +31 (one per lane column) against query tile qt (rows 32qt .. +31) of every query
+// block that keeps j, ascending (from the transposed mask); role 0 accumulates dV, role 1 dK
+// (both form S; splitting them halves each wave's accumulators). The two query tiles'
+// partial sums are added through LDS at the end. Per query block, its Q and dO
+// (head-dim-reduction and token-reduction tiles), lse and D arrive by DMA in a two-stage LDS
+// ring, one block ahead. Per block: S = Q K^T (lanes = keys, registers = queries), P from
+// lse; role 0: dV^T += dO^T P; role 1: dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS.
+__device__ __forceinline__ int next_set(const uint32_t* row, int nw, int from) {
+  for (int wi = from >> 5; wi < nw; wi++) {
+    uint32_t b = row[wi];
+    if (wi == (from >> 5)) b &= 0xFFFFFFFFu << (from & 31);
+    if (b) return 32 * wi + __builtin_ctz(b);
+  }
+  return -1;
+}
+
+__global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                           const uint16_t* __restrict__ qh_, const uint16_t* __restrict__ doh,
+                                                           const uint16_t* __restrict__ qt_, const uint16_t* __restrict__ dot_,
+                                                           const float* __restrict__ lse, const float* __restrict__ dsum,
+                                                           const uint32_t* __restrict__ mask, int BH, int N, int Nb, int nw,
+                                                           int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
+  __shared__ __attribute__((aligned(1024))) uint16_t sQh0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sDh0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQt0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sDt0[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQh1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sDh1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sQt1[kTrTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t sDt1[kTrTile];
+  __shared__ __attribute__((aligned(256))) float sL0[kBlk], sS0[kBlk], sL1[kBlk], sS1[kBlk];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, j = tile % Nb;
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
-  const int kj = kBlk * j + 32 * w + r;
+  const int role = w >> 2, kh = (w >> 1) & 1, qt = w & 1;
+  const int kj = kBlk * j + 32 * kh + r;
   const bool kvalid = kj < N;
   const size_t hoff = (size_t)bh * N * kD;
   const float c = kLog2e * 0.08838834764831845f;
@@ -373,75 +438,125 @@ __global__ __launch_bounds__(128) void sla_bwd_dkdv_kernel(const uint16_t* __res
   for (int s = 0; s < 8; s++) {
     const size_t e = hoff + (size_t)kj * kD + 16 * s + 8 * g;
     kop[s] = kvalid ? ld8(k + e) : (v8bf){};
-    vop[s] = kvalid ? ld8(v + e) : (v8bf){};
+    vop[s] = (kvalid && role == 1) ? ld8(v + e) : (v8bf){};
   }
-  v16f dka[4], dva[4];
+  v16f acc[4];
 #pragma unroll
-  for (int ct = 0; ct < 4; ct++) dka[ct] = dva[ct] = (v16f){};
+  for (int ct = 0; ct < 4; ct++) acc[ct] = (v16f){};
 
   const uint32_t* mrow = mask + ((size_t)bh * Nb + j) * nw;
-  for (int wi = 0; wi < nw; wi++) {
-    uint32_t bits = mrow[wi];
-    while (bits) {
-      const int i = 32 * wi + __builtin_ctz(bits);
-      bits &= bits - 1;
-      const int ni = block_len(i, N);
-      const uint16_t* qb = qt_ + ((size_t)bh * Nb + i) * kTrTile + l * 8;
-      const uint16_t* db = dot_ + ((size_t)bh * Nb + i) * kTrTile + l * 8;
+  // per-lane byte offsets kept opaque, so that the DMAs use a scalar base + lane offset;
+  // each wave copies an eighth of each 16 KiB tile (2 DMAs of 1 KiB), wave 0 the block's
+  // lse and wave 1 its D (rows past N repeat the last row; never used)
+  int lo16 = (w * 2 * 64 + l) * 16, lo4 = l * 4;
+  auto issue = [&](uint16_t* a, uint16_t* b, uint16_t* c2, uint16_t* d, float* sl, float* ss, int i) {
+    asm volatile("" : "+v"(lo16), "+v"(lo4));
+    const size_t tb = ((size_t)bh * Nb + i) * kTrTile * 2;  // bytes
+    const char* s0 = (const char*)qh_ + tb;
+    const char* s1 = (const char*)doh + tb;
+    const char* s2 = (const char*)qt_ + tb;
+    const char* s3 = (const char*)dot_ + tb;
 #pragma unroll
-      for (int qt = 0; qt < 2; qt++) {
-        const int qr = 32 * qt + r;
-        const size_t roff = hoff + ((size_t)i * kBlk + qr) * kD + 8 * g;
-        v16f s_ = (v16f){}, dp = (v16f){};
+    for (int cc = 0; cc < 2; cc++) {
+      const int ld = (w * 2 + cc) * 512;
+      __builtin_amdgcn_global_load_lds((const void*)(s0 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(a + ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(s1 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(b + ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(s2 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(c2 + ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(s3 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(d + ld), 16, 0, 0);
+    }
+    const size_t r0 = (size_t)bh * N + (size_t)kBlk * i;
+    const int nrow = min(kBlk, N - kBlk * i);
+    const uint32_t off4 = (uint32_t)min(lo4, 4 * (nrow - 1));
+    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)((const char*)(lse + r0) + off4), (lds_ptr_t)sl, 4, 0, 0);
+    if (w == 1) __builtin_amdgcn_global_load_lds((const void*)((const char*)(dsum + r0) + off4), (lds_ptr_t)ss, 4, 0, 0);
+  };
+  auto compute = [&](const uint16_t* a, const uint16_t* b, const uint16_t* c2, const uint16_t* d, const float* sl,
+                     const float* ss, int i) {
+    const int ni = block_len(i, N);
+    v16f s_ = (v16f){}, dp = (v16f){};
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-          const bool qv = qr < ni;
-          s_ = mfma(qv ? ld8(q + roff + 16 * s) : (v8bf){}, kop[s], s_);
-          dp = mfma(qv ? ld8(dout + roff + 16 * s) : (v8bf){}, vop[s], dp);
-        }
-        // registers x hold query rows 32qt + 8(x/4) + 4g + x%4: four runs of four
-        const float* lrow = lse + (size_t)bh * N + (size_t)i * kBlk + 32 * qt + 4 * g;
-        const float* drow = dsum + (size_t)bh * N + (size_t)i * kBlk + 32 * qt + 4 * g;
-        float p[16], ds[16];
+    for (int s = 0; s < 8; s++) s_ = mfma(*(const v8bf*)(a + ((qt * 8 + s) * 64 + l) * 8), kop[s], s_);
+    if (role == 1) {
 #pragma unroll
-        for (int x4 = 0; x4 < 4; x4++) {
-          const int q0 = 32 * qt + 8 * x4 + 4 * g;  // within the block
+      for (int s = 0; s < 8; s++) dp = mfma(*(const v8bf*)(b + ((qt * 8 + s) * 64 + l) * 8), vop[s], dp);
+    }
+    // registers x hold query rows 32qt + 8(x/4) + 4g + x%4 of the block
+    float p[16];
 #pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int x = 4 * x4 + e;
-            const bool ok = q0 + e < ni;
-            const float Lq = ok ? lrow[8 * x4 + e] : 0.f;
-            const float Dq = ok ? drow[8 * x4 + e] : 0.f;
-            p[x] = ok ? exp2f(s_[x] * c - Lq) : 0.f;
-            ds[x] = p[x] * (dp[x] - Dq);
-          }
-        }
+    for (int x4 = 0; x4 < 4; x4++) {
+      const int q0 = 32 * qt + 8 * x4 + 4 * g;
+      const float4 L4 = *(const float4*)(sl + q0);
+      const float Lq[4] = {L4.x, L4.y, L4.z, L4.w};
+      float Dq[4] = {0.f, 0.f, 0.f, 0.f};
+      if (role == 1) {
+        const float4 D4 = *(const float4*)(ss + q0);
+        Dq[0] = D4.x;
+        Dq[1] = D4.y;
+        Dq[2] = D4.z;
+        Dq[3] = D4.w;
+      }
 #pragma unroll
-        for (int t = 0; t < 2; t++) {
-          const v8bf pb = pack8(&p[8 * t]), sb = pack8(&ds[8 * t]);
-#pragma unroll
-          for (int ct = 0; ct < 4; ct++) {
-            const int off = ((qt * 4 + ct) * 2 + t) * 512;
-            dva[ct] = mfma(ld8(db + off), pb, dva[ct]);
-            dka[ct] = mfma(ld8(qb + off), sb, dka[ct]);
-          }
-        }
+      for (int e = 0; e < 4; e++) {
+        const int x = 4 * x4 + e;
+        const float pe = (q0 + e < ni) ? exp2f(s_[x] * c - Lq[e]) : 0.f;
+        p[x] = role == 0 ? pe : pe * (dp[x] - Dq[e]);
       }
     }
+    const uint16_t* src = role == 0 ? d : c2;  // dO^T for dV, Q^T for dK
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const v8bf pb = pack8(&p[8 * t]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ct++)
+        acc[ct] = mfma(*(const v8bf*)(src + ((((qt * 4 + ct) * 2 + t) * 64) + l) * 8), pb, acc[ct]);
+    }
+  };
+
+  int icur = next_set(mrow, nw, 0);
+  if (icur >= 0) issue(sQh0, sDh0, sQt0, sDt0, sL0, sS0, icur);
+  while (icur >= 0) {
+    int inext = next_set(mrow, nw, icur + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (inext >= 0) issue(sQh1, sDh1, sQt1, sDt1, sL1, sS1, inext);
+    compute(sQh0, sDh0, sQt0, sDt0, sL0, sS0, icur);
+    icur = inext;
+    if (icur < 0) break;
+    inext = next_set(mrow, nw, icur + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (inext >= 0) issue(sQh0, sDh0, sQt0, sDt0, sL0, sS0, inext);
+    compute(sQh1, sDh1, sQt1, sDt1, sL1, sS1, icur);
+    icur = inext;
   }
 
-  if (!kvalid) return;
-  const float sc = 0.08838834764831845f;
-  float* krow = dk + hoff + (size_t)kj * kD;
-  float* vrow = dv + hoff + (size_t)kj * kD;
+  // the query-tile-1 waves hand their partial sums to the query-tile-0 waves through LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // 16 KiB per (role, key half)
+  float* red = (float*)(role == 0 ? (kh == 0 ? sQh0 : sDh0) : (kh == 0 ? sQt0 : sDt0));
+  if (qt == 1) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int x = 0; x < 16; x++) red[(ct * 16 + x) * 64 + l] = acc[ct][x];
+  }
+  __syncthreads();
+  if (qt == 1 || !kvalid) return;
+  const float sc = role == 1 ? 0.08838834764831845f : 1.f;  // dK carries the 1/sqrt(d) of the scores
+  float* row = (role == 1 ? dk : dv) + hoff + (size_t)kj * kD;
 #pragma unroll
   for (int ct = 0; ct < 4; ct++)
 #pragma unroll
     for (int v4 = 0; v4 < 4; v4++) {
       const int ch = 32 * ct + 8 * v4 + 4 * g;
-      *(float4*)(krow + ch) = make_float4(dka[ct][4 * v4] * sc, dka[ct][4 * v4 + 1] * sc, dka[ct][4 * v4 + 2] * sc,
-                                          dka[ct][4 * v4 + 3] * sc);
-      *(float4*)(vrow + ch) = make_float4(dva[ct][4 * v4], dva[ct][4 * v4 + 1], dva[ct][4 * v4 + 2], dva[ct][4 * v4 + 3]);
+      float a4[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int x = 4 * v4 + e;
+        a4[e] = (acc[ct][x] + red[(ct * 16 + x) * 64 + l]) * sc;
+      }
+      *(float4*)(row + ch) = make_float4(a4[0], a4[1], a4[2], a4[3]);
     }
 }
 
@@ -925,22 +1040,22 @@ hipError_t launch_sla_fwd(const void* q, const void* k, const void* vt, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_sla_bwd_dq(const void* q, const void* k, const void* v, const void* kt, const void* dout,
+hipError_t launch_sla_bwd_dq(const void* q, const void* kh, const void* vh, const void* kt, const void* dout,
                              const void* os, const void* lse, const void* idx, int BH, int N, int Nb, int ksel,
                              void* dsum, void* dq, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(sla_bwd_dq_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)kt, (const uint16_t*)dout, (const float*)os,
+  hipLaunchKernelGGL(sla_bwd_dq_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)kh,
+                     (const uint16_t*)vh, (const uint16_t*)kt, (const uint16_t*)dout, (const float*)os,
                      (const float*)lse, (const int*)idx, BH, N, Nb, ksel, per_xcd, (float*)dsum, (float*)dq);
   return hipGetLastError();
 }
 
-hipError_t launch_sla_bwd_dkdv(const void* q, const void* k, const void* v, const void* qt, const void* dout,
+hipError_t launch_sla_bwd_dkdv(const void* k, const void* v, const void* qh, const void* doh, const void* qt,
                                const void* dot, const void* lse, const void* dsum, const void* mask, int BH, int N,
                                int Nb, void* dk, void* dv, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8, nw = (Nb + 31) / 32;
-  hipLaunchKernelGGL(sla_bwd_dkdv_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)qt, (const uint16_t*)dout,
+  hipLaunchKernelGGL(sla_bwd_dkdv_kernel, dim3(per_xcd * 8), dim3(512), 0, st, (const uint16_t*)k,
+                     (const uint16_t*)v, (const uint16_t*)qh, (const uint16_t*)doh, (const uint16_t*)qt,
                      (const uint16_t*)dot, (const float*)lse, (const float*)dsum, (const uint32_t*)mask, BH, N, Nb, nw,
                      per_xcd, (float*)dk, (float*)dv);
   return hipGetLastError();
