@@ -39,6 +39,7 @@ def parse():
     ap.add_argument("--cpu-blocks", type=int, default=200, help="query blocks in the oracle sample")
     ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 linear-layer measurement")
     ap.add_argument("--no-sla-train", action="store_true", help="skip the SLA training-path measurement")
+    ap.add_argument("--no-topk-sweep", action="store_true", help="skip the top-k sweep")
     ap.add_argument("--w8a8-shape", default="75600,5120,5120", help="M,K,N of the W8A8 linear layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MiB (a kernel of known "
@@ -210,12 +211,61 @@ def main():
         res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks)
     if not args.no_w8a8:
         res["w8a8"] = w8a8_measure(args)
+    if not args.no_topk_sweep:
+        res["topk_sweep"] = topk_sweep(args, cfg, x)
     if not args.no_sla_train:
         res["sla_train"] = sla_train_measure(args, cfg, x)
     print(json.dumps(res), flush=True)
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+
+def topk_sweep(args, cfg, x, topks=(0.05, 0.1, 0.15, 0.2, 0.25), heads=(0, 1)):
+    """The SageSLA forward on the same inputs at several top-k fractions: ms per call and
+    executed TOP/s, and, as context for the sparsity/accuracy trade-off, the relative L2
+    distance of the output from dense softmax attention (fp32, on two heads)."""
+    import sparse_attention_sagesla_amd as S
+    q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
+    B, H, N, d = q.shape
+    # dense fp32 attention of the sampled heads, in query chunks
+    dense = []
+    for h in heads:
+        qf, kf, vf = (t[0, h].float() for t in (q, k, v))
+        kt = kf.t().contiguous()
+        o = torch.empty_like(qf)
+        for r0 in range(0, N, 4096):
+            s_ = (qf[r0:r0 + 4096] @ kt) * (1.0 / d ** 0.5)
+            o[r0:r0 + 4096] = torch.softmax(s_, dim=-1) @ vf
+        dense.append(o)
+        del s_, kt
+    torch.cuda.empty_cache()
+    out = torch.empty_like(q)
+    rows = []
+    for tk in topks:
+        ws = S.alloc_workspace(q, tk, proj is not None)
+        for _ in range(args.warmup):
+            S.fwd(q, k, v, proj, topk=tk, out=out, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            S.fwd(q, k, v, proj, topk=tk, out=out, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        idx = S.workspace_views(ws, B, H, N, topk=tk, linear=proj is not None)["idx"].long()
+        Nb = (N + 63) // 64
+        nlen = torch.full((Nb,), 64, dtype=torch.int64, device=q.device)
+        nlen[-1] = N - 64 * (Nb - 1)
+        ops = 4.0 * d * float((nlen[idx].sum(-1) * nlen[None, :]).sum().item())
+        err = [float((out[0, h].float() - dense[n]).norm() / dense[n].norm()) for n, h in enumerate(heads)]
+        rows.append({"topk": tk, "ksel": S.ksel(N, tk), "ms": round(ms, 4),
+                     "executed_tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                     "rel_l2_vs_dense": [round(e, 4) for e in err]})
+        del ws
+    return {"workload": "%s inputs, SageSLA forward at each top-k; dense fp32 attention of heads %s as the "
+                        "accuracy reference" % (cfg.name, list(heads)), "points": rows}
 
 
 def sla_train_measure(args, cfg, x):
