@@ -115,6 +115,27 @@ sagesla_status sagesla_fwd(const void *q, const void *k, const void *v, const vo
                            int B, int H, int N, int d, double topk, int block, void *out,
                            void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
 
+/* ---- producer-side fusion -------------------------------------------------------------
+ * The pages fuse the rewritten LayerNorm/RMSNorm kernels with their neighbours (news.qq.com
+ * explainer, "Fourth key"). sagesla_prepare takes the QKV projection output qkv bf16
+ * [B, N, 3, H, d] (token-major, as a linear layer writes it) and, in one pass over it,
+ * RMS-normalizes q and k over their model width D = H*d (per token:
+ * r = fp32(1/sqrt(mean(x^2) + eps)) with the mean in fp64; out = bf16(bf16(x r) g) with the
+ * learned weights gq, gk bf16 [D]), writes q, k, v bf16 [B, H, N, d], and fills the pool
+ * regions of a forward workspace (QBAR, KBART, KSUM, VAMAXB, Q8, SQ) from them.
+ * sagesla_fwd_prepared then runs the forward from the next stage on, on the same q, k, v,
+ * sizes and topk; its result equals sagesla_fwd's on those q, k, v. The workspace is sized
+ * by sagesla_workspace_size with the same topk and linear flag. */
+sagesla_status sagesla_prepare(const void *qkv, const void *gq, const void *gk, double eps, int B,
+                               int H, int N, int d, double topk, int block, int linear, void *q,
+                               void *k, void *v, void *workspace, size_t workspace_bytes,
+                               sagesla_stream_t stream);
+
+sagesla_status sagesla_fwd_prepared(const void *q, const void *k, const void *v, const void *proj,
+                                    int B, int H, int N, int d, double topk, int block, void *out,
+                                    void *workspace, size_t workspace_bytes,
+                                    sagesla_stream_t stream);
+
 /* ---- stages ("friends"): the same conventions; buffers as in the workspace table ---- */
 
 /* Block pooling of Q and K (fp64 sums of the bf16 inputs), K block sums, V block max,

@@ -5,7 +5,8 @@ kernels (``csrc/``, interface in ``include/sagesla.h``); this package only marsh
 tensors into it. The library is loaded on first use; there is no CPU fallback.
 """
 from . import synth  # noqa: F401  (seeded synthetic inputs)
-from ._lib import (GROUP, SageSLAError, alloc_workspace, fwd, ksel, lib, sla_bwd, sla_fwd,  # noqa: F401
+from ._lib import (GROUP, SageSLAError, alloc_workspace, fwd, fwd_prepared, ksel, lib, prepare,  # noqa: F401
+                   sla_bwd, sla_fwd,
                    sla_workspace_layout, sla_workspace_size, sla_workspace_views, status_string,
                    w8a8_gemm, w8a8_linear, w8a8_quant_act, w8a8_quant_weight, w8a8_sizes, workspace_layout,
                    workspace_size, workspace_views)
@@ -13,4 +14,4 @@ from ._lib import (GROUP, SageSLAError, alloc_workspace, fwd, ksel, lib, sla_bwd
 __all__ = ["fwd", "ksel", "workspace_size", "workspace_layout", "workspace_views", "alloc_workspace",
            "SageSLAError", "status_string", "lib", "synth", "w8a8_sizes", "w8a8_quant_weight", "w8a8_quant_act",
            "w8a8_gemm", "w8a8_linear", "sla_fwd", "sla_bwd", "sla_workspace_size", "sla_workspace_layout",
-           "sla_workspace_views"]
+           "sla_workspace_views", "prepare", "fwd_prepared"]

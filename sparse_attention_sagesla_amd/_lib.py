@@ -25,7 +25,8 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_workspace_layout", "sagesla_fwd", "sagesla_pool", "sagesla_head_stats", "sagesla_select",
            "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
-           "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd"]
+           "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd",
+           "sagesla_prepare", "sagesla_fwd_prepared"]
 SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask", "h0", "h1", "phq", "du", "ol", "ds", "dwp"]
 SLA_WS_COUNT = len(SLA_WS_REGIONS)
 
@@ -69,6 +70,8 @@ def lib():
             "sagesla_sla_workspace_layout": (i32, dims + [i32, f64, i32, C.POINTER(sz * SLA_WS_COUNT)]),
             "sagesla_sla_fwd": (i32, [P, P, P, P] + dims + [f64, i32, P, P, sz, P]),
             "sagesla_sla_bwd": (i32, [P] * 5 + dims + [f64, i32] + [P] * 5 + [sz, P]),
+            "sagesla_prepare": (i32, [P, P, P, f64] + dims + [f64, i32, i32, P, P, P, P, sz, P]),
+            "sagesla_fwd_prepared": (i32, [P, P, P, P] + dims + [f64, i32, P, P, sz, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -297,5 +300,37 @@ def sla_workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> 
         nbytes = torch.Size(shape).numel() * torch.empty((), dtype=dt).element_size()
         if off + nbytes <= ws.numel():
             out[name] = ws[off:off + nbytes].view(dt).view(shape)
+    return out
+
+
+# ---------------------------------------------------------------- producer-side fusion
+
+def prepare(qkv, gq, gk, H, eps=1e-6, topk=0.1, linear=True, block=64, q=None, k=None, v=None, workspace=None,
+            stream=None):
+    """RMSNorm of q and k + attention layout + the pool stage, from the QKV projection
+    output qkv bf16 [B, N, 3*H*d]. Returns (q, k, v, workspace) for fwd_prepared."""
+    B, N, C = qkv.shape
+    d = C // (3 * H)
+    shape = (B, H, N, d)
+    q = torch.empty(shape, dtype=torch.bfloat16, device=qkv.device) if q is None else q
+    k = torch.empty(shape, dtype=torch.bfloat16, device=qkv.device) if k is None else k
+    v = torch.empty(shape, dtype=torch.bfloat16, device=qkv.device) if v is None else v
+    if workspace is None:
+        workspace = torch.empty(workspace_size(B, H, N, d, block, topk, linear), dtype=torch.uint8,
+                                device=qkv.device)
+    _check(lib().sagesla_prepare(_ptr(qkv), _ptr(gq), _ptr(gk), float(eps), B, H, N, d, float(topk), block,
+                                 int(bool(linear)), _ptr(q), _ptr(k), _ptr(v), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "sagesla_prepare")
+    return q, k, v, workspace
+
+
+def fwd_prepared(q, k, v, workspace, proj=None, topk=0.1, block=64, out=None, stream=None):
+    """The forward from the stage after pooling, on the workspace prepare() filled."""
+    B, H, N, d = _shape(q)
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().sagesla_fwd_prepared(_ptr(q), _ptr(k), _ptr(v), _ptr(proj), B, H, N, d, float(topk), block,
+                                      _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "sagesla_fwd_prepared")
     return out
 

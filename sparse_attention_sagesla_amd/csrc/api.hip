@@ -40,6 +40,8 @@ hipError_t launch_sla_lin_bwd_k(const void*, const void*, const void*, int, int,
 hipError_t launch_sla_dw(const void*, const void*, int, void*, void*, hipStream_t);
 int sla_dw_parts();
 hipError_t launch_sla_zero(void*, size_t, hipStream_t);
+hipError_t launch_prepare(const void*, const void*, const void*, double, int, int, int, int, void*, void*, void*,
+                          void*, void*, void*, void*, void*, void*, void*, hipStream_t);
 int w8a8_row_tiles(int M);
 hipError_t launch_w8a8_quant_act(const void*, int, int, void*, void*, hipStream_t);
 hipError_t launch_w8a8_quant_weight(const void*, int, int, void*, void*, hipStream_t);
@@ -207,9 +209,48 @@ sagesla_status sagesla_workspace_size(int B, int H, int N, int d, int block, dou
   return SAGESLA_OK;
 }
 
+static sagesla_status run_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
+                              int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
+                              sagesla_stream_t stream, bool pooled);
+
 sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
                            int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
                            sagesla_stream_t stream) {
+  return run_fwd(q, k, v, proj, B, H, N, d, topk, block, out, workspace, workspace_bytes, stream, false);
+}
+
+sagesla_status sagesla_fwd_prepared(const void* q, const void* k, const void* v, const void* proj, int B, int H,
+                                    int N, int d, double topk, int block, void* out, void* workspace,
+                                    size_t workspace_bytes, sagesla_stream_t stream) {
+  return run_fwd(q, k, v, proj, B, H, N, d, topk, block, out, workspace, workspace_bytes, stream, true);
+}
+
+sagesla_status sagesla_prepare(const void* qkv, const void* gq, const void* gk, double eps, int B, int H, int N,
+                               int d, double topk, int block, int linear, void* q, void* k, void* v, void* workspace,
+                               size_t workspace_bytes, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if (!(eps >= 0.0 && eps < 1e30)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  if ((s = check_ptrs({qkv, gq, gk, q, k, v, workspace})) != SAGESLA_OK) return s;
+  size_t off[SAGESLA_WS_COUNT], total;
+  layout(gm, linear != 0 && gm.ksel < gm.Nb, off, &total);
+  if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  char* ws = (char*)workspace;
+  auto P = [&](int r) { return (void*)(ws + off[r]); };
+  // the per-token scales live in the K8 region until the forward's K quantization overwrites it
+  return from_hip(launch_prepare(qkv, gq, gk, eps, B, H, N, gm.Nb, P(SAGESLA_WS_K8), q, k, v, P(SAGESLA_WS_QBAR),
+                                 P(SAGESLA_WS_KBART), P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8),
+                                 P(SAGESLA_WS_SQ), (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+static sagesla_status run_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
+                              int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
+                              sagesla_stream_t stream, bool pooled) {
   Geom gm;
   sagesla_status s = check_sizes(B, H, N, d, block, &gm);
   if (s != SAGESLA_OK) return s;
@@ -226,9 +267,9 @@ sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const vo
   char* ws = (char*)workspace;
   auto P = [&](int r) { return (void*)(ws + off[r]); };
   hipError_t e;
-  if ((e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART),
-                       P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), st)) !=
-      hipSuccess)
+  if (!pooled && (e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART),
+                                  P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ),
+                                  st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb,
                              P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
@@ -254,6 +295,8 @@ sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const vo
                          linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH, gm.N, gm.Nb, gm.ksel, out, st);
   return from_hip(e);
 }
+
+extern "C" {
 
 sagesla_status sagesla_pool(const void* q, const void* k, const void* v, int B, int H, int N, int d, int block,
                             void* qbar, void* kbart, void* ksum, void* vamax_blk, void* q8, void* sq,

@@ -9,11 +9,40 @@
 
 namespace sagesla {
 
+// Where the pool pass reads its rows from. Plain: q, k, v as [B, H, N, d]. From the
+// projection (the producer-side fusion): the QKV projection output [B, N, 3, H, d]; q and k
+// are RMS-normalized on the way in (scale r per token from rms_scale_kernel, then the
+// learned weight, each product rounded to bf16), and all three are written out as
+// [B, H, N, d] for the rest of the attention.
+struct ProjSrc {
+  const uint16_t* qkv;  // [B][N][3][H][d]
+  const float* rs;      // [2][B][N]: r of q, then of k
+  const uint16_t* gq;   // [H*d]
+  const uint16_t* gk;   // [H*d]
+  uint16_t *q, *k, *v;  // [B][H][N][d] outputs
+  int H;
+};
+
+// bf16(bf16(x * r) * g) for 8 channels
+__device__ __forceinline__ uint4 rms_apply(uint4 x, float r, uint4 g) {
+  const uint16_t* xh = (const uint16_t*)&x;
+  const uint16_t* gh = (const uint16_t*)&g;
+  uint4 o;
+  uint16_t* oh = (uint16_t*)&o;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const uint16_t nb = f32_to_bf16(bf16_to_f32(xh[e]) * r);
+    oh[e] = f32_to_bf16(bf16_to_f32(nb) * bf16_to_f32(gh[e]));
+  }
+  return o;
+}
+
 // One workgroup (256 threads) per (bh, block). Thread t covers rows t/16 + 16m
 // (m = 0..3) and channels 8*(t%16) .. +7.
+template <bool kFromProj>
 __global__ __launch_bounds__(256) void pool_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    int N, int Nb, double* __restrict__ qbar, double* __restrict__ kbart, double* __restrict__ ksum,
+    ProjSrc ps, int N, int Nb, double* __restrict__ qbar, double* __restrict__ kbart, double* __restrict__ ksum,
     float* __restrict__ vamax_blk, int8_t* __restrict__ q8, float* __restrict__ sq) {
   __shared__ double s_q[16][kD];
   __shared__ double s_k[16][kD];
@@ -38,9 +67,21 @@ __global__ __launch_bounds__(256) void pool_kernel(
     uint4 qa = {0, 0, 0, 0}, ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
     if (row < n) {
       size_t off = base + (size_t)row * kD + ch * 8;
-      qa = *(const uint4*)(q + off);
-      ka = *(const uint4*)(k + off);
-      va = *(const uint4*)(v + off);
+      if (kFromProj) {
+        const int b = bh / ps.H, h = bh % ps.H, tok = i * kBlk + row, D = ps.H * kD;
+        const uint16_t* src = ps.qkv + ((size_t)b * N + tok) * 3 * D + h * kD + ch * 8;
+        const size_t rr = (size_t)b * N + tok, BN = (size_t)(gridDim.x / Nb / ps.H) * N;
+        qa = rms_apply(*(const uint4*)src, ps.rs[rr], *(const uint4*)(ps.gq + h * kD + ch * 8));
+        ka = rms_apply(*(const uint4*)(src + D), ps.rs[BN + rr], *(const uint4*)(ps.gk + h * kD + ch * 8));
+        va = *(const uint4*)(src + 2 * D);
+        *(uint4*)(ps.q + off) = qa;
+        *(uint4*)(ps.k + off) = ka;
+        *(uint4*)(ps.v + off) = va;
+      } else {
+        qa = *(const uint4*)(q + off);
+        ka = *(const uint4*)(k + off);
+        va = *(const uint4*)(v + off);
+      }
     }
     const uint16_t* qh = (const uint16_t*)&qa;
     const uint16_t* kh = (const uint16_t*)&ka;
@@ -134,9 +175,48 @@ __global__ __launch_bounds__(256) void head_stats_kernel(const double* __restric
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int BH, int N, int Nb, void* qbar,
                        void* kbart, void* ksum, void* vamax_blk, void* q8, void* sq, hipStream_t st) {
-  hipLaunchKernelGGL(pool_kernel, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)k, (const uint16_t*)v, N, Nb, (double*)qbar, (double*)kbart,
+  hipLaunchKernelGGL(pool_kernel<false>, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)k, (const uint16_t*)v, ProjSrc{}, N, Nb, (double*)qbar, (double*)kbart,
                      (double*)ksum, (float*)vamax_blk, (int8_t*)q8, (float*)sq);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- producer-side fusion
+// Per token: r = fp32(1 / sqrt(mean(x^2) + eps)) of its q row and of its k row (D = H*d
+// channels each), the squares and their sum in fp64 (exact for bf16 inputs of ordinary
+// range, so the sum does not depend on its order), one wave per (q or k, token).
+__global__ __launch_bounds__(256) void rms_scale_kernel(const uint16_t* __restrict__ qkv, int BN, int D, double eps,
+                                                        float* __restrict__ rs) {
+  const int wv = blockIdx.x * 4 + (threadIdx.x >> 6), l = threadIdx.x & 63;
+  if (wv >= 2 * BN) return;
+  const int part = wv / BN, row = wv % BN;  // part 0: q, 1: k
+  const uint16_t* src = qkv + (size_t)row * 3 * D + (size_t)part * D;
+  double ss = 0.0;
+  for (int c = l * 8; c < D; c += 512) {
+    const uint4 x = *(const uint4*)(src + c);
+    const uint16_t* xh = (const uint16_t*)&x;
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      const double f = (double)bf16_to_f32(xh[e]);
+      ss += f * f;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+  if (l == 0) rs[(size_t)part * BN + row] = (float)(1.0 / sqrt(ss / (double)D + eps));
+}
+
+hipError_t launch_prepare(const void* qkv, const void* gq, const void* gk, double eps, int B, int H, int N, int Nb,
+                          void* rs, void* q, void* k, void* v, void* qbar, void* kbart, void* ksum, void* vamax_blk,
+                          void* q8, void* sq, hipStream_t st) {
+  const int BN = B * N, D = H * kD;
+  hipLaunchKernelGGL(rms_scale_kernel, dim3((2 * BN + 3) / 4), dim3(256), 0, st, (const uint16_t*)qkv, BN, D, eps,
+                     (float*)rs);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  ProjSrc ps{(const uint16_t*)qkv, (const float*)rs, (const uint16_t*)gq, (const uint16_t*)gk,
+             (uint16_t*)q,       (uint16_t*)k,      (uint16_t*)v,        H};
+  hipLaunchKernelGGL(pool_kernel<true>, dim3(B * H * Nb), dim3(256), 0, st, nullptr, nullptr, nullptr, ps, N, Nb,
+                     (double*)qbar, (double*)kbart, (double*)ksum, (float*)vamax_blk, (int8_t*)q8, (float*)sq);
   return hipGetLastError();
 }
 

@@ -219,3 +219,20 @@ def make_linear_inputs(M: int, K: int, N: int, seed: int, device="cpu", bias: bo
     if bias:
         b = (0.02 * torch.randn((N,), generator=gen, device=device, dtype=torch.float32)).to(torch.bfloat16)
     return {"x": x, "w": w, "bias": b}
+
+
+def make_projection_inputs(B: int, N: int, H: int, d: int, seed: int, device="cpu"):
+    """A QKV projection output and RMSNorm weights: dict(qkv bf16 [B, N, 3*H*d], gq, gk bf16
+    [H*d]). qkv ~ N(0, 1) times a per-token magnitude exp(N(0, 1/4)) per part, plus a
+    per-channel offset N(0, 1/4) on the k part (the channel bias that K smoothing removes);
+    gq, gk ~ 1 + N(0, 0.1^2)."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    D = H * d
+    x = torch.randn((B, N, 3, D), generator=gen, device=device, dtype=torch.float32)
+    x *= torch.exp(0.5 * torch.randn((B, N, 3, 1), generator=gen, device=device, dtype=torch.float32))
+    x[:, :, 1, :] += 0.5 * torch.randn((D,), generator=gen, device=device, dtype=torch.float32)
+    g = 1.0 + 0.1 * torch.randn((2, D), generator=gen, device=device, dtype=torch.float32)
+    return {"qkv": x.reshape(B, N, 3 * D).to(torch.bfloat16), "gq": g[0].to(torch.bfloat16),
+            "gk": g[1].to(torch.bfloat16)}
