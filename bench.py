@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--no-w8a8", action="store_true", help="skip the W8A8 linear-layer measurement")
     ap.add_argument("--no-sla-train", action="store_true", help="skip the SLA training-path measurement")
     ap.add_argument("--no-topk-sweep", action="store_true", help="skip the top-k sweep")
+    ap.add_argument("--no-prepare", action="store_true", help="skip the producer-side fusion measurement")
     ap.add_argument("--w8a8-shape", default="75600,5120,5120", help="M,K,N of the W8A8 linear layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MiB (a kernel of known "
@@ -213,12 +214,80 @@ def main():
         res["w8a8"] = w8a8_measure(args)
     if not args.no_topk_sweep:
         res["topk_sweep"] = topk_sweep(args, cfg, x)
+    if not args.no_prepare:
+        res["prepare"] = prepare_measure(args, cfg)
     if not args.no_sla_train:
         res["sla_train"] = sla_train_measure(args, cfg, x)
     print(json.dumps(res), flush=True)
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+
+def prepare_measure(args, cfg, eps=1e-6):
+    """The producer-side fusion at the headline shape: from a QKV projection output, RMSNorm
+    of q and k + attention layout + pool stage in one pass (sagesla_prepare), against the
+    unfused chain (torch's rms_norm, the layout copies, then the pool stage), each timed with
+    HIP events; and the whole forward both ways."""
+    import sparse_attention_sagesla_amd as S
+    from sparse_attention_sagesla_amd import synth
+    B, H, N, d, topk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.topk
+    D = H * d
+    dev = torch.device("cuda:0")
+    inp = synth.make_projection_inputs(B, N, H, d, seed=cfg.seed + 5, device=dev)
+    qkv, gq, gk = inp["qkv"], inp["gq"], inp["gk"]
+    proj = (torch.randn((d, d), generator=torch.Generator(device=dev).manual_seed(9), device=dev) / d ** 0.5).to(
+        torch.bfloat16)
+    ws = S.alloc_workspace(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev), topk, True)
+    q = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    k, v, out = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lay = S.workspace_layout(B, H, N, topk=topk, linear=True)
+    P = {n: ws.data_ptr() + o for n, o in lay.items()}
+    L = S.lib()
+    stream = torch.cuda.current_stream()
+
+    def fused():
+        S.prepare(qkv, gq, gk, H, eps=eps, topk=topk, q=q, k=k, v=v, workspace=ws)
+
+    def unfused():
+        x = qkv.view(B, N, 3, D)
+        qn = torch.nn.functional.rms_norm(x[:, :, 0], (D,), gq, eps)
+        kn = torch.nn.functional.rms_norm(x[:, :, 1], (D,), gk, eps)
+        q.copy_(qn.view(B, N, H, d).permute(0, 2, 1, 3))
+        k.copy_(kn.view(B, N, H, d).permute(0, 2, 1, 3))
+        v.copy_(x[:, :, 2].view(B, N, H, d).permute(0, 2, 1, 3))
+        st = L.sagesla_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, 64, P["qbar"], P["kbart"],
+                            P["ksum"], P["vamax_blk"], P["q8"], P["sq"], stream.cuda_stream)
+        assert st == 0
+
+    def timeit(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_f, ms_u = timeit(fused), timeit(unfused)
+    ms_ff = timeit(lambda: (fused(), S.fwd_prepared(q, k, v, ws, proj=proj, topk=topk, out=out)))
+    ms_uf = timeit(lambda: (unfused(), S.fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)))
+    nbytes = 8.0 * B * N * D * 2  # q, k read for the scales; q, k, v read and written once
+    gbs = nbytes / (ms_f * 1e-3) / 1e9
+    return {
+        "workload": "QKV projection output [B=%d, N=%d, 3x%d] -> RMSNorm(q, k) + [B, H, N, d] layout + pool "
+                    "stage (H=%d, d=%d)" % (B, N, D, H, d),
+        "ms_fused": round(ms_f, 4),
+        "ms_unfused_torch_norm_layout_then_pool": round(ms_u, 4),
+        "ms_forward_from_projection_fused": round(ms_ff, 4),
+        "ms_forward_from_projection_unfused": round(ms_uf, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "rms_scale_kernel + pool_kernel<proj>",
+                     "bytes_per_call": nbytes},
+    }
 
 
 def topk_sweep(args, cfg, x, topks=(0.05, 0.1, 0.15, 0.2, 0.25), heads=(0, 1)):
