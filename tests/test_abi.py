@@ -141,3 +141,43 @@ def test_w8a8_sizes():
     assert sz == {"x8": 512 * 384, "sx": 3 * 512 * 4, "w8": 512 * 384, "sw": 4 * 3 * 4}
     sz = S.w8a8_sizes(75600, 5120, 5120)
     assert sz["x8"] == 75776 * 5120 and sz["sx"] == 40 * 75776 * 4
+
+
+def test_sla_workspace_regions():
+    lay = S.sla_workspace_layout(1, 4, 1000, topk=0.2, linear=True)
+    total = S.sla_workspace_size(1, 4, 1000, topk=0.2, linear=True)
+    offs = sorted(lay.values())
+    assert all(o % 256 == 0 for o in offs)
+    assert len(set(offs)) == len(offs) and max(offs) < total
+    # the training workspace holds the forward's regions at the same offsets
+    fwd = S.workspace_layout(1, 4, 1000, topk=0.2, linear=True)
+    assert all(lay[n] == fwd[n] for n in fwd)
+    assert S.sla_workspace_size(1, 4, 1000, topk=0.2, linear=False) < total
+
+
+def test_sla_bwd_rejects_on_host():
+    L = S.lib()
+    p = C.c_void_p(1 << 20)  # never dereferenced: the checks fail first
+    # proj given without dproj (and the reverse)
+    st = L.sagesla_sla_bwd(p, p, p, p, p, 1, 2, 256, 128, 0.2, 64, p, p, p, None, p, 1 << 30, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT
+    st = L.sagesla_sla_bwd(p, p, p, None, p, 1, 2, 256, 128, 0.2, 64, p, p, p, p, p, 1 << 30, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT
+    # unsupported head dimension; workspace too small
+    st = L.sagesla_sla_bwd(p, p, p, None, p, 1, 2, 256, 64, 0.2, 64, p, p, p, None, p, 1 << 30, None)
+    assert st == _lib.ERR_UNSUPPORTED
+    st = L.sagesla_sla_fwd(p, p, p, None, 1, 2, 256, 128, 0.2, 64, p, p, 1024, None)
+    assert st == _lib.ERR_WORKSPACE
+
+
+def test_prepare_rejects_on_host():
+    L = S.lib()
+    p = C.c_void_p(1 << 20)
+    for eps in (-1.0, float("nan"), float("inf")):
+        st = L.sagesla_prepare(p, p, p, eps, 1, 2, 256, 128, 0.1, 64, 1, p, p, p, p, 1 << 30, None)
+        assert st == _lib.ERR_INVALID_ARGUMENT
+    st = L.sagesla_prepare(p, p, p, 1e-6, 1, 2, 256, 128, 0.1, 64, 1, p, p, p, p, 16, None)
+    assert st == _lib.ERR_WORKSPACE
+    unaligned = C.c_void_p((1 << 20) + 2)
+    st = L.sagesla_prepare(unaligned, p, p, 1e-6, 1, 2, 256, 128, 0.1, 64, 1, p, p, p, p, 1 << 30, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT
