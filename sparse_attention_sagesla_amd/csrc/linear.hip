@@ -135,11 +135,10 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
 
 // ---------------------------------------------------------------- masked sum on MFMA
 
-constexpr int kBp = 72;     // LDS row pitch (bf16) of a [state][64 columns] operand tile: 144 B
-constexpr int kMgSlots = 4;  // steps of 32 union entries in flight (registers, then LDS)
-constexpr int kUlChunk = 1024;  // union-list entries per LDS chunk
+constexpr int kMgSlots = 4;  // ring depth: steps of 32 union entries in flight
 typedef short v4s_ __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // gfx950 transposing LDS read: within each group of 16 lanes, lanes 4a..4a+3 each name
 // 4 consecutive 16-bit elements of row a of a 4 x 16 tile, and lane j receives column j.
@@ -147,148 +146,207 @@ __device__ __forceinline__ v4s_ lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(p));
 }
 
-// Per (bh, group, state row c in 0..128, column half h): for the group's kGroup query
-// blocks i and columns a in 64 h .. 64 h + 63,
+// One ring slot: the step's 32 state rows x 128 columns (bf16, 256-byte rows of 16-byte
+// chunks placed by mg_pos), the step's membership word of each of the group's query
+// blocks (permuted, see issue), and the union entries of a later step (per wave: its 8
+// rows in lanes 0..7 of a 64-word row). Each slot is its own LDS object, so that the
+// compiler waits for a slot's own copies only.
+struct MgSlot {
+  uint16_t st[32 * 128];
+  uint32_t mk[kGroup];
+  int32_t ul[4 * 64];
+};
+
+// The 8 transposing reads of four column tiles (rows r and r + 4 of each; a0..a3 are LDS
+// byte addresses), waited for in the same block. Written out so that the compiler, which
+// cannot tell which ring slot's DMAs a read depends on, adds no wait of its own: the slot
+// is complete by the explicit wait and barrier of the step.
+typedef int v2i_ __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void mg_tr_reads(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, v2i_ (&x)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Chunk cc (0..15) of state row r sits at chunk position mg_pos(r, cc) of its 256-byte
+// row (an involution). With it the two transposing reads of a half-wave (rows 8 kg + a,
+// kg in {0, 1}, a in 0..3, four 8-byte column pieces each) cover all 64 banks once.
+__device__ __forceinline__ int mg_pos(int r, int cc) { return cc ^ (2 * ((r & 3) | (((r >> 3) & 1) << 2))); }
+
+// Per (bh, group, state row c in 0..128): for the group's kGroup query blocks i and the
+// 128 columns a,
 //   hc[i][c][a] = htot[c][a] - sum_u C[i][u] S_{union[u]}[c][a]
-// as a [kGroup x U] x [U x 64] product on v_mfma_f32_16x16x32_bf16 (the 0/1 mask is
-// exact in bf16, the states are bf16, the sums fp32). Wave w owns query blocks
-// 64w .. 64w+63 (4 M-tiles) and the 4 column tiles. Union entries stream in steps of
-// 32, fetched kMgSlots steps ahead.
-__global__ __launch_bounds__(256, 3) void linear_mask_gemm_kernel(
+// (or the sum alone when the union lists the blocks NOT kept), taken transposed,
+// M^T = S^T C^T, as [128 x U] x [U x kGroup] products on v_mfma_f32_16x16x32_bf16: the
+// 0/1 mask is exact in bf16, the states are bf16, the sums fp32. Wave w owns query
+// blocks 64w .. 64w+63 (4 column tiles) and the 8 row tiles of state columns; each lane
+// ends with 4 consecutive columns of one query block per tile, stored as 8 bytes.
+// Union entries stream in steps of 32 through a ring of kMgSlots LDS slots filled by
+// global_load_lds DMA; the union entries that address a step's rows arrive kMgSlots
+// steps before them. Tiles are ordered (bh, state row, group) and dealt to the XCDs in
+// contiguous ranges (workgroup b runs on XCD b % 8), so the groups that read the same
+// 256-byte row slice of the states run together on one XCD and share its L2.
+__global__ __launch_bounds__(256, 2) void linear_mask_gemm_kernel(
     const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
     const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
-    int complement, uint16_t* __restrict__ hc) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[kMgSlots][32 * kBp];
-  __shared__ uint32_t s_m[kMgSlots][kGroup];  // per step: the 32 union entries' bits of each query block
-  __shared__ v8s s_lut[256];                  // byte -> its 8 bits as bf16 0.0 / 1.0
-  __shared__ __attribute__((aligned(16))) uint16_t s_out[kGroup / 2 * 64];
-  __shared__ int32_t s_ul[2][kUlChunk];  // union list, two chunks of kUlChunk entries
+    int complement, int ntiles, int per_xcd, uint16_t* __restrict__ hc) {
+  __shared__ __attribute__((aligned(16))) MgSlot s0, s1, s2, s3;
+  __shared__ __attribute__((aligned(8))) uint2 s_nib[16];  // nibble -> its 4 bits as bf16 0.0 / 1.0
 
-  const int per_bh = ngroups * 129 * 2;
-  const int bh = blockIdx.x / per_bh, rem = blockIdx.x % per_bh;
-  const int grp = rem / 258, c = (rem % 258) >> 1, half = rem & 1;
+  const int tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (tile >= ntiles) return;
+  const int per_bh = ngroups * 129;
+  const int bh = tile / per_bh, rem = tile % per_bh;
+  const int grp = rem % ngroups, c = rem / ngroups;
   const size_t gbase = (size_t)bh * ngroups + grp;
   const int U = ucount[gbase];
   const int32_t* ul = ulist + gbase * Nb;
   const int nw = (Nb + 31) / 32;
   const uint32_t* um = umask + gbase * kGroup * nw;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, kg = lane >> 4;
+  const int t = threadIdx.x, lane = t & 63, l16 = lane & 15, kg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
 
-  v4f_ acc[4][4];
+  if (t < 16) {
+    uint2 e;
+    e.x = ((t & 1) ? 0x3F80u : 0u) | ((t & 2) ? 0x3F800000u : 0u);  // bf16 1.0
+    e.y = ((t & 4) ? 0x3F80u : 0u) | ((t & 8) ? 0x3F800000u : 0u);
+    s_nib[t] = e;
+  }
+
+  v4f_ acc[4][8];
 #pragma unroll
   for (int m = 0; m < 4; m++)
 #pragma unroll
-    for (int n = 0; n < 4; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
+    for (int n = 0; n < 8; n++) acc[m][n] = (v4f_){0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (U + 31) / 32;
-  // The union list goes through LDS in chunks of kUlChunk entries, each staged one step
-  // before the first state load that needs it, so that no state load waits on a
-  // dependent global load of its index.
-  auto fill_ul = [&](int chunk) {
-    for (int e = t; e < kUlChunk; e += 256) {
-      const int u = chunk * kUlChunk + e;
-      s_ul[chunk & 1][e] = u < U ? ul[u] : 0;
-    }
+  // this lane's DMA rows: state rows 8w + 4k + lane/16 (k = 0, 1) of a step, chunk
+  // position lane % 16
+  const int dr0 = 8 * w + (lane >> 4), dr1 = dr0 + 4;
+  const uint16_t* hs_row = hs + (size_t)bh * Nb * kStateElems + (size_t)c * kD;
+  const uint32_t src0 = 8 * mg_pos(dr0, lane & 15), src1 = 8 * mg_pos(dr1, lane & 15);
+  // Every DMA is issued, with step indices clamped to the last step, so that each wave
+  // issues four per step (two of state rows, membership words, later union entries)
+  // and the wait counts below are exact.
+  auto issue_ul = [&](MgSlot& d, int step) {
+    const int sb = min(step, nsteps - 1);
+    const int u = min(32 * sb + 8 * w + (lane & 7), U - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(ul + u), (lds_void_ptr)(d.ul + 64 * w), 4, 0, 0);
   };
-  // 32 states x 64 columns per step: thread t holds 16 B (8 columns) of state t/8, and
-  // the step's mask word of query block t; stored row-major ([state][column]) into LDS
-  // the step before use. The MFMA B operand (8 consecutive states of one column) comes
-  // from transposing reads.
-  uint4 pre[kMgSlots];
-  uint32_t pmask[kMgSlots];
-  const size_t col0 = (size_t)c * kD + 64 * half + (t & 7) * 8;
-  auto load = [&](int slot, int step) {
-    const int u = step * 32 + (t >> 3);
-    pre[slot] = make_uint4(0, 0, 0, 0);
-    if (u < U) {
-      const int j = s_ul[(u / kUlChunk) & 1][u % kUlChunk];
-      pre[slot] = *(const uint4*)(hs + ((size_t)bh * Nb + j) * kStateElems + col0);
-    }
-    pmask[slot] = um[(size_t)step * kGroup + t];
+  auto issue = [&](MgSlot& d, int step) {
+    const int sa = min(step, nsteps - 1);
+    const int j0 = d.ul[64 * w + (lane >> 4)], j1 = d.ul[64 * w + 4 + (lane >> 4)];
+    __builtin_amdgcn_global_load_lds((const void*)(hs_row + (size_t)j0 * kStateElems + src0),
+                                     (lds_void_ptr)(d.st + 1024 * w), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(hs_row + (size_t)j1 * kStateElems + src1),
+                                     (lds_void_ptr)(d.st + 1024 * w + 512), 16, 0, 0);
+    // word position 64w + 4 p + m holds query block 64w + 16m + p: a lane's four words
+    // (one per column tile) are one 16-byte read
+    __builtin_amdgcn_global_load_lds((const void*)(um + (size_t)sa * kGroup + 64 * w + 16 * (lane & 3) + (lane >> 2)),
+                                     (lds_void_ptr)(d.mk + 64 * w), 4, 0, 0);
+    issue_ul(d, step + kMgSlots);
   };
-  auto store = [&](int slot) {
-    *(uint4*)(&s_b[slot][(t >> 3) * kBp + (t & 7) * 8]) = pre[slot];
-    s_m[slot][t] = pmask[slot];
-  };
-  auto step_body = [&](int slot) {
-    // A operand: rows = query blocks 64w + 16m + l16, k = union entries 8kg .. 8kg+7:
-    // byte kg of the query block's step word, expanded through the table
-    v8s a[4];
+  // lane (kg, l16) of the transposing reads: rows 8kg + ta (+4), columns 16n + 4tb .. +3
+  const int ta = l16 >> 2, tb = l16 & 3, r0 = 8 * kg + ta;
+  uint32_t toff[8];  // byte offsets in a slot's state tile
 #pragma unroll
-    for (int m = 0; m < 4; m++) a[m] = s_lut[(s_m[slot][64 * w + 16 * m + l16] >> (8 * kg)) & 255u];
-    // lane (kg, l16): states 8kg..8kg+7 of column 16n + l16, as two 4 x 16 transposes
-    const int ta = l16 >> 2, tb = l16 & 3;
+  for (int n = 0; n < 8; n++) toff[n] = 2 * (r0 * 128 + 8 * mg_pos(r0, 2 * n + (tb >> 1)) + 4 * (tb & 1));
+  auto compute = [&](const MgSlot& d) {
+    // B operand of column tile m: query block 64w + 16m + l16, union entries 8kg .. 8kg+7
+    v8bf bop[4];
+    const uint4 words = *(const uint4*)(d.mk + 64 * w + 4 * l16);
 #pragma unroll
-    for (int n = 0; n < 4; n++) {
-      const v4s_ r0 = lds_read_tr16(&s_b[slot][(8 * kg + ta) * kBp + 16 * n + 4 * tb]);
-      const v4s_ r1 = lds_read_tr16(&s_b[slot][(8 * kg + 4 + ta) * kBp + 16 * n + 4 * tb]);
-      const v8s bs = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-      const v8bf b = __builtin_bit_cast(v8bf, bs);
-#pragma unroll
-      for (int m = 0; m < 4; m++)
-        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[m]), b, acc[m][n], 0, 0, 0);
+    for (int m = 0; m < 4; m++) {
+      const uint32_t word = m == 0 ? words.x : m == 1 ? words.y : m == 2 ? words.z : words.w;
+      const uint32_t byte = (word >> (8 * kg)) & 255u;
+      const uint2 lo = s_nib[byte & 15u], hi = s_nib[byte >> 4];
+      bop[m] = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
-  };
-  static_assert(kUlChunk % 32 == 0 && kUlChunk >= 32 * (kMgSlots + 1), "chunk holds whole steps");
-  {
-    v8s e;
+    const uint32_t base = lds_addr(d.st);
 #pragma unroll
-    for (int x = 0; x < 8; x++) e[x] = ((t >> x) & 1) ? (short)0x3F80 : (short)0;  // bf16 1.0
-    s_lut[t] = e;
-  }
-  fill_ul(0);
-  __syncthreads();
-#pragma unroll
-  for (int p = 0; p < kMgSlots; p++)
-    if (p < nsteps) load(p, p);
-  if (nsteps > 0) store(0);
-  __syncthreads();
-  // step s uses slot s % kMgSlots (LDS and registers); that register slot refills with
-  // step s + kMgSlots, and step s + 1 moves from its registers into LDS
-  for (int s0 = 0; s0 < nsteps; s0 += kMgSlots) {
-#pragma unroll
-    for (int ph = 0; ph < kMgSlots; ph++) {
-      const int step = s0 + ph;
-      if (step < nsteps) {
-        if (step + kMgSlots < nsteps) load(ph, step + kMgSlots);
-        // the next step loads step + kMgSlots + 1: stage its chunk now if it starts one
-        const int un = (step + kMgSlots + 1) * 32;
-        if (un < U && un % kUlChunk == 0) fill_ul(un / kUlChunk);
-        step_body(ph);
-        if (step + 1 < nsteps) store((ph + 1) % kMgSlots);
-      }
-      __syncthreads();
-    }
-  }
-  // hc = htot - M (kept sets) or M (complement sets), staged through LDS (two halves of
-  // kGroup/2 query blocks) for 16-byte stores
-  const float* ht = htot + (size_t)bh * kStateElems + c * kD + 64 * half;
-  const int q0 = grp * kGroup;
-#pragma unroll
-  for (int hh = 0; hh < 2; hh++) {
-    if ((w >> 1) == hh) {
+    for (int h = 0; h < 2; h++) {
+      v2i_ x[8];
+      mg_tr_reads(base + toff[4 * h], base + toff[4 * h + 1], base + toff[4 * h + 2], base + toff[4 * h + 3], x);
 #pragma unroll
       for (int n = 0; n < 4; n++) {
-        const int col = 16 * n + l16;
-        const float tot = complement ? 0.f : ht[col];
-        const float sgn = complement ? 1.f : -1.f;
+        const v4i aop4 = {x[2 * n][0], x[2 * n][1], x[2 * n + 1][0], x[2 * n + 1][1]};
+        const v8bf aop = __builtin_bit_cast(v8bf, aop4);
 #pragma unroll
         for (int m = 0; m < 4; m++)
-#pragma unroll
-          for (int v = 0; v < 4; v++) {
-            const int qi = 64 * (w & 1) + 16 * m + 4 * kg + v;  // within the half
-            s_out[qi * 64 + col] = f32_to_bf16(tot + sgn * acc[m][n][v]);
-          }
+          acc[m][4 * h + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[m], acc[m][4 * h + n], 0, 0, 0);
       }
     }
-    __syncthreads();
-    for (int e = t; e < kGroup / 2 * 8; e += 256) {
-      const int qi = e >> 3, ch = e & 7, qb = q0 + kGroup / 2 * hh + qi;
-      if (qb < Nb)
-        *(uint4*)(hc + ((size_t)bh * Nb + qb) * kStateElems + c * kD + 64 * half + ch * 8) =
-            *(const uint4*)(s_out + qi * 64 + ch * 8);
+  };
+  // Ring: step s lives in slot s % 4. At the top of step s this wave has issued, after
+  // the state rows and words of step s, the union entries of step s + 4 and the four
+  // DMAs of each of steps s + 1 .. s + 2, all of which may still be in flight.
+  static_assert(kMgSlots == 4, "the slot objects and the wait count assume a ring of 4");
+  constexpr int kWait = 1 + 4 * (kMgSlots - 2);
+  constexpr int kWaitImm = (kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (15 << 8);  // vmcnt only
+  auto phase = [&](MgSlot& cur, MgSlot& prev, int step) {
+    __builtin_amdgcn_s_waitcnt(kWaitImm);
+    // step's slot complete from every wave; step - 1's slot free (every wave has used
+    // the operands it read from it). A plain barrier: a fence would wait for every DMA.
+    asm volatile("s_barrier" ::: "memory");
+    issue(prev, step + kMgSlots - 1);
+    compute(cur);
+  };
+  if (nsteps > 0) {
+    issue_ul(s0, 0);
+    issue_ul(s1, 1);
+    issue_ul(s2, 2);
+    issue_ul(s3, 3);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's union entries of steps 0..3 (read by itself only)
+    issue(s0, 0);
+    issue(s1, 1);
+    issue(s2, 2);
+    int s = 0;
+    for (; s + 4 <= nsteps; s += 4) {
+      phase(s0, s3, s);
+      phase(s1, s0, s + 1);
+      phase(s2, s1, s + 2);
+      phase(s3, s2, s + 3);
     }
-    __syncthreads();
+    if (s < nsteps) phase(s0, s3, s);
+    if (s + 1 < nsteps) phase(s1, s0, s + 1);
+    if (s + 2 < nsteps) phase(s2, s1, s + 2);
+    __builtin_amdgcn_s_waitcnt(0);  // no DMA may land after the workgroup ends
+  }
+  // hc = htot - M (kept sets) or M (complement sets): 4 consecutive columns of one query
+  // block per lane and tile, one 8-byte store
+  const int q0 = grp * kGroup;
+  const float* ht = htot + (size_t)bh * kStateElems + c * kD;
+  const float sgn = complement ? 1.f : -1.f;
+#pragma unroll
+  for (int m = 0; m < 4; m++) {
+    const int qb = q0 + 64 * w + 16 * m + l16;
+    if (qb < Nb) {
+      uint16_t* dst = hc + ((size_t)bh * Nb + qb) * kStateElems + c * kD;
+#pragma unroll
+      for (int n = 0; n < 8; n++) {
+        const int col = 16 * n + 4 * kg;
+        const float4 tv = complement ? make_float4(0.f, 0.f, 0.f, 0.f) : *(const float4*)(ht + col);
+        const v4f_ a = acc[m][n];
+        uint2 o;
+        o.x = pack_bf16x2(tv.x + sgn * a[0], tv.y + sgn * a[1]);
+        o.y = pack_bf16x2(tv.z + sgn * a[2], tv.w + sgn * a[3]);
+        *(uint2*)(dst + col) = o;
+      }
+    }
   }
 }
 
@@ -482,6 +540,15 @@ int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
 // the kept ones (see linear_union_kernel).
 static int use_complement_sets(int Nb, int ksel) { return 2 * ksel > Nb; }
 
+static void launch_mask_gemm(const void* hs, const void* htot, const void* ulist, const void* umask,
+                             const void* ucount, int BH, int Nb, int ksel, void* hc, hipStream_t st) {
+  const int ng = linear_groups(Nb);
+  const int ntiles = BH * ng * 129, per_xcd = (ntiles + 7) / 8;
+  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)hs,
+                     (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
+                     Nb, ng, use_complement_sets(Nb, ksel), ntiles, per_xcd, (uint16_t*)hc);
+}
+
 hipError_t launch_linear_union(const void* idx, int BH, int Nb, int ksel, void* ulist, void* umask, void* ucount,
                               hipStream_t st) {
   const int ng = linear_groups(Nb);
@@ -493,10 +560,7 @@ hipError_t launch_linear_union(const void* idx, int BH, int Nb, int ksel, void* 
 hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot, const void* proj, int BH, int N,
                                 int Nb, int ksel, const void* ulist, const void* umask, const void* ucount, void* hc,
                                 void* y, hipStream_t st) {
-  const int ng = linear_groups(Nb);
-  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
-                     (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
-                     Nb, ng, use_complement_sets(Nb, ksel), (uint16_t*)hc);
+  launch_mask_gemm(hs, htot, ulist, umask, ucount, BH, Nb, ksel, hc, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
@@ -510,10 +574,7 @@ hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot,
 // state gradients through it with the kept relation transposed).
 hipError_t launch_linear_mask_gemm(const void* hs, const void* htot, const void* ulist, const void* umask,
                                    const void* ucount, int BH, int Nb, int ksel, void* hc, hipStream_t st) {
-  const int ng = linear_groups(Nb);
-  hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(BH * ng * 129 * 2), dim3(256), 0, st, (const uint16_t*)hs,
-                     (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
-                     Nb, ng, use_complement_sets(Nb, ksel), (uint16_t*)hc);
+  launch_mask_gemm(hs, htot, ulist, umask, ucount, BH, Nb, ksel, hc, st);
   return hipGetLastError();
 }
 
