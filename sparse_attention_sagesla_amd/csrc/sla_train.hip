@@ -122,18 +122,20 @@ __global__ __launch_bounds__(256) void sla_kept_mask_kernel(const int* __restric
 }
 
 // ------------------------------------------------------------------ forward
-// One workgroup (2 waves) per (head, query block); wave w owns query rows 32w .. +31, one
-// per lane column. The kept key blocks' K (head-dim-reduction tiles) and V (token-reduction
-// tiles) arrive by DMA in a two-stage LDS ring, one block ahead, and both waves read them
-// there. Per block: S^T = K Q^T (two 32-key tiles), online softmax in the base-2 domain,
-// O^T += V^T P^T. Epilogue: O_s (fp32, for the backward's D), lse, and out = O_s + y (bf16).
+// One workgroup (4 waves) per (head, query block). Wave w = (kh, rg) owns query rows
+// 32rg .. +31 (one per lane column) and keys 32kh .. +31 of every kept key block: the two
+// key halves run separate online softmaxes, merged at the end. The kept blocks' K
+// (head-dim-reduction tiles) and V (token-reduction tiles) arrive by DMA in a two-stage
+// LDS ring, one block ahead; each wave copies a quarter of each tile. Per block and wave:
+// S^T = K Q^T over its 32 keys, online softmax in the base-2 domain, O^T += V^T P^T.
+// Epilogue: O_s (fp32, for the backward's D), lse, and out = O_s + y (bf16).
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                      const uint16_t* __restrict__ vt, const int* __restrict__ idx,
-                                                      const uint16_t* __restrict__ y, int BH, int N, int Nb, int ksel,
-                                                      int per_xcd, uint16_t* __restrict__ out,
-                                                      float* __restrict__ os, float* __restrict__ lse) {
+__global__ __launch_bounds__(256, 2) void sla_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ vt, const int* __restrict__ idx,
+                                                         const uint16_t* __restrict__ y, int BH, int N, int Nb, int ksel,
+                                                         int per_xcd, uint16_t* __restrict__ out,
+                                                         float* __restrict__ os, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) uint16_t sK0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sV0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sK1[kTrTile];
@@ -141,8 +143,10 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, i = tile % Nb;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
-  const int qi = kBlk * i + 32 * w + r;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = w & 1, kh = w >> 1;
+  const int l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  const int qi = kBlk * i + 32 * rg + r;
   const bool qvalid = qi < N;
   const uint16_t* Qh = q + (size_t)bh * N * kD;
   const float c = kLog2e * 0.08838834764831845f;  // log2(e) / sqrt(128)
@@ -158,69 +162,66 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
   for (int ct = 0; ct < 4; ct++) o[ct] = (v16f){};
 
   const int* irow = idx + ((size_t)bh * Nb + i) * ksel;
-  // each wave copies half of each 16 KiB tile: 8 DMAs of 1 KiB (16 bytes per lane)
+  // each wave copies a quarter of each 16 KiB tile: 4 DMAs of 1 KiB (16 bytes per lane)
   auto issue = [&](uint16_t* dk_, uint16_t* dv_, int j) {
-    const uint16_t* ks = k + ((size_t)bh * Nb + j) * kTrTile + (w * 8 * 64 + l) * 8;
-    const uint16_t* vs = vt + ((size_t)bh * Nb + j) * kTrTile + (w * 8 * 64 + l) * 8;
+    const uint16_t* ks = k + ((size_t)bh * Nb + j) * kTrTile + (w * 4 * 64 + l) * 8;
+    const uint16_t* vs = vt + ((size_t)bh * Nb + j) * kTrTile + (w * 4 * 64 + l) * 8;
 #pragma unroll
-    for (int cc = 0; cc < 8; cc++)
-      __builtin_amdgcn_global_load_lds((const void*)(ks + cc * 512), (lds_ptr_t)(dk_ + (w * 8 + cc) * 512), 16, 0, 0);
+    for (int cc = 0; cc < 4; cc++)
+      __builtin_amdgcn_global_load_lds((const void*)(ks + cc * 512), (lds_ptr_t)(dk_ + (w * 4 + cc) * 512), 16, 0, 0);
 #pragma unroll
-    for (int cc = 0; cc < 8; cc++)
-      __builtin_amdgcn_global_load_lds((const void*)(vs + cc * 512), (lds_ptr_t)(dv_ + (w * 8 + cc) * 512), 16, 0, 0);
+    for (int cc = 0; cc < 4; cc++)
+      __builtin_amdgcn_global_load_lds((const void*)(vs + cc * 512), (lds_ptr_t)(dv_ + (w * 4 + cc) * 512), 16, 0, 0);
   };
   auto compute = [&](const uint16_t* ck, const uint16_t* cv, int j) {
     const int nj = block_len(j, N);
-    float sc[2][16];
+    if (nj <= 32 * kh) return;  // this wave's key half is past the sequence's end
+    v16f acc = (v16f){};
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++) {
-      v16f acc = (v16f){};
+    for (int s = 0; s < 8; s++) acc = mfma(*(const v8bf*)(ck + ((kh * 8 + s) * 64 + l) * 8), qop[s], acc);
+    if (nj < 32 * kh + 32) {  // the partial last block: keys past its end drop out
 #pragma unroll
-      for (int s = 0; s < 8; s++) acc = mfma(*(const v8bf*)(ck + ((kt * 8 + s) * 64 + l) * 8), qop[s], acc);
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int key = 32 * kt + 8 * (v >> 2) + 4 * g + (v & 3);
-        sc[kt][v] = key < nj ? acc[v] * c : -INFINITY;
-      }
+      for (int v = 0; v < 16; v++)
+        if (32 * kh + 8 * (v >> 2) + 4 * g + (v & 3) >= nj) acc[v] = -INFINITY;
     }
+    // the maximum of the raw products; scaling by c > 0 commutes with it
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) mx = fmaxf(mx, sc[kt][v]);
+    for (int v = 0; v < 16; v++) mx = fmaxf(mx, acc[v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+    const float mn = fmaxf(m, mx * c);
+    // rescale only when some row of the wave has a new maximum (alpha = 1 exactly otherwise)
+    if (__any(mn > m)) {
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) o[ct][v] *= alpha;
+    }
+    m = mn;
+    float sc[16];
     float rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        sc[kt][v] = exp2f(sc[kt][v] - mn);
-        rs += sc[kt][v];
-      }
+    for (int v = 0; v < 16; v++) {
+      sc[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], c, -mn));
+      rs += sc[v];
+    }
     rs += __shfl_xor(rs, 32);
-    lsum = lsum * alpha + rs;
-    m = mn;
+    lsum += rs;
 #pragma unroll
-    for (int ct = 0; ct < 4; ct++)
+    for (int t = 0; t < 2; t++) {
+      const v8bf pb = pack8(&sc[8 * t]);
 #pragma unroll
-      for (int v = 0; v < 16; v++) o[ct][v] *= alpha;
-#pragma unroll
-    for (int kt = 0; kt < 2; kt++)
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        const v8bf pb = pack8(&sc[kt][8 * t]);
-#pragma unroll
-        for (int ct = 0; ct < 4; ct++)
-          o[ct] = mfma(*(const v8bf*)(cv + ((((kt * 4 + ct) * 2 + t) * 64) + l) * 8), pb, o[ct]);
-      }
+      for (int ct = 0; ct < 4; ct++)
+        o[ct] = mfma(*(const v8bf*)(cv + ((((kh * 4 + ct) * 2 + t) * 64) + l) * 8), pb, o[ct]);
+    }
   };
 
   issue(sK0, sV0, irow[0]);
   for (int kk = 0; kk < ksel; kk += 2) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs of block kk have landed
-    __syncthreads();                // and the other wave's; all reads of the other stage are done
+    __syncthreads();                // and the other waves'; all reads of the other stage are done
     if (kk + 1 < ksel) issue(sK1, sV1, irow[kk + 1]);
     compute(sK0, sV0, irow[kk]);
     if (kk + 1 < ksel) {
@@ -231,7 +232,33 @@ __global__ __launch_bounds__(128) void sla_fwd_kernel(const uint16_t* __restrict
     }
   }
 
-  if (!qvalid) return;
+  // merge the two key halves: the kh = 1 waves hand m, the row sum and O^T (in their
+  // lane order) to the kh = 0 waves through the ring's memory
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  float* xo = reinterpret_cast<float*>(rg == 0 ? sK0 : sK1);  // 64 x 64 floats (one K tile)
+  float* xm = reinterpret_cast<float*>(rg == 0 ? sV0 : sV1);  // 2 x 64 floats
+  if (kh == 1) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) xo[(ct * 16 + v) * 64 + l] = o[ct][v];
+    xm[l] = m;
+    xm[64 + l] = lsum;
+  }
+  __syncthreads();
+  if (kh == 1 || !qvalid) return;
+  {
+    const float m1 = xm[l], l1 = xm[64 + l];
+    const float mt = fmaxf(m, m1);  // m is finite: key half 0 of every kept block has a key
+    const float a0 = __builtin_amdgcn_exp2f(m - mt), a1 = __builtin_amdgcn_exp2f(m1 - mt);
+    lsum = lsum * a0 + l1 * a1;
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) o[ct][v] = o[ct][v] * a0 + xo[(ct * 16 + v) * 64 + l] * a1;
+    m = mt;
+  }
   const float inv = 1.f / lsum;
   if (g == 0) lse[(size_t)bh * N + qi] = m + log2f(lsum);
   const size_t rowoff = ((size_t)bh * N + qi) * kD;
@@ -1034,7 +1061,7 @@ hipError_t launch_sla_kept_mask(const void* idx, int BH, int Nb, int ksel, void*
 hipError_t launch_sla_fwd(const void* q, const void* k, const void* vt, const void* idx, const void* y, int BH, int N,
                           int Nb, int ksel, void* out, void* os, void* lse, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
-  hipLaunchKernelGGL(sla_fwd_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const uint16_t*)q, (const uint16_t*)k,
+  hipLaunchKernelGGL(sla_fwd_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)k,
                      (const uint16_t*)vt, (const int*)idx, (const uint16_t*)y, BH, N, Nb, ksel, per_xcd,
                      (uint16_t*)out, (float*)os, (float*)lse);
   return hipGetLastError();
