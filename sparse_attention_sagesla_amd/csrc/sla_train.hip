@@ -359,12 +359,15 @@ __global__ __launch_bounds__(256) void sla_bwd_dq_kernel(const uint16_t* __restr
       s_ = mfma(*(const v8bf*)(ca + off), qop[s], s_);
       dp = mfma(*(const v8bf*)(cb + off), dop[s], dp);
     }
+    // rows past the sequence's end have Q = dO = 0 and D = 0, so their dS is 0 without a
+    // mask; keys past it (zero rows of the tiles) are masked in the partial last block
     float ds[16];
 #pragma unroll
-    for (int x = 0; x < 16; x++) {
-      const int key = 32 * kt + 8 * (x >> 2) + 4 * g + (x & 3);
-      const float p = (key < nj && qvalid) ? exp2f(s_[x] * c - L) : 0.f;
-      ds[x] = p * (dp[x] - D);
+    for (int x = 0; x < 16; x++) ds[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[x], c, -L)) * (dp[x] - D);
+    if (nj < kBlk) {
+#pragma unroll
+      for (int x = 0; x < 16; x++)
+        if (32 * kt + 8 * (x >> 2) + 4 * g + (x & 3) >= nj) ds[x] = 0.f;
     }
 #pragma unroll
     for (int t = 0; t < 2; t++) {
@@ -525,9 +528,14 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int x = 4 * x4 + e;
-        const float pe = (q0 + e < ni) ? exp2f(s_[x] * c - Lq[e]) : 0.f;
+        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[x], c, -Lq[e]));
         p[x] = role == 0 ? pe : pe * (dp[x] - Dq[e]);
       }
+    }
+    if (ni < kBlk) {  // the partial last query block: rows past its end drop out
+#pragma unroll
+      for (int x = 0; x < 16; x++)
+        if (32 * qt + 8 * (x >> 2) + 4 * g + (x & 3) >= ni) p[x] = 0.f;
     }
     const uint16_t* src = role == 0 ? d : c2;  // dO^T for dV, Q^T for dK
 #pragma unroll
