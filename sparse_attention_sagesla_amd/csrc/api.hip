@@ -27,9 +27,9 @@ hipError_t launch_sla_relayout_hd(const void*, int, int, int, void*, hipStream_t
 hipError_t launch_sla_fwd(const void*, const void*, const void*, const void*, const void*, int, int, int, int, void*,
                           void*, void*, hipStream_t);
 hipError_t launch_sla_bwd_dq(const void*, const void*, const void*, const void*, const void*, const void*, const void*,
-                             const void*, int, int, int, int, void*, void*, hipStream_t);
+                             int, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_sla_bwd_dkdv(const void*, const void*, const void*, const void*, const void*, const void*,
-                               const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
+                               const void*, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_sla_lin_bwd_q(const void*, const void*, const void*, const void*, int, int, int, void*, void*, void*,
                                 void*, void*, hipStream_t);
 hipError_t launch_sla_lin_dhc(const void*, const void*, const void*, int, int, int, void*, void*, hipStream_t);
@@ -570,30 +570,27 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
   auto P = [&](int r) { return (void*)(ws + off[r]); };
   hipError_t e;
   // sparse part: dq, dk, dv written
-  if ((e = launch_sla_relayout(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_KT), st)) != hipSuccess) return from_hip(e);
-  if ((e = launch_sla_relayout(q, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_QT), st)) != hipSuccess) return from_hip(e);
-  if ((e = launch_sla_relayout(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_DOT), st)) != hipSuccess)
-    return from_hip(e);
   if ((e = launch_sla_kept_mask(P(SAGESLA_WS_IDX), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_MASK), st)) != hipSuccess)
     return from_hip(e);
-  // dQ: K and V in head-dim-reduction tiles (V's in the V tile region), K in token-reduction tiles
+  // dQ: K and V in head-dim-reduction tiles (V's in the V tile region); the kernel reads K
+  // with tokens as the reduction index from the same tile
   if ((e = launch_sla_relayout_hd(k, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H0), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_sla_relayout_hd(v, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_VT), st)) != hipSuccess)
     return from_hip(e);
-  if ((e = launch_sla_bwd_dq(q, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_VT), P(SAGESLA_SLA_WS_KT), dout,
+  if ((e = launch_sla_bwd_dq(q, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_VT), dout,
                              P(SAGESLA_SLA_WS_OS), P(SAGESLA_SLA_WS_LSE),
                              P(SAGESLA_WS_IDX), gm.BH, gm.N, gm.Nb, gm.ksel, P(SAGESLA_SLA_WS_DSUM), dq, st)) !=
       hipSuccess)
     return from_hip(e);
-  // dK, dV: Q and dO in head-dim-reduction tiles (Q's in H0, which K's no longer need) and
-  // token-reduction tiles
+  // dK, dV: Q and dO in head-dim-reduction tiles (Q's in H0, which K's no longer need),
+  // read with either index reduced
   if ((e = launch_sla_relayout_hd(q, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H0), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_sla_relayout_hd(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_H1), st)) != hipSuccess)
     return from_hip(e);
-  if ((e = launch_sla_bwd_dkdv(k, v, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_H1), P(SAGESLA_SLA_WS_QT),
-                               P(SAGESLA_SLA_WS_DOT), P(SAGESLA_SLA_WS_LSE), P(SAGESLA_SLA_WS_DSUM),
+  if ((e = launch_sla_bwd_dkdv(k, v, P(SAGESLA_SLA_WS_H0), P(SAGESLA_SLA_WS_H1), P(SAGESLA_SLA_WS_LSE),
+                               P(SAGESLA_SLA_WS_DSUM),
                                P(SAGESLA_SLA_WS_MASK), gm.BH, gm.N, gm.Nb, dk, dv, st)) != hipSuccess)
     return from_hip(e);
   if (proj == nullptr) return SAGESLA_OK;
@@ -623,6 +620,9 @@ sagesla_status sagesla_sla_bwd(const void* q, const void* k, const void* v, cons
                                    P(SAGESLA_WS_UCOUNT), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_HC), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_sla_lin_bwd_k(k, v, P(SAGESLA_WS_HC), gm.BH, gm.N, gm.Nb, dk, dv, st)) != hipSuccess)
+    return from_hip(e);
+  // dW = O_l^T dO: both in token-reduction tiles
+  if ((e = launch_sla_relayout(dout, gm.BH, gm.N, gm.Nb, P(SAGESLA_SLA_WS_DOT), st)) != hipSuccess)
     return from_hip(e);
   e = launch_sla_dw(P(SAGESLA_SLA_WS_VT), P(SAGESLA_SLA_WS_DOT), gm.BH * gm.Nb, P(SAGESLA_SLA_WS_DWP), dproj, st);
   return from_hip(e);

@@ -53,6 +53,43 @@ __device__ __forceinline__ v16f mfma(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Head-dim-reduction tiles store the 16-byte chunk of lane l of step s at position
+// hd_swz(s, l) of its 64-chunk group (an involution: bits 2 and 3 of l flipped by the
+// step's parity and by l / 32). A lane-contiguous operand read stays one permutation of
+// a 1 KiB group; the transposing reads below (tokens as the reduction index, taken from
+// the same tile) then hit every bank once per half-wave.
+__device__ __forceinline__ int hd_swz(int s, int l) { return l ^ (((s & 1) << 2) | ((l >> 5) << 3)); }
+
+// The operand of lane l for head-dim step s of key/query tile tt from an LDS copy of a
+// head-dim-reduction tile.
+__device__ __forceinline__ v8bf hd_op(const uint16_t* tile, int tt, int s, int l) {
+  return *(const v8bf*)(tile + ((tt * 8 + s) * 64 + hd_swz(s, l)) * 8);
+}
+
+typedef short v4s_ __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_* lds_v4s_ptr;
+
+// Byte offsets, within a head-dim-reduction tile in LDS, of the two transposing reads that
+// give lane l the token-reduction operand of tile (tt, ct, t) = (0, 0, 0): within each
+// 16 lanes (group G = l / 16), lanes 4a + b name channels 16(G % 2) + 4b .. +3 of token
+// 4(G / 2) + a (+8 for the second read), and lane j of the group receives channel
+// 16(G % 2) + j at those 4 tokens, which is the token-reduction lane order. Tile (tt, ct,
+// t) adds tt * 8192 + ct * 2048 + t * 256 bytes.
+__device__ __forceinline__ void tok_offsets(int l, uint32_t& o0, uint32_t& o1) {
+  const int G = l >> 4, a = (l >> 2) & 3, b = l & 3, sp = G & 1, g = G >> 1, gch = b >> 1;
+  const int i0 = 4 * g + a + 32 * gch, i1 = i0 + 8;
+  o0 = (uint32_t)((sp * 64 + hd_swz(sp, i0)) * 16 + 8 * (b & 1));
+  o1 = (uint32_t)((sp * 64 + hd_swz(sp, i1)) * 16 + 8 * (b & 1));
+}
+
+__device__ __forceinline__ v8bf tok_op(const uint16_t* tile, uint32_t o0, uint32_t o1, int tt, int ct, int t) {
+  const char* b = (const char*)tile + (tt * 8192 + ct * 2048 + t * 256);
+  const v4s_ x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(b + o0));
+  const v4s_ x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(b + o1));
+  const v8s r = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  return __builtin_bit_cast(v8bf, r);
+}
+
 // ------------------------------------------------------------------ token-reduction tiles
 // X [BH][N][128] bf16 -> Xt [BH][Nb][kTrTile] bf16 (tokens past N are zero). One workgroup
 // per block: the block is staged in LDS, then each thread gathers 8 values per chunk.
@@ -86,9 +123,10 @@ __global__ __launch_bounds__(256) void sla_relayout_kernel(const uint16_t* __res
   }
 }
 
-// X [BH][N][128] bf16 -> "head-dim-reduction tiles" [BH][Nb][kTrTile]: chunk (tt*8 + s)*64 + l
-// holds X[32tt + r][16s + 8g .. +7], the operand order of products that reduce over the head
-// dimension, so that one operand is one lane-contiguous 1 KiB read (tokens past N are 0).
+// X [BH][N][128] bf16 -> "head-dim-reduction tiles" [BH][Nb][kTrTile]: chunk
+// (tt*8 + s)*64 + hd_swz(s, l) holds X[32tt + r][16s + 8g .. +7], the operand order of
+// products that reduce over the head dimension, so that one operand is one 1 KiB read
+// (tokens past N are 0).
 __global__ __launch_bounds__(256) void sla_relayout_hd_kernel(const uint16_t* __restrict__ x, int N, int Nb,
                                                               uint16_t* __restrict__ xh) {
   const int bh = blockIdx.x / Nb, blk = blockIdx.x % Nb, t = threadIdx.x;
@@ -97,8 +135,8 @@ __global__ __launch_bounds__(256) void sla_relayout_hd_kernel(const uint16_t* __
   uint16_t* dst = xh + ((size_t)bh * Nb + blk) * kTrTile;
 #pragma unroll
   for (int k = 0; k < 4; k++) {
-    const int c = t + 256 * k;  // chunk (tt*8 + s)*64 + l
-    const int l = c & 63, s = (c >> 6) & 7, tt = c >> 9, row = 32 * tt + (l & 31), col = 16 * s + 8 * (l >> 5);
+    const int c = t + 256 * k;  // stored position (tt*8 + s)*64 + hd_swz(s, l)
+    const int s = (c >> 6) & 7, l = hd_swz(s, c & 63), tt = c >> 9, row = 32 * tt + (l & 31), col = 16 * s + 8 * (l >> 5);
     v4i val = (v4i){0, 0, 0, 0};
     if (row < n) val = *(const v4i*)(src + (size_t)row * kD + col);
     *(v4i*)(dst + (size_t)c * 8) = val;
@@ -178,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_kernel(const uint16_t* __restr
     if (nj <= 32 * kh) return;  // this wave's key half is past the sequence's end
     v16f acc = (v16f){};
 #pragma unroll
-    for (int s = 0; s < 8; s++) acc = mfma(*(const v8bf*)(ck + ((kh * 8 + s) * 64 + l) * 8), qop[s], acc);
+    for (int s = 0; s < 8; s++) acc = mfma(hd_op(ck, kh, s, l), qop[s], acc);
     if (nj < 32 * kh + 32) {  // the partial last block: keys past its end drop out
 #pragma unroll
       for (int v = 0; v < 16; v++)
@@ -295,18 +333,16 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_kernel(const uint16_t* __restr
 // pass). The kept blocks' K and V (head-dim-reduction tiles) and K (token-reduction tiles)
 // arrive by DMA in a two-stage LDS ring, one block ahead. Per block and wave:
 // S^T = K Q^T, dP^T = V dO^T, dS^T = P^T * (dP^T - D), dQ^T += K^T dS^T.
-__global__ __launch_bounds__(256) void sla_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh,
-                                                         const uint16_t* __restrict__ vh, const uint16_t* __restrict__ kt_,
-                                                         const uint16_t* __restrict__ dout, const float* __restrict__ os,
+__global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kh,
+                                                            const uint16_t* __restrict__ vh,
+                                                            const uint16_t* __restrict__ dout, const float* __restrict__ os,
                                                          const float* __restrict__ lse, const int* __restrict__ idx,
                                                          int BH, int N, int Nb, int ksel, int per_xcd,
                                                          float* __restrict__ dsum, float* __restrict__ dq) {
   __shared__ __attribute__((aligned(1024))) uint16_t sA0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sB0[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sC0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sA1[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sB1[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sC1[kTrTile];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, i = tile % Nb;
@@ -341,23 +377,24 @@ __global__ __launch_bounds__(256) void sla_bwd_dq_kernel(const uint16_t* __restr
 
   const int* irow = idx + ((size_t)bh * Nb + i) * ksel;
   // each wave copies a quarter of each 16 KiB tile: 4 DMAs of 1 KiB
-  auto issue = [&](uint16_t* da, uint16_t* db, uint16_t* dc, int j) {
+  auto issue = [&](uint16_t* da, uint16_t* db, int j) {
     const size_t to = ((size_t)bh * Nb + j) * kTrTile + (w * 4 * 64 + l) * 8;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++) {
       __builtin_amdgcn_global_load_lds((const void*)(kh + to + cc * 512), (lds_ptr_t)(da + (w * 4 + cc) * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(vh + to + cc * 512), (lds_ptr_t)(db + (w * 4 + cc) * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(kt_ + to + cc * 512), (lds_ptr_t)(dc + (w * 4 + cc) * 512), 16, 0, 0);
     }
   };
-  auto compute = [&](const uint16_t* ca, const uint16_t* cb, const uint16_t* cc_, int j) {
+  uint32_t to0, to1;
+  tok_offsets(l, to0, to1);
+  // K^T for dQ comes from the same K tile through transposing reads
+  auto compute = [&](const uint16_t* ca, const uint16_t* cb, int j) {
     const int nj = block_len(j, N);
     v16f s_ = (v16f){}, dp = (v16f){};
 #pragma unroll
     for (int s = 0; s < 8; s++) {
-      const int off = ((kt * 8 + s) * 64 + l) * 8;
-      s_ = mfma(*(const v8bf*)(ca + off), qop[s], s_);
-      dp = mfma(*(const v8bf*)(cb + off), dop[s], dp);
+      s_ = mfma(hd_op(ca, kt, s, l), qop[s], s_);
+      dp = mfma(hd_op(cb, kt, s, l), dop[s], dp);
     }
     // rows past the sequence's end have Q = dO = 0 and D = 0, so their dS is 0 without a
     // mask; keys past it (zero rows of the tiles) are masked in the partial last block
@@ -373,22 +410,21 @@ __global__ __launch_bounds__(256) void sla_bwd_dq_kernel(const uint16_t* __restr
     for (int t = 0; t < 2; t++) {
       const v8bf bq = pack8(&ds[8 * t]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++)
-        acc[ct] = mfma(*(const v8bf*)(cc_ + ((((kt * 4 + ct) * 2 + t) * 64) + l) * 8), bq, acc[ct]);
+      for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(tok_op(ca, to0, to1, kt, ct, t), bq, acc[ct]);
     }
   };
 
-  issue(sA0, sB0, sC0, irow[0]);
+  issue(sA0, sB0, irow[0]);
   for (int kk = 0; kk < ksel; kk += 2) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (kk + 1 < ksel) issue(sA1, sB1, sC1, irow[kk + 1]);
-    compute(sA0, sB0, sC0, irow[kk]);
+    if (kk + 1 < ksel) issue(sA1, sB1, irow[kk + 1]);
+    compute(sA0, sB0, irow[kk]);
     if (kk + 1 < ksel) {
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (kk + 2 < ksel) issue(sA0, sB0, sC0, irow[kk + 2]);
-      compute(sA1, sB1, sC1, irow[kk + 1]);
+      if (kk + 2 < ksel) issue(sA0, sB0, irow[kk + 2]);
+      compute(sA1, sB1, irow[kk + 1]);
     }
   }
 
@@ -440,18 +476,13 @@ __device__ __forceinline__ int next_set(const uint32_t* row, int nw, int from) {
 
 __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                            const uint16_t* __restrict__ qh_, const uint16_t* __restrict__ doh,
-                                                           const uint16_t* __restrict__ qt_, const uint16_t* __restrict__ dot_,
                                                            const float* __restrict__ lse, const float* __restrict__ dsum,
                                                            const uint32_t* __restrict__ mask, int BH, int N, int Nb, int nw,
                                                            int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) uint16_t sQh0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sDh0[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQt0[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sDt0[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sQh1[kTrTile];
   __shared__ __attribute__((aligned(1024))) uint16_t sDh1[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQt1[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sDt1[kTrTile];
   __shared__ __attribute__((aligned(256))) float sL0[kBlk], sS0[kBlk], sL1[kBlk], sS1[kBlk];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
@@ -479,20 +510,16 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
   // each wave copies an eighth of each 16 KiB tile (2 DMAs of 1 KiB), wave 0 the block's
   // lse and wave 1 its D (rows past N repeat the last row; never used)
   int lo16 = (w * 2 * 64 + l) * 16, lo4 = l * 4;
-  auto issue = [&](uint16_t* a, uint16_t* b, uint16_t* c2, uint16_t* d, float* sl, float* ss, int i) {
+  auto issue = [&](uint16_t* a, uint16_t* b, float* sl, float* ss, int i) {
     asm volatile("" : "+v"(lo16), "+v"(lo4));
     const size_t tb = ((size_t)bh * Nb + i) * kTrTile * 2;  // bytes
     const char* s0 = (const char*)qh_ + tb;
     const char* s1 = (const char*)doh + tb;
-    const char* s2 = (const char*)qt_ + tb;
-    const char* s3 = (const char*)dot_ + tb;
 #pragma unroll
     for (int cc = 0; cc < 2; cc++) {
       const int ld = (w * 2 + cc) * 512;
       __builtin_amdgcn_global_load_lds((const void*)(s0 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(a + ld), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(s1 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(b + ld), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(s2 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(c2 + ld), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(s3 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(d + ld), 16, 0, 0);
     }
     const size_t r0 = (size_t)bh * N + (size_t)kBlk * i;
     const int nrow = min(kBlk, N - kBlk * i);
@@ -500,15 +527,18 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
     if (w == 0) __builtin_amdgcn_global_load_lds((const void*)((const char*)(lse + r0) + off4), (lds_ptr_t)sl, 4, 0, 0);
     if (w == 1) __builtin_amdgcn_global_load_lds((const void*)((const char*)(dsum + r0) + off4), (lds_ptr_t)ss, 4, 0, 0);
   };
-  auto compute = [&](const uint16_t* a, const uint16_t* b, const uint16_t* c2, const uint16_t* d, const float* sl,
-                     const float* ss, int i) {
+  uint32_t to0, to1;
+  tok_offsets(l, to0, to1);
+  // Q^T and dO^T (tokens as the reduction index) come from the same tiles through
+  // transposing reads
+  auto compute = [&](const uint16_t* a, const uint16_t* b, const float* sl, const float* ss, int i) {
     const int ni = block_len(i, N);
     v16f s_ = (v16f){}, dp = (v16f){};
 #pragma unroll
-    for (int s = 0; s < 8; s++) s_ = mfma(*(const v8bf*)(a + ((qt * 8 + s) * 64 + l) * 8), kop[s], s_);
+    for (int s = 0; s < 8; s++) s_ = mfma(hd_op(a, qt, s, l), kop[s], s_);
     if (role == 1) {
 #pragma unroll
-      for (int s = 0; s < 8; s++) dp = mfma(*(const v8bf*)(b + ((qt * 8 + s) * 64 + l) * 8), vop[s], dp);
+      for (int s = 0; s < 8; s++) dp = mfma(hd_op(b, qt, s, l), vop[s], dp);
     }
     // registers x hold query rows 32qt + 8(x/4) + 4g + x%4 of the block
     float p[16];
@@ -537,31 +567,30 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
       for (int x = 0; x < 16; x++)
         if (32 * qt + 8 * (x >> 2) + 4 * g + (x & 3) >= ni) p[x] = 0.f;
     }
-    const uint16_t* src = role == 0 ? d : c2;  // dO^T for dV, Q^T for dK
+    const uint16_t* src = role == 0 ? b : a;  // dO^T for dV, Q^T for dK
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const v8bf pb = pack8(&p[8 * t]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++)
-        acc[ct] = mfma(*(const v8bf*)(src + ((((qt * 4 + ct) * 2 + t) * 64) + l) * 8), pb, acc[ct]);
+      for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(tok_op(src, to0, to1, qt, ct, t), pb, acc[ct]);
     }
   };
 
   int icur = next_set(mrow, nw, 0);
-  if (icur >= 0) issue(sQh0, sDh0, sQt0, sDt0, sL0, sS0, icur);
+  if (icur >= 0) issue(sQh0, sDh0, sL0, sS0, icur);
   while (icur >= 0) {
     int inext = next_set(mrow, nw, icur + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (inext >= 0) issue(sQh1, sDh1, sQt1, sDt1, sL1, sS1, inext);
-    compute(sQh0, sDh0, sQt0, sDt0, sL0, sS0, icur);
+    if (inext >= 0) issue(sQh1, sDh1, sL1, sS1, inext);
+    compute(sQh0, sDh0, sL0, sS0, icur);
     icur = inext;
     if (icur < 0) break;
     inext = next_set(mrow, nw, icur + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (inext >= 0) issue(sQh0, sDh0, sQt0, sDt0, sL0, sS0, inext);
-    compute(sQh1, sDh1, sQt1, sDt1, sL1, sS1, icur);
+    if (inext >= 0) issue(sQh0, sDh0, sL0, sS0, inext);
+    compute(sQh1, sDh1, sL1, sS1, icur);
     icur = inext;
   }
 
@@ -569,7 +598,7 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // 16 KiB per (role, key half)
-  float* red = (float*)(role == 0 ? (kh == 0 ? sQh0 : sDh0) : (kh == 0 ? sQt0 : sDt0));
+  float* red = (float*)(role == 0 ? (kh == 0 ? sQh0 : sDh0) : (kh == 0 ? sQh1 : sDh1));
   if (qt == 1) {
 #pragma unroll
     for (int ct = 0; ct < 4; ct++)
@@ -1075,23 +1104,22 @@ hipError_t launch_sla_fwd(const void* q, const void* k, const void* vt, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_sla_bwd_dq(const void* q, const void* kh, const void* vh, const void* kt, const void* dout,
+hipError_t launch_sla_bwd_dq(const void* q, const void* kh, const void* vh, const void* dout,
                              const void* os, const void* lse, const void* idx, int BH, int N, int Nb, int ksel,
                              void* dsum, void* dq, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sla_bwd_dq_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q, (const uint16_t*)kh,
-                     (const uint16_t*)vh, (const uint16_t*)kt, (const uint16_t*)dout, (const float*)os,
+                     (const uint16_t*)vh, (const uint16_t*)dout, (const float*)os,
                      (const float*)lse, (const int*)idx, BH, N, Nb, ksel, per_xcd, (float*)dsum, (float*)dq);
   return hipGetLastError();
 }
 
-hipError_t launch_sla_bwd_dkdv(const void* k, const void* v, const void* qh, const void* doh, const void* qt,
-                               const void* dot, const void* lse, const void* dsum, const void* mask, int BH, int N,
+hipError_t launch_sla_bwd_dkdv(const void* k, const void* v, const void* qh, const void* doh,
+                               const void* lse, const void* dsum, const void* mask, int BH, int N,
                                int Nb, void* dk, void* dv, hipStream_t st) {
   const int tiles = BH * Nb, per_xcd = (tiles + 7) / 8, nw = (Nb + 31) / 32;
   hipLaunchKernelGGL(sla_bwd_dkdv_kernel, dim3(per_xcd * 8), dim3(512), 0, st, (const uint16_t*)k,
-                     (const uint16_t*)v, (const uint16_t*)qh, (const uint16_t*)doh, (const uint16_t*)qt,
-                     (const uint16_t*)dot, (const float*)lse, (const float*)dsum, (const uint32_t*)mask, BH, N, Nb, nw,
+                     (const uint16_t*)v, (const uint16_t*)qh, (const uint16_t*)doh, (const float*)lse, (const float*)dsum, (const uint32_t*)mask, BH, N, Nb, nw,
                      per_xcd, (float*)dk, (float*)dv);
   return hipGetLastError();
 }
