@@ -82,6 +82,34 @@ __device__ __forceinline__ void tok_offsets(int l, uint32_t& o0, uint32_t& o1) {
   o1 = (uint32_t)((sp * 64 + hd_swz(sp, i1)) * 16 + 8 * (b & 1));
 }
 
+// The token-reduction operands of tiles (tt, ct = 0..3, t) in one block of 8 transposing
+// reads, waited for inside it. Written out so that the compiler, which cannot tell which
+// LDS object such a read depends on, adds no wait for DMAs still in flight: the caller
+// has waited for this tile's copies.
+typedef int v2i_ __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void tok_ops4(const uint16_t* tile, uint32_t o0, uint32_t o1, int tt, int t, v8bf (&out)[4]) {
+  const uint32_t b = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)tile + tt * 8192 + t * 256;
+  v2i_ x[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:6144\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
+      : "v"(b + o0), "v"(b + o1)
+      : "memory");
+#pragma unroll
+  for (int ct = 0; ct < 4; ct++) {
+    const v4i v = {x[2 * ct][0], x[2 * ct][1], x[2 * ct + 1][0], x[2 * ct + 1][1]};
+    out[ct] = __builtin_bit_cast(v8bf, v);
+  }
+}
+
 __device__ __forceinline__ v8bf tok_op(const uint16_t* tile, uint32_t o0, uint32_t o1, int tt, int ct, int t) {
   const char* b = (const char*)tile + (tt * 8192 + ct * 2048 + t * 256);
   const v4s_ x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(b + o0));
@@ -465,6 +493,17 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(const uint16_t* __re
 // (head-dim-reduction and token-reduction tiles), lse and D arrive by DMA in a two-stage LDS
 // ring, one block ahead. Per block: S = Q K^T (lanes = keys, registers = queries), P from
 // lse; role 0: dV^T += dO^T P; role 1: dP = dO V^T, dS = P * (dP - D), dK^T += Q^T dS.
+// One ring slot of the dK/dV kernel: a query block's Q and dO head-dim-reduction tiles
+// and its lse and D.
+constexpr int kMaxMaskWords = 512;  // 32-bit words of a kept-by row: N <= 2^20 tokens
+
+struct DkvSlot {
+  uint16_t qh[kTrTile];
+  uint16_t dh[kTrTile];
+  float L[kBlk];
+  float S[kBlk];
+};
+
 __device__ __forceinline__ int next_set(const uint32_t* row, int nw, int from) {
   for (int wi = from >> 5; wi < nw; wi++) {
     uint32_t b = row[wi];
@@ -479,15 +518,12 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
                                                            const float* __restrict__ lse, const float* __restrict__ dsum,
                                                            const uint32_t* __restrict__ mask, int BH, int N, int Nb, int nw,
                                                            int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
-  __shared__ __attribute__((aligned(1024))) uint16_t sQh0[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sDh0[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sQh1[kTrTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t sDh1[kTrTile];
-  __shared__ __attribute__((aligned(256))) float sL0[kBlk], sS0[kBlk], sL1[kBlk], sS1[kBlk];
+  __shared__ __attribute__((aligned(1024))) DkvSlot z0, z1, z2, z3;
+  __shared__ uint32_t s_mrow[kMaxMaskWords];  // this key block's kept-by row (Nb <= 32 * kMaxMaskWords)
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, j = tile % Nb;
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, r = l & 31, g = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), l = threadIdx.x & 63, r = l & 31, g = l >> 5;
   const int role = w >> 2, kh = (w >> 1) & 1, qt = w & 1;
   const int kj = kBlk * j + 32 * kh + r;
   const bool kvalid = kj < N;
@@ -507,10 +543,11 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
 
   const uint32_t* mrow = mask + ((size_t)bh * Nb + j) * nw;
   // per-lane byte offsets kept opaque, so that the DMAs use a scalar base + lane offset;
-  // each wave copies an eighth of each 16 KiB tile (2 DMAs of 1 KiB), wave 0 the block's
-  // lse and wave 1 its D (rows past N repeat the last row; never used)
+  // each wave copies an eighth of each 16 KiB tile (2 DMAs of 1 KiB) and the block's lse
+  // and D (every wave the same 256 bytes, so that each issues six DMAs per step; rows
+  // past N repeat the last row and are never used)
   int lo16 = (w * 2 * 64 + l) * 16, lo4 = l * 4;
-  auto issue = [&](uint16_t* a, uint16_t* b, float* sl, float* ss, int i) {
+  auto issue = [&](DkvSlot& z, int i) {
     asm volatile("" : "+v"(lo16), "+v"(lo4));
     const size_t tb = ((size_t)bh * Nb + i) * kTrTile * 2;  // bytes
     const char* s0 = (const char*)qh_ + tb;
@@ -518,20 +555,22 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
 #pragma unroll
     for (int cc = 0; cc < 2; cc++) {
       const int ld = (w * 2 + cc) * 512;
-      __builtin_amdgcn_global_load_lds((const void*)(s0 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(a + ld), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(s1 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(b + ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(s0 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(z.qh + ld), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(s1 + (uint32_t)lo16 + cc * 1024), (lds_ptr_t)(z.dh + ld), 16, 0, 0);
     }
     const size_t r0 = (size_t)bh * N + (size_t)kBlk * i;
     const int nrow = min(kBlk, N - kBlk * i);
     const uint32_t off4 = (uint32_t)min(lo4, 4 * (nrow - 1));
-    if (w == 0) __builtin_amdgcn_global_load_lds((const void*)((const char*)(lse + r0) + off4), (lds_ptr_t)sl, 4, 0, 0);
-    if (w == 1) __builtin_amdgcn_global_load_lds((const void*)((const char*)(dsum + r0) + off4), (lds_ptr_t)ss, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)(lse + r0) + off4), (lds_ptr_t)z.L, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)(dsum + r0) + off4), (lds_ptr_t)z.S, 4, 0, 0);
   };
   uint32_t to0, to1;
   tok_offsets(l, to0, to1);
   // Q^T and dO^T (tokens as the reduction index) come from the same tiles through
   // transposing reads
-  auto compute = [&](const uint16_t* a, const uint16_t* b, const float* sl, const float* ss, int i) {
+  auto compute = [&](const DkvSlot& z, int i) {
+    const uint16_t *a = z.qh, *b = z.dh;
+    const float *sl = z.L, *ss = z.S;
     const int ni = block_len(i, N);
     v16f s_ = (v16f){}, dp = (v16f){};
 #pragma unroll
@@ -571,34 +610,67 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       const v8bf pb = pack8(&p[8 * t]);
+      v8bf op[4];
+      tok_ops4(src, to0, to1, qt, t, op);
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(tok_op(src, to0, to1, qt, ct, t), pb, acc[ct]);
+      for (int ct = 0; ct < 4; ct++) acc[ct] = mfma(op[ct], pb, acc[ct]);
     }
   };
 
-  int icur = next_set(mrow, nw, 0);
-  if (icur >= 0) issue(sQh0, sDh0, sL0, sS0, icur);
-  while (icur >= 0) {
-    int inext = next_set(mrow, nw, icur + 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (inext >= 0) issue(sQh1, sDh1, sL1, sS1, inext);
-    compute(sQh0, sDh0, sL0, sS0, icur);
-    icur = inext;
-    if (icur < 0) break;
-    inext = next_set(mrow, nw, icur + 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (inext >= 0) issue(sQh0, sDh0, sL0, sS0, inext);
-    compute(sQh1, sDh1, sL1, sS1, icur);
-    icur = inext;
+  // Ring of four slots, one LDS object each: step n (the n-th query block that keeps
+  // this key block) lives in slot n % 4; at the top of step n the DMAs of steps n + 1
+  // and n + 2 (six each) may still be in flight. Past the last step the last block is
+  // fetched again into the free slot, so that every step issues six DMAs.
+  // the row goes to LDS first: a global load inside the loop would wait for every DMA
+  // in flight (loads complete in order)
+  for (int e = threadIdx.x; e < nw; e += 512) s_mrow[e] = mrow[e];
+  __syncthreads();
+  int cnt = 0;
+  for (int wi = 0; wi < nw; wi++) cnt += __popc(s_mrow[wi]);
+  auto next_blk = [&](int cur) {
+    const int nx = next_set(s_mrow, nw, cur + 1);
+    return nx < 0 ? cur : nx;
+  };
+  constexpr int kWaitImm = 12 | (7 << 4) | (15 << 8);  // vmcnt(12)
+  int blk[4];
+  int ia = 0;
+  auto phase = [&](DkvSlot& cur, DkvSlot& prev, int k) {
+    __builtin_amdgcn_s_waitcnt(kWaitImm);
+    // step's slot complete from every wave; the previous step's slot free. A plain
+    // barrier: a fence would wait for every DMA.
+    asm volatile("s_barrier" ::: "memory");
+    ia = next_blk(ia);
+    issue(prev, ia);
+    blk[(k + 3) & 3] = ia;
+    compute(cur, blk[k]);
+  };
+  if (cnt > 0) {
+    ia = next_set(s_mrow, nw, 0);
+    blk[0] = ia;
+    issue(z0, ia);
+    ia = next_blk(ia);
+    blk[1] = ia;
+    issue(z1, ia);
+    ia = next_blk(ia);
+    blk[2] = ia;
+    issue(z2, ia);
+    int n = 0;
+    for (; n + 4 <= cnt; n += 4) {
+      phase(z0, z3, 0);
+      phase(z1, z0, 1);
+      phase(z2, z1, 2);
+      phase(z3, z2, 3);
+    }
+    if (n < cnt) phase(z0, z3, 0);
+    if (n + 1 < cnt) phase(z1, z0, 1);
+    if (n + 2 < cnt) phase(z2, z1, 2);
   }
 
   // the query-tile-1 waves hand their partial sums to the query-tile-0 waves through LDS
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // 16 KiB per (role, key half)
-  float* red = (float*)(role == 0 ? (kh == 0 ? sQh0 : sDh0) : (kh == 0 ? sQh1 : sDh1));
+  float* red = (float*)(role == 0 ? (kh == 0 ? z0.qh : z0.dh) : (kh == 0 ? z1.qh : z1.dh));
   if (qt == 1) {
 #pragma unroll
     for (int ct = 0; ct < 4; ct++)
