@@ -82,7 +82,9 @@ __device__ __forceinline__ v8i softmax_tile(RowState& st, v16i (&S)[2], float a)
         const int sv = S[tt][4 * v4 + e];
         p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sv, a, bias));
       }
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+      // the first conversion keeps the high half of its third operand, which the second
+      // overwrites: any register will do (p[0]'s bits; a constant would cost a move)
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
       pb[4 * tt + v4] = wd;
     }
