@@ -153,6 +153,10 @@ def main():
     ms_staged = start2.elapsed_time(stop2) / args.steps
     per_kernel = {n: sum(ev[s][c].elapsed_time(ev[s][c + 1]) for s in range(args.steps)) / args.steps
                   for c, n in enumerate(names)}
+    # per-pass and per-sparse-kernel spread over the staged passes (median and minimum)
+    pass_ms = sorted(ev[s][0].elapsed_time(ev[s][len(calls)]) for s in range(args.steps))
+    ci = names.index("sparse_attn")
+    sa_each = sorted(ev[s][ci].elapsed_time(ev[s][ci + 1]) for s in range(args.steps))
 
     # the staged pass computes exactly what sagesla_fwd computes
     same = bool(torch.equal(out, fwd_out))
@@ -200,6 +204,8 @@ def main():
         "sparse_attn_frac_of_mfma_peak": round(achieved / PEAK_INT8_FP8_TOPS, 4),
         "kernel_ms": {n: round(t, 4) for n, t in per_kernel.items()},
         "staged_ms_per_step": round(ms_staged, 4),
+        "staged_pass_ms_median_min": [round(pass_ms[len(pass_ms) // 2], 4), round(pass_ms[0], 4)],
+        "sparse_attn_ms_median_min": [round(sa_each[len(sa_each) // 2], 4), round(sa_each[0], 4)],
         "staged_equals_fwd": same,
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_FP8_TOPS,
