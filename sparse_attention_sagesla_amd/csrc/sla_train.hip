@@ -520,6 +520,7 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
                                                            int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ __attribute__((aligned(1024))) DkvSlot z0, z1, z2, z3;
   __shared__ uint32_t s_mrow[kMaxMaskWords];  // this key block's kept-by row (Nb <= 32 * kMaxMaskWords)
+  __shared__ float s_px[4 * 16 * 64];           // P of each (key half, query half), fp32
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
   const int bh = tile / Nb, j = tile % Nb;
@@ -568,43 +569,51 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
   tok_offsets(l, to0, to1);
   // Q^T and dO^T (tokens as the reduction index) come from the same tiles through
   // transposing reads
+  // The dV waves form S and P; P goes to the dK waves of the same (key half, query half)
+  // through LDS (fp32, lane order), so that S is formed once per pair and each wave does
+  // 16 products per step. A second barrier per step separates the write from the reads.
   auto compute = [&](const DkvSlot& z, int i) {
     const uint16_t *a = z.qh, *b = z.dh;
     const float *sl = z.L, *ss = z.S;
     const int ni = block_len(i, N);
-    v16f s_ = (v16f){}, dp = (v16f){};
+    float* px = s_px + (kh * 2 + qt) * 16 * 64;
+    float p[16];
+    v16f dp = (v16f){};
+    if (role == 0) {
+      v16f s_ = (v16f){};
 #pragma unroll
-    for (int s = 0; s < 8; s++) s_ = mfma(hd_op(a, qt, s, l), kop[s], s_);
-    if (role == 1) {
+      for (int s = 0; s < 8; s++) s_ = mfma(hd_op(a, qt, s, l), kop[s], s_);
+      // registers x hold query rows 32qt + 8(x/4) + 4g + x%4 of the block
+#pragma unroll
+      for (int x4 = 0; x4 < 4; x4++) {
+        const float4 L4 = *(const float4*)(sl + 32 * qt + 8 * x4 + 4 * g);
+        const float Lq[4] = {L4.x, L4.y, L4.z, L4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) p[4 * x4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[4 * x4 + e], c, -Lq[e]));
+      }
+      if (ni < kBlk) {  // the partial last query block: rows past its end drop out
+#pragma unroll
+        for (int x = 0; x < 16; x++)
+          if (32 * qt + 8 * (x >> 2) + 4 * g + (x & 3) >= ni) p[x] = 0.f;
+      }
+#pragma unroll
+      for (int x = 0; x < 16; x++) px[x * 64 + l] = p[x];
+    } else {
 #pragma unroll
       for (int s = 0; s < 8; s++) dp = mfma(hd_op(b, qt, s, l), vop[s], dp);
     }
-    // registers x hold query rows 32qt + 8(x/4) + 4g + x%4 of the block
-    float p[16];
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // P of this step written
+    if (role == 1) {
 #pragma unroll
-    for (int x4 = 0; x4 < 4; x4++) {
-      const int q0 = 32 * qt + 8 * x4 + 4 * g;
-      const float4 L4 = *(const float4*)(sl + q0);
-      const float Lq[4] = {L4.x, L4.y, L4.z, L4.w};
-      float Dq[4] = {0.f, 0.f, 0.f, 0.f};
-      if (role == 1) {
-        const float4 D4 = *(const float4*)(ss + q0);
-        Dq[0] = D4.x;
-        Dq[1] = D4.y;
-        Dq[2] = D4.z;
-        Dq[3] = D4.w;
+      for (int x4 = 0; x4 < 4; x4++) {
+        const float4 D4 = *(const float4*)(ss + 32 * qt + 8 * x4 + 4 * g);
+        const float Dq[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int x = 4 * x4 + e;
+          p[x] = px[x * 64 + l] * (dp[x] - Dq[e]);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int x = 4 * x4 + e;
-        const float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[x], c, -Lq[e]));
-        p[x] = role == 0 ? pe : pe * (dp[x] - Dq[e]);
-      }
-    }
-    if (ni < kBlk) {  // the partial last query block: rows past its end drop out
-#pragma unroll
-      for (int x = 0; x < 16; x++)
-        if (32 * qt + 8 * (x >> 2) + 4 * g + (x & 3) >= ni) p[x] = 0.f;
     }
     const uint16_t* src = role == 0 ? b : a;  // dO^T for dV, Q^T for dK
 #pragma unroll
