@@ -245,7 +245,8 @@ __global__ __launch_bounds__(256, 2) void sla_fwd_kernel(const uint16_t* __restr
     v16f acc = (v16f){};
 #pragma unroll
     for (int s = 0; s < 8; s++) acc = mfma(hd_op(ck, kh, s, l), qop[s], acc);
-    if (nj < 32 * kh + 32) {  // the partial last block: keys past its end drop out
+    if (__builtin_expect(nj < 32 * kh + 32, 0)) {  // the partial last block: keys past its end drop out
+      asm volatile("" ::: "memory");  // a real branch: the masking is not run on full blocks
 #pragma unroll
       for (int v = 0; v < 16; v++)
         if (32 * kh + 8 * (v >> 2) + 4 * g + (v & 3) >= nj) acc[v] = -INFINITY;
@@ -429,7 +430,8 @@ __global__ __launch_bounds__(256, 2) void sla_bwd_dq_kernel(const uint16_t* __re
     float ds[16];
 #pragma unroll
     for (int x = 0; x < 16; x++) ds[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[x], c, -L)) * (dp[x] - D);
-    if (nj < kBlk) {
+    if (__builtin_expect(nj < kBlk, 0)) {
+      asm volatile("" ::: "memory");  // a real branch: the masking is not run on full blocks
 #pragma unroll
       for (int x = 0; x < 16; x++)
         if (32 * kt + 8 * (x >> 2) + 4 * g + (x & 3) >= nj) ds[x] = 0.f;
@@ -591,7 +593,8 @@ __global__ __launch_bounds__(512) void sla_bwd_dkdv_kernel(const uint16_t* __res
 #pragma unroll
         for (int e = 0; e < 4; e++) p[4 * x4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s_[4 * x4 + e], c, -Lq[e]));
       }
-      if (ni < kBlk) {  // the partial last query block: rows past its end drop out
+      if (__builtin_expect(ni < kBlk, 0)) {  // the partial last query block: rows past its end drop out
+        asm volatile("" ::: "memory");  // a real branch: the masking is not run on full blocks
 #pragma unroll
         for (int x = 0; x < 16; x++)
           if (32 * qt + 8 * (x >> 2) + 4 * g + (x & 3) >= ni) p[x] = 0.f;
