@@ -20,11 +20,13 @@ from _helpers import cos, mask_mismatch
 pytestmark = pytest.mark.gpu
 
 NAMES = ["wan1.3b-480p", "wan14b-480p", "wan14b-720p", "i2v-a14b-720p", "i2v-a14b-720p-dense",
-         "long-sequence", "wan14b-720p-topk0.05", "wan14b-720p-topk0.25"]
+         "long-sequence", "max-length", "wan14b-720p-topk0.05", "wan14b-720p-topk0.25"]
 # one head of a 2^18-token sequence (4096 key blocks): several passes of the union and
 # selection kernels and union lists longer than one LDS chunk
 EXTRA = {"long-sequence": synth.scaled(synth.CONFIGS["wan14b-720p"], H=1, grid=(16, 64, 256), seed=41,
                                        name="long-sequence"),
+         # the longest sequence the library accepts: 2^20 tokens, 16384 key blocks, k_sel = 1639
+         "max-length": synth.scaled(synth.CONFIGS["wan14b-720p"], H=1, grid=(16, 256, 256), seed=42, name="max-length"),
          # the ends of the top-k sweep the benchmark reports (the pages recommend 0.1 - 0.15)
          "wan14b-720p-topk0.05": synth.scaled(synth.CONFIGS["wan14b-720p"], topk=0.05, name="wan14b-720p-topk0.05"),
          "wan14b-720p-topk0.25": synth.scaled(synth.CONFIGS["wan14b-720p"], topk=0.25, name="wan14b-720p-topk0.25")}
