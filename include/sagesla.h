@@ -209,10 +209,12 @@ typedef enum {
     SAGESLA_SLA_WS_LSE = SAGESLA_WS_COUNT, /* fp32 [BH][N] row log-sum-exp of the scores
                                               s/sqrt(d), base 2: log2 sum_j 2^(s_ij log2(e)/sqrt(d)) */
     SAGESLA_SLA_WS_OS,    /* fp32 [BH][N][d]     O_s                                      */
-    SAGESLA_SLA_WS_KT,    /* bf16 [BH][Nb][8192] K token-reduction tiles (below)          */
-    SAGESLA_SLA_WS_VT,    /* bf16 [BH][Nb][8192] V token-reduction tiles                  */
-    SAGESLA_SLA_WS_QT,    /* bf16 [BH][Nb][8192] Q token-reduction tiles (backward)       */
-    SAGESLA_SLA_WS_DOT,   /* bf16 [BH][Nb][8192] dO token-reduction tiles (backward)      */
+    SAGESLA_SLA_WS_KT,    /* bf16 [BH][Nb][8192] tiles (below): K head-dim-reduction (forward),
+                             phi(q) token-reduction (backward, linear part)                */
+    SAGESLA_SLA_WS_VT,    /* bf16 [BH][Nb][8192] V token-reduction (forward); V head-dim-
+                             reduction, then O_l token-reduction (backward)                */
+    SAGESLA_SLA_WS_QT,    /* bf16 [BH][Nb][8192] du token-reduction tiles (backward, linear) */
+    SAGESLA_SLA_WS_DOT,   /* bf16 [BH][Nb][8192] dO token-reduction tiles (backward, dW)  */
     SAGESLA_SLA_WS_DSUM,  /* fp32 [BH][N]        D = rowsum(dO * O_s) (backward)          */
     SAGESLA_SLA_WS_MASK,  /* u32 [BH][Nb][ceil(Nb/32)] bit i of row j: query block i keeps j */
     SAGESLA_SLA_WS_H0,    /* bf16 [BH][Nb][8192] head-dim-reduction tiles (below) of K, then of Q */
@@ -226,10 +228,11 @@ typedef enum {
 } sagesla_sla_ws_region;
 /* Token-reduction tiles of a [N][d] tensor X, per 64-token block: element
  * ((tt*4 + ct)*2 + t)*512 + l*8 + e holds X[32*tt + 16*t + 8*(e/4) + 4*g + e%4][32*ct + r]
- * (tt, t in 0..1, ct in 0..3, e in 0..7; tokens past N are 0). Head-dim-reduction tiles:
- * element (tt*8 + s)*512 + l*8 + e holds X[32*tt + r][16*s + 8*g + e] (s in 0..7). The
- * forward leaves K's head-dim-reduction tiles in SAGESLA_SLA_WS_KT and the backward
- * rewrites the tile regions. */
+ * (l in 0..63, r = l%32, g = l/32; tt, t in 0..1, ct in 0..3, e in 0..7; tokens past N are
+ * 0). Head-dim-reduction tiles: element (tt*8 + s)*512 + p*8 + e, with
+ * p = l ^ (4*(s%2) + 8*(l/32)), holds X[32*tt + r][16*s + 8*g + e] (s in 0..7). The forward
+ * leaves K's head-dim-reduction tiles in SAGESLA_SLA_WS_KT and the backward rewrites the
+ * tile regions. */
 
 /* Bytes of the training workspace (linear = 0 when proj will be NULL). Host only. */
 sagesla_status sagesla_sla_workspace_size(int B, int H, int N, int d, int block, double topk,
