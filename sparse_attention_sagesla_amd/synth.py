@@ -79,10 +79,13 @@ CONFIGS = {
 
 
 def scaled(cfg: Config, H: int | None = None, grid: tuple | None = None, seed: int | None = None,
-           topk: float | None = None, name: str | None = None, linear: bool | None = None) -> Config:
+           topk: float | None = None, name: str | None = None, linear: bool | None = None,
+           B: int | None = None) -> Config:
     """A copy of ``cfg`` with fewer heads / a smaller grid (same recipe), for quick tests."""
     from dataclasses import replace
     kw = {}
+    if B is not None:
+        kw["B"] = B
     if H is not None:
         kw["H"] = H
     if grid is not None:

@@ -40,6 +40,8 @@ CASES = {
     "lin-two-groups": (synth.CONFIGS["wan1.3b-480p"], dict(H=1, grid=(3, 10, 640), topk=0.1, seed=59, linear=True)),
     # every block kept: no linear part, dW = 0
     "lin-dense": (synth.CONFIGS["tiny"], dict(H=1, grid=(1, 3, 50), topk=1.0, seed=60, linear=True)),
+    # two sequences in the batch (dW sums over both)
+    "lin-batch2": (synth.CONFIGS["wan1.3b-480p"], dict(B=2, H=2, grid=(1, 5, 60), topk=0.3, seed=61, linear=True)),
 }
 
 
@@ -76,27 +78,28 @@ def test_sla_train_parity(name):
     N = cfg.N
     wb = None if proj is None else _bf16(proj)
     dw_ref = 0.0
-    for h in range(cfg.H):
-        qb, kb, vb, db = (_bf16(t[0, h]) for t in (q, k, v, dout))
+    for b, h in [(b, h) for b in range(cfg.B) for h in range(cfg.H)]:
+        bh = b * cfg.H + h
+        qb, kb, vb, db = (_bf16(t[b, h]) for t in (q, k, v, dout))
         ora = O.sagesla_head(qb, kb, vb, wb, cfg.topk, quant=False)
-        gi = views["idx"][h].cpu().numpy()
+        gi = views["idx"][bh].cpu().numpy()
         assert all(set(gi[r].tolist()) == set(ora["idx"][r].tolist()) for r in range(len(gi))), "kept sets differ"
         ref = G.sla_backward(_f64(qb), _f64(kb), _f64(vb), None if wb is None else _f64(wb), ora["idx"], _f64(db))
         if ref["dw"] is not None:
             dw_ref = dw_ref + ref["dw"]
-        o = out[0, h].float().cpu().numpy()
-        os_ = views["os"][h].float().cpu().numpy()
+        o = out[b, h].float().cpu().numpy()
+        os_ = views["os"][bh].float().cpu().numpy()
         for got, want, what in ((o, ref["out"], "out"), (os_, ref["out_s"], "O_s")):
             c, e = cos(got, want), float(np.abs(got - want).max())
-            print("  head %d %s: cos %.7f maxabs %.3g" % (h, what, c, e))
+            print("  seq %d head %d %s: cos %.7f maxabs %.3g" % (b, h, what, c, e))
             # the linear part's states are bf16 (as in the inference forward): 2e-2 there
             assert c >= 0.9999 and e <= (2e-2 if what == "out" and wb is not None else 1e-2), (what, c, e)
-        lse = views["lse"][h].cpu().numpy().astype(np.float64) * np.log(2.0)
+        lse = views["lse"][bh].cpu().numpy().astype(np.float64) * np.log(2.0)
         assert np.abs(lse - ref["lse"]).max() <= 1e-4
         for got, want, what in ((dq, ref["dq"], "dQ"), (dk, ref["dk"], "dK"), (dv, ref["dv"], "dV")):
-            g = got[0, h].cpu().numpy().astype(np.float64)
+            g = got[b, h].cpu().numpy().astype(np.float64)
             c, e, m = cos(g, want), float(np.abs(g - want).max()), float(np.abs(want).max())
-            print("  head %d %s: cos %.7f maxabs %.3g (max|g| %.3g)" % (h, what, c, e, m))
+            print("  seq %d head %d %s: cos %.7f maxabs %.3g (max|g| %.3g)" % (b, h, what, c, e, m))
             assert c >= 0.999 and e <= 2e-2 * m, (what, c, e, m)
     assert N == q.shape[2]
     if proj is not None:
