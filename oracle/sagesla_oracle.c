@@ -322,9 +322,12 @@ int32_t oracle_dot_i8(const int8_t *a, const int8_t *b, int d)
  * on the kept blocks): for each kept key block j in the row's processing order,
  *   S = q8 . k8 (int32), a = (s_q[i]*s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
  *   x = fp32(S)*a, m' = max(m, max x), alpha = exp2f(m - m'),
- *   w = exp2f(fmaf(fp32(S), a, L - m')) with L = fp32(log2(448)), i.e. w = 448 p for
- *     p = 2^(x - m') (the exponent argument is formed in fp32 exactly as the FP8 code
- *     decision is taken on the GPU),
+ *   w = exp2f(fmaf(F, a, c)) with F = 1.5*2^23 + S (an integer below 2^24, exact in
+ *     fp32), c = (L - m') - fp32(1.5*2^23 * a) and L = fp32(log2(448)); in exact
+ *     arithmetic F*a + c = S*a + L - m', so w = 448 p for p = 2^(x - m') up to the fp32
+ *     roundings of c and of the fused product (the exponent argument is formed in fp32
+ *     exactly as the FP8 code decision is taken on the GPU, whose integer accumulators
+ *     start from the bit pattern of 1.5*2^23),
  *   p8 = e4m3(w) (saturating),
  *   l = l*alpha + sum dec(p8), acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
  * Output row: acc[c] * sv[c] / l, i.e. the average of the dequantized V rows weighted by
@@ -361,12 +364,12 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
             }
             float mn = m > mb ? m : mb;
             float alpha = exp2f(m - mn);
-            float bias = L - mn;
+            float c = (L - mn) - 12582912.0f * a;
             l *= (double)alpha;
             for (int c = 0; c < d; c++)
                 acc[c] *= (double)alpha;
             for (int t = 0; t < nk; t++) {
-                double pq = dec8(oracle_e4m3_encode(exp2f(fmaf(sf[t], a, bias))));
+                double pq = dec8(oracle_e4m3_encode(exp2f(fmaf(12582912.0f + sf[t], a, c))));
                 l += pq;
                 const uint8_t *vrow = v8 + (size_t)(j * blk + t) * d;
                 for (int c = 0; c < d; c++)
