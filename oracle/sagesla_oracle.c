@@ -17,8 +17,8 @@
  *    attention branch (bonega.ai blog, SLA paragraph; tiemojia.cn article, 2.2.1).
  *  - SageAttention quantizes to 8-bit integers (news.qq.com, "First key"); outliers
  *    are smoothed into the normal range before quantization and restored after
- *    (news.qq.com, "Third key"); each small block shares one scale factor
- *    (news.qq.com, "Third key").
+ *    (news.qq.com, "Third key"); every small block is quantized with a single
+ *    scale of its own (news.qq.com, "Third key").
  * The pages give no formulas. Every step below that they leave open follows one
  * stated reading (block granularity 64, mean pooling, scores qbar.kbar/sqrt(d),
  * ceil(topk*Nb) blocks per query block, K-mean smoothing, per-block INT8 Q/K,
@@ -130,7 +130,7 @@ static int block_len(int i, int N, int blk)
 
 /*
  * Number of key blocks kept per query block: the Top-K ratio applied to the number of
- * key blocks, rounded up, at least 1 and at most all (reading of "keep the top 10 %",
+ * key blocks, rounded up, at least 1 and at most all (reading of keeping the top tenth,
  * news.qq.com, "First key"). The 1e-9 guards products such as 0.1*30 that land a hair
  * above an integer in binary.
  */
@@ -258,7 +258,7 @@ static int8_t q_int8(float x, float inv)
 
 /*
  * Per-block symmetric INT8 of fp32 values x: [N][d] (one scale per block of blk tokens
- * over all d channels; "each small block shares one scale factor", news.qq.com,
+ * over all d channels; one scale per small block, news.qq.com,
  * "Third key"). amax over the valid tokens; inv = 127/amax, scale = amax/127 (fp32
  * IEEE divisions); amax = 0 gives zero codes and scale 0. Padded rows are 0.
  * q8: [Nb*blk][d], scale: [Nb].
