@@ -11,8 +11,9 @@
  *
  * The pages give no formulas. This library computes, per (batch, head):
  *   1. pooling + selection: mean-pool Q and K over 64-token blocks, score block pairs
- *      s_ij = Qbar_i . Kbar_j / sqrt(d), keep the ksel = ceil(topk * Nb) best key blocks
- *      of every query block (ties: lower index), stored ascending;
+ *      s_ij = Qbar_i . Kbar_j / sqrt(d) (fp64, compared exactly), keep the
+ *      ksel = ceil(topk * Nb) best key blocks of every query block (ties: lower index),
+ *      stored best first (highest score, lowest index on ties), then the rest ascending;
  *   2. quantization: K smoothed by its per-channel mean over all tokens; Q and K to INT8
  *      per 64-token block (scale amax/127, round half to even); V to FP8 e4m3 per
  *      channel (scale amax/448);
@@ -70,7 +71,7 @@ enum {
     SAGESLA_WS_K8,        /* int8 [BH][Nb][8192] smoothed-K codes, MFMA operand order      */
     SAGESLA_WS_SK,        /* fp32 [BH][Nb]      K block scales                             */
     SAGESLA_WS_V8,        /* e4m3 [BH][Nb][8192] V codes, MFMA operand order               */
-    SAGESLA_WS_IDX,       /* int32 [BH][Nb][ksel] kept key blocks, ascending               */
+    SAGESLA_WS_IDX,       /* int32 [BH][Nb][ksel] kept key blocks: best first, then ascending */
     SAGESLA_WS_HS,        /* bf16 [BH][Nb][129][d] state S_j: rows c<128 = H_j^T, row 128 = z_j */
     SAGESLA_WS_HPART,     /* fp32 [BH][Nc][129][d] sums of 16 consecutive S_j (linear)      */
     SAGESLA_WS_HTOT,      /* fp32 [BH][129][d]  sum of all S_j                  (linear)   */
@@ -94,6 +95,27 @@ enum {
 int sagesla_version(void);
 const char *sagesla_status_string(sagesla_status s);
 
+/* Tensor descriptors for sagesla_fwd_tensors: element type, rank, sizes and strides (in
+ * elements). The library accepts only contiguous row-major tensors (a dimension of size 1
+ * may carry any stride) of the element type each argument needs; anything else returns
+ * SAGESLA_ERR_INVALID_ARGUMENT before any work is enqueued. */
+typedef enum {
+    SAGESLA_BF16 = 0,
+    SAGESLA_F32 = 1,
+    SAGESLA_I8 = 2,
+    SAGESLA_FP8E4M3 = 3,
+    SAGESLA_I32 = 4,
+    SAGESLA_U8 = 5
+} sagesla_dtype;
+
+typedef struct {
+    void *data;          /* device pointer, 16-byte aligned */
+    sagesla_dtype dtype;
+    int ndim;            /* 1..4 */
+    int64_t shape[4];
+    int64_t stride[4];
+} sagesla_tensor;
+
 /* Number of kept key blocks per query block: clamp(ceil(topk*Nb - 1e-9), 1, Nb). */
 sagesla_status sagesla_ksel(int N, int block, double topk, int *ksel);
 
@@ -114,6 +136,15 @@ sagesla_status sagesla_workspace_layout(int B, int H, int N, int d, int block, d
 sagesla_status sagesla_fwd(const void *q, const void *k, const void *v, const void *proj,
                            int B, int H, int N, int d, double topk, int block, void *out,
                            void *workspace, size_t workspace_bytes, sagesla_stream_t stream);
+
+/* The same forward with tensor descriptors: q, k, v, out bf16 [B, H, N, d]; proj bf16
+ * [d, d] or NULL (linear branch off); workspace u8 [bytes]. Each descriptor's type, rank,
+ * shape and contiguity are checked first (SAGESLA_ERR_INVALID_ARGUMENT on a mismatch);
+ * then the call is sagesla_fwd. */
+sagesla_status sagesla_fwd_tensors(const sagesla_tensor *q, const sagesla_tensor *k,
+                                   const sagesla_tensor *v, const sagesla_tensor *proj, double topk,
+                                   int block, sagesla_tensor *out, const sagesla_tensor *workspace,
+                                   sagesla_stream_t stream);
 
 /* ---- producer-side fusion -------------------------------------------------------------
  * The pages fuse the rewritten LayerNorm/RMSNorm kernels with their neighbours (news.qq.com
@@ -136,35 +167,76 @@ sagesla_status sagesla_fwd_prepared(const void *q, const void *k, const void *v,
                                     void *workspace, size_t workspace_bytes,
                                     sagesla_stream_t stream);
 
-/* ---- stages ("friends"): the same conventions; buffers as in the workspace table ---- */
+/* ---- stages ("friends"): the same conventions; buffers as in the workspace table ----
+ * sagesla_fwd runs, in order: pool, head_stats, select, quant_kv (codes and, with the
+ * linear branch, its states), linear_total and linear_complement (linear branch only),
+ * sparse_attn. Three grouped calls cover the same launches by purpose:
+ * sagesla_pool_select = pool + head_stats + select, sagesla_quantize = quant_kv without
+ * states, sagesla_linear_states = quant_kv with states + linear_total. */
+
+/* Pooling and selection together: the block means of Q and K, the per-head K channel
+ * mean and V channel max, and the kept key blocks of every query block (SLA's quick
+ * scoring of how strongly blocks are related and its Top-K choice: news.qq.com
+ * explainer, "First key: attention"). Q's INT8 codes are made in the same pass, which
+ * reads Q anyway. Outputs as in the workspace table (QBAR, KBART, KSUM, VAMAXB, Q8, SQ,
+ * KMEAN, VAMAX, IDX). */
+sagesla_status sagesla_pool_select(const void *q, const void *k, const void *v, int B, int H, int N,
+                                   int d, int block, double topk, void *qbar, void *kbart,
+                                   void *ksum, void *vamax_blk, void *q8, void *sq, void *kmean,
+                                   void *vamax, void *idx, sagesla_stream_t stream);
+
+/* SageAttention's quantization of K and V (news.qq.com explainer, "First key" and "Third
+ * key": 8-bit data, outliers smoothed before quantizing, one scale per small block): K
+ * minus its channel mean to INT8 per 64-token block, V to FP8 e4m3 per channel. */
+sagesla_status sagesla_quantize(const void *k, const void *v, const void *kmean,
+                                const void *vamax, int B, int H, int N, int d, int block, void *k8,
+                                void *sk, void *v8, sagesla_stream_t stream);
+
+/* The linear-attention states of every key block and their totals (the SLA branch that
+ * carries the blocks not computed exactly: bonega.ai blog, SLA paragraph; tiemojia.cn
+ * article, 2.2.1). They are formed in the same pass over K and V as the K/V codes, so this
+ * call fills k8, sk, v8 too (as sagesla_quantize would), then hs, hpart and htot. */
+sagesla_status sagesla_linear_states(const void *k, const void *v, const void *kmean,
+                                     const void *vamax, int B, int H, int N, int d, int block,
+                                     void *k8, void *sk, void *v8, void *hs, void *hpart,
+                                     void *htot, sagesla_stream_t stream);
 
 /* Block pooling of Q and K (fp64 sums of the bf16 inputs), K block sums, V block max,
- * and INT8 quantization of Q per block. */
+ * and INT8 quantization of Q per block (pooling for SLA's quick block scoring and
+ * SageAttention's per-block INT8: news.qq.com explainer, "First key" and "Third key"). */
 sagesla_status sagesla_pool(const void *q, const void *k, const void *v, int B, int H, int N,
                             int d, int block, void *qbar, void *kbart, void *ksum,
                             void *vamax_blk, void *q8, void *sq, sagesla_stream_t stream);
 
-/* Per-head reductions: K channel mean (from block sums) and V channel max. */
+/* Per-head reductions: K channel mean (from block sums) and V channel max: the smoothing
+ * offset and the FP8 range of SageAttention's quantization (news.qq.com explainer, "Third
+ * key"). */
 sagesla_status sagesla_head_stats(const void *ksum, const void *vamax_blk, int B, int H, int N,
                                   int d, int block, void *kmean, void *vamax,
                                   sagesla_stream_t stream);
 
-/* Block scores (fp64) and top-ksel selection per query block. */
+/* Block scores (fp64) and top-ksel selection per query block (SLA's Top-K of the block
+ * scores: news.qq.com explainer, "First key"; kept list best first, then ascending). */
 sagesla_status sagesla_select(const void *qbar, const void *kbart, int B, int H, int N, int d,
                               int block, double topk, void *idx, sagesla_stream_t stream);
 
-/* K smoothing + INT8, V FP8, and (when hs != NULL) the linear-branch states S_j and
- * their 16-block fp32 partial sums. */
+/* K smoothing + INT8, V FP8 (news.qq.com explainer, "Third key"), and (when hs != NULL)
+ * the linear-branch states S_j and their 16-block fp32 partial sums (bonega.ai blog, SLA
+ * paragraph). */
 sagesla_status sagesla_quant_kv(const void *k, const void *v, const void *kmean,
                                 const void *vamax, int B, int H, int N, int d, int block,
                                 void *k8, void *sk, void *v8, void *hs, void *hpart,
                                 sagesla_stream_t stream);
 
-/* Totals S_total = sum_j S_j (fp32) from the partial sums. */
+/* Totals S_total = sum_j S_j (fp32) from the partial sums: the linear branch's state over
+ * all key blocks, from which each query block's complement is taken (tiemojia.cn article,
+ * 2.2.1). */
 sagesla_status sagesla_linear_total(const void *hpart, int B, int H, int N, int d, int block,
                                     void *htot, sagesla_stream_t stream);
 
-/* Linear branch: per group of 256 query blocks the union of their kept sets (ulist,
+/* Linear branch (the blocks SLA does not compute exactly go to linear attention:
+ * bonega.ai blog, SLA paragraph; tiemojia.cn article, 2.2.1): per group of 256 query
+ * blocks the union of their kept sets (ulist,
  * umask, ucount), the complement states hc = S_total - sum_kept S_j (a 0/1-mask product
  * on the matrix cores), and y = O_l W with O_l = phi(q) H^c / (phi(q) . z^c). When more
  * than half the blocks are kept (2 ksel > Nb) the lists and masks describe the blocks
@@ -175,8 +247,9 @@ sagesla_status sagesla_linear_complement(const void *q, const void *idx, const v
                                          void *umask, void *ucount, void *hc, void *y,
                                          sagesla_stream_t stream);
 
-/* Sparse attention over the kept blocks and the epilogue out = O_s (+ y if y != NULL;
- * y is bf16 [B,H,N,d]). */
+/* Sparse attention over the kept blocks, on the 8-bit matrix cores (news.qq.com explainer,
+ * "First key": the exact part at 8-bit precision), and the epilogue out = O_s (+ y if
+ * y != NULL; y is bf16 [B,H,N,d]). */
 sagesla_status sagesla_sparse_attn(const void *q8, const void *sq, const void *k8,
                                    const void *sk, const void *v8, const void *vamax,
                                    const void *idx, const void *y, int B, int H, int N, int d,

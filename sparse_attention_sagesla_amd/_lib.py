@@ -26,7 +26,32 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_quant_kv", "sagesla_linear_total", "sagesla_linear_complement", "sagesla_sparse_attn",
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
            "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd",
-           "sagesla_prepare", "sagesla_fwd_prepared"]
+           "sagesla_prepare", "sagesla_fwd_prepared", "sagesla_fwd_tensors", "sagesla_pool_select",
+           "sagesla_quantize", "sagesla_linear_states"]
+
+# sagesla_dtype values and the sagesla_tensor descriptor
+DT_BF16, DT_F32, DT_I8, DT_FP8E4M3, DT_I32, DT_U8 = range(6)
+
+
+class Tensor(C.Structure):
+    _fields_ = [("data", C.c_void_p), ("dtype", C.c_int), ("ndim", C.c_int),
+                ("shape", C.c_int64 * 4), ("stride", C.c_int64 * 4)]
+
+
+_TORCH_DT = {torch.bfloat16: DT_BF16, torch.float32: DT_F32, torch.int8: DT_I8, torch.int32: DT_I32,
+             torch.uint8: DT_U8}
+
+
+def tensor_desc(t) -> Tensor:
+    """The sagesla_tensor descriptor of a torch tensor (element strides as torch has them)."""
+    d = Tensor()
+    d.data = t.data_ptr()
+    d.dtype = _TORCH_DT.get(t.dtype, DT_FP8E4M3 if t.dtype == getattr(torch, "float8_e4m3fn", None) else -1)
+    d.ndim = t.dim()
+    for a in range(t.dim()):
+        d.shape[a] = t.shape[a]
+        d.stride[a] = t.stride(a)
+    return d
 SLA_WS_REGIONS = WS_REGIONS + ["lse", "os", "kt", "vt", "qt", "dot", "dsum", "mask", "h0", "h1", "phq", "du", "ol", "ds", "dwp"]
 SLA_WS_COUNT = len(SLA_WS_REGIONS)
 
@@ -72,6 +97,11 @@ def lib():
             "sagesla_sla_bwd": (i32, [P] * 5 + dims + [f64, i32] + [P] * 5 + [sz, P]),
             "sagesla_prepare": (i32, [P, P, P, f64] + dims + [f64, i32, i32, P, P, P, P, sz, P]),
             "sagesla_fwd_prepared": (i32, [P, P, P, P] + dims + [f64, i32, P, P, sz, P]),
+            "sagesla_fwd_tensors": (i32, [C.POINTER(Tensor)] * 4 + [f64, i32, C.POINTER(Tensor),
+                                                                    C.POINTER(Tensor), P]),
+            "sagesla_pool_select": (i32, [P, P, P] + dims + [i32, f64] + [P] * 9 + [P]),
+            "sagesla_quantize": (i32, [P, P, P, P] + dims + [i32, P, P, P, P]),
+            "sagesla_linear_states": (i32, [P, P, P, P] + dims + [i32] + [P] * 6 + [P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)

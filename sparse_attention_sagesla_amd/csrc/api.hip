@@ -298,6 +298,94 @@ static sagesla_status run_fwd(const void* q, const void* k, const void* v, const
 
 extern "C" {
 
+// ---------------------------------------------------------------- tensor descriptors
+
+static bool t_contiguous(const sagesla_tensor* t) {
+  int64_t want = 1;
+  for (int a = t->ndim - 1; a >= 0; a--) {
+    if (t->shape[a] < 1) return false;
+    if (t->shape[a] > 1 && t->stride[a] != want) return false;
+    want *= t->shape[a];
+  }
+  return true;
+}
+
+static sagesla_status t_check(const sagesla_tensor* t, sagesla_dtype dtype, int ndim) {
+  if (!t || !t->data || t->dtype != dtype || t->ndim != ndim || !t_contiguous(t)) return SAGESLA_ERR_INVALID_ARGUMENT;
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_fwd_tensors(const sagesla_tensor* q, const sagesla_tensor* k, const sagesla_tensor* v,
+                                   const sagesla_tensor* proj, double topk, int block, sagesla_tensor* out,
+                                   const sagesla_tensor* workspace, sagesla_stream_t stream) {
+  sagesla_status s;
+  if ((s = t_check(q, SAGESLA_BF16, 4)) != SAGESLA_OK || (s = t_check(k, SAGESLA_BF16, 4)) != SAGESLA_OK ||
+      (s = t_check(v, SAGESLA_BF16, 4)) != SAGESLA_OK || (s = t_check(out, SAGESLA_BF16, 4)) != SAGESLA_OK ||
+      (s = t_check(workspace, SAGESLA_U8, 1)) != SAGESLA_OK)
+    return s;
+  for (int a = 0; a < 4; a++)
+    if (k->shape[a] != q->shape[a] || v->shape[a] != q->shape[a] || out->shape[a] != q->shape[a])
+      return SAGESLA_ERR_INVALID_ARGUMENT;
+  for (int a = 0; a < 4; a++)
+    if (q->shape[a] > INT32_MAX) return SAGESLA_ERR_INVALID_ARGUMENT;
+  const int B = (int)q->shape[0], H = (int)q->shape[1], N = (int)q->shape[2], d = (int)q->shape[3];
+  if (proj) {
+    if ((s = t_check(proj, SAGESLA_BF16, 2)) != SAGESLA_OK) return s;
+    if (proj->shape[0] != d || proj->shape[1] != d) return SAGESLA_ERR_INVALID_ARGUMENT;
+  }
+  return run_fwd(q->data, k->data, v->data, proj ? proj->data : nullptr, B, H, N, d, topk, block, out->data,
+                 workspace->data, (size_t)workspace->shape[0], stream, false);
+}
+
+// ---------------------------------------------------------------- grouped stages
+
+sagesla_status sagesla_pool_select(const void* q, const void* k, const void* v, int B, int H, int N, int d,
+                                   int block, double topk, void* qbar, void* kbart, void* ksum, void* vamax_blk,
+                                   void* q8, void* sq, void* kmean, void* vamax, void* idx,
+                                   sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, qbar, kbart, ksum, vamax_blk, q8, sq, kmean, vamax, idx})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, qbar, kbart, ksum, vamax_blk, q8, sq, st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_head_stats(ksum, vamax_blk, gm.BH, gm.N, gm.Nb, kmean, vamax, st)) != hipSuccess)
+    return from_hip(e);
+  return from_hip(launch_select(qbar, kbart, gm.BH, gm.Nb, gm.ksel, idx, st));
+}
+
+sagesla_status sagesla_quantize(const void* k, const void* v, const void* kmean, const void* vamax, int B, int H,
+                                int N, int d, int block, void* k8, void* sk, void* v8, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({k, v, kmean, vamax, k8, sk, v8})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_quant_kv(k, v, kmean, vamax, gm.BH, gm.N, gm.Nb, k8, sk, v8, nullptr, nullptr,
+                                  (hipStream_t)stream));
+}
+
+sagesla_status sagesla_linear_states(const void* k, const void* v, const void* kmean, const void* vamax, int B,
+                                     int H, int N, int d, int block, void* k8, void* sk, void* v8, void* hs,
+                                     void* hpart, void* htot, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({k, v, kmean, vamax, k8, sk, v8, hs, hpart, htot})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  const hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+  if ((e = launch_quant_kv(k, v, kmean, vamax, gm.BH, gm.N, gm.Nb, k8, sk, v8, hs, hpart, st)) != hipSuccess)
+    return from_hip(e);
+  return from_hip(launch_linear_total(hpart, gm.BH, gm.Nb, htot, st));
+}
+
+// ---------------------------------------------------------------- single stages
+
 sagesla_status sagesla_pool(const void* q, const void* k, const void* v, int B, int H, int N, int d, int block,
                             void* qbar, void* kbart, void* ksum, void* vamax_blk, void* q8, void* sq,
                             sagesla_stream_t stream) {

@@ -7,7 +7,7 @@
 //   S^c_i = S_total - sum_{j kept by i} S_j,
 // so its cost does not depend on how many blocks are left to the linear branch.
 // Neighbouring query blocks keep mostly the same key blocks, so the kept sums of a
-// group of 128 consecutive query blocks are one matrix product on the matrix cores:
+// group of 256 consecutive query blocks are one matrix product on the matrix cores:
 //   M[i][e] = sum_{u in union} C[i][u] * S_{union[u]}[e],  C = 0/1 kept mask,
 // over the union of the group's kept sets (each state row is read once per group).
 // phi is the softmax over the d channels of the raw bf16 row.

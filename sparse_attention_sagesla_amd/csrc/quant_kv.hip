@@ -3,8 +3,8 @@
 // SageAttention smooths outliers into range before quantizing and undoes the transform
 // afterwards (TurboDiffusion explainer, news.qq.com, "Third key"); for K this is the
 // subtraction of the per-channel mean over all tokens, which leaves softmax(q.k)
-// unchanged. Q and K share one scale per 64-token block ("each small block shares one
-// scale factor", same section); V is FP8 e4m3 with one scale per channel.
+// unchanged. Q and K take one scale per 64-token block (the page has every small block
+// share a single scale, same section); V is FP8 e4m3 with one scale per channel.
 // The linear half of SLA (bonega.ai blog, SLA paragraph; tiemojia.cn article, 2.2.1)
 // needs, per key block j, H_j = phi(K_j)^T V_j and z_j = colsum phi(K_j) with
 // phi = softmax over the d channels of the raw K row; they are computed here from the

@@ -2,29 +2,30 @@
 //
 // SLA keeps only the most strongly related pairs, a Top-K ratio of 0.1 (TurboDiffusion
 // explainer, news.qq.com, "First key: attention"; 0.1-0.15 recommended in "From
-// training to deployment"). Scores are s_ij = Qbar_i . Kbar_j / sqrt(d) in fp64, the
-// selection key is that score rounded to fp32, and equal keys prefer the lower key
-// index. The kept indices are written in processing order: the best block first
-// (highest key, lowest index on ties), then the others ascending, so that the attention
-// kernel's running maximum starts near its final value.
+// training to deployment"). Scores are s_ij = Qbar_i . Kbar_j / sqrt(d) in fp64, and the
+// selection compares those fp64 scores exactly (order-preserving 64-bit keys); equal
+// scores prefer the lower key index. The kept indices are written in processing order:
+// the best block first (highest score, lowest index on ties), then the others ascending,
+// so that the attention kernel's running maximum starts near its final value.
 #include "common.h"
 
 namespace sagesla {
 
 constexpr int kSelThreads = 256;
 
-// float -> uint32 with the same order (larger float -> larger integer)
-__device__ __forceinline__ uint32_t ord_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// double -> uint64 with the same order (larger double -> larger integer); -0 is taken
+// as +0 (adding +0 does that), so that equal scores give equal keys
+__device__ __forceinline__ uint64_t ord_key(double f) {
+  const uint64_t u = (uint64_t)__double_as_longlong(f + 0.0);
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
 
 // Scores of up to 8 query-block rows (qbar in LDS, fp64) against key blocks j0 + 256 q,
 // q < JT (JT <= 6): s = sum_c qbar[r][c] kbar[c][j] in channel order with fused multiply-adds,
-// divided by sqrt(d) (one rounding), and stored as order-preserving fp32 keys.
+// divided by sqrt(d) (one rounding), and stored as order-preserving 64-bit keys.
 template <int JT>
 __device__ __forceinline__ void score_pass(const double* __restrict__ kb, const double (*s_qb)[kD],
-                                           uint32_t* s_keys, int Nb, int nr, int j0) {
+                                           uint64_t* s_keys, int Nb, int nr, int j0) {
   const double inv_sqrt_d = 1.0 / sqrt((double)kD);
   double acc[JT][8];
 #pragma unroll
@@ -79,12 +80,12 @@ __device__ __forceinline__ void score_pass(const double* __restrict__ kb, const 
     if (j < Nb) {
 #pragma unroll
       for (int r = 0; r < 8; r++)
-        if (r < nr) s_keys[r * Nb + j] = ord_key((float)(acc[q][r] * inv_sqrt_d));
+        if (r < nr) s_keys[r * Nb + j] = ord_key(acc[q][r] * inv_sqrt_d);
     }
   }
 }
 
-// R query blocks of one head per workgroup (4 waves). Dynamic LDS: keys [R][Nb] uint32.
+// R query blocks of one head per workgroup (4 waves). Dynamic LDS: keys [R][Nb] uint64.
 // Phase 1: all threads score the R rows against every key block (4 key blocks per
 // thread in flight). Phase 2: one wave per row selects, with a wave-private histogram
 // and ballots (no workgroup barriers).
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
                                                              const double* __restrict__ kbart, int Nb,
                                                              int ksel, int R, int groups,
                                                              int32_t* __restrict__ idx) {
-  extern __shared__ uint32_t s_keys[];  // [R][Nb]
+  extern __shared__ uint64_t s_keys[];  // [R][Nb]
   __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
   __shared__ uint32_t s_hist[4][256];
 
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
     s_qb[e / kD][e % kD] = qbar[((size_t)bh * Nb + g0 + e / kD) * kD + e % kD];
   __syncthreads();
 
-  // ---- phase 1: scores (fp64, channel order fixed), keys = order-preserving fp32 bits.
+  // ---- phase 1: scores (fp64, channel order fixed), keys = order-preserving fp64 bits.
   // Thread t scores key blocks t + 256 q; the ceil(Nb / 256) blocks per thread are taken
   // in the fewest balanced passes of at most 6.
   const double* kb = kbart + (size_t)bh * kD * Nb;
@@ -127,19 +128,22 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
   uint32_t* hist = s_hist[w];
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int r = w; r < nr; r += 4) {
-    const uint32_t* keys = s_keys + r * Nb;
-    // radix select (4 x 8 bits, most significant first) of the ksel-th largest key
-    uint32_t prefix = 0, mask = 0;
+    const uint64_t* keys = s_keys + r * Nb;
+    // Radix select of the ksel-th largest key, 8 bits per pass from the top. After a pass
+    // the keys whose selected bits exceed the prefix are kept, and kk more are wanted
+    // from those equal to it; when that whole bin is wanted the selection is complete
+    // (for distinct fp64 scores this happens after a few passes).
+    uint64_t prefix = 0, mask = 0;
     int kk = ksel;
-    for (int pass = 0; pass < 4; pass++) {
-      const int shift = 24 - 8 * pass;
+    for (int pass = 0; pass < 8; pass++) {
+      const int shift = 56 - 8 * pass;
 #pragma unroll
       for (int b = 0; b < 4; b++) hist[4 * lane + b] = 0u;
       // the wave's LDS operations execute in order; keep the compiler from moving them
       __builtin_amdgcn_wave_barrier();
       for (int j = lane; j < Nb; j += 64) {
-        const uint32_t u = keys[j];
-        if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
+        const uint64_t u = keys[j];
+        if ((u & mask) == prefix) atomicAdd(&hist[(uint32_t)(u >> shift) & 255u], 1u);
       }
       __builtin_amdgcn_wave_barrier();
       // lane owns bins 4*lane .. 4*lane+3; suffix counts from the top bin down
@@ -153,12 +157,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
       }
       int above = suf - loc;
       const int hs[4] = {h0, h1, h2, h3};
-      int sel_bin = -1, sel_k = 0;
+      int sel_bin = -1, sel_k = 0, sel_n = 0;
 #pragma unroll
       for (int b = 3; b >= 0; b--) {
         if (above < kk && above + hs[b] >= kk) {
           sel_bin = 4 * lane + b;
           sel_k = kk - above;
+          sel_n = hs[b];
         }
         above += hs[b];
       }
@@ -166,33 +171,38 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
       const int src = __ffsll((long long)who) - 1;
       sel_bin = __shfl(sel_bin, src);
       sel_k = __shfl(sel_k, src);
-      prefix |= (uint32_t)sel_bin << shift;
-      mask |= 255u << shift;
+      sel_n = __shfl(sel_n, src);
+      prefix |= (uint64_t)sel_bin << shift;
+      mask |= (uint64_t)255u << shift;
       kk = sel_k;
       __builtin_amdgcn_wave_barrier();
+      if (sel_n == sel_k) break;  // every key of the bin is kept
     }
     // best block: highest key, lowest index
-    uint32_t kmax = 0u;
+    uint64_t kmax = 0u;
     for (int j = lane; j < Nb; j += 64) kmax = max(kmax, keys[j]);
-    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o));
+    for (int o = 32; o > 0; o >>= 1) {
+      const uint64_t y = (uint64_t)__shfl_xor((long long)kmax, o);
+      kmax = max(kmax, y);
+    }
     int jb = INT_MAX;
     for (int j0 = 0; j0 < Nb && jb == INT_MAX; j0 += 64) {
       const int j = j0 + lane;
       const unsigned long long hit = __ballot(j < Nb && keys[j] == kmax);
       if (hit) jb = j0 + __ffsll((long long)hit) - 1;
     }
-    // keys > prefix are kept; of the keys == prefix the kk lowest indices; ascending
-    // after the best block
+    // keys whose selected bits exceed the prefix are kept; of those equal to it the kk
+    // lowest indices; ascending after the best block
     int32_t* out = idx + ((size_t)bh * Nb + g0 + r) * ksel;
     if (lane == 0) out[0] = jb;
     int pos = 1, eq_seen = 0;
     for (int j0 = 0; j0 < Nb; j0 += 64) {
       const int j = j0 + lane;
-      const uint32_t u = j < Nb ? keys[j] : 0u;
-      const bool eq = j < Nb && u == prefix;
+      const uint64_t um = j < Nb ? (keys[j] & mask) : 0u;
+      const bool eq = j < Nb && um == prefix;
       const unsigned long long eqm = __ballot(eq);
       const int eq_rank = eq_seen + __popcll(eqm & below);
-      const bool keep = j < Nb && (u > prefix || (eq && eq_rank < kk)) && j != jb;
+      const bool keep = j < Nb && (um > prefix || (eq && eq_rank < kk)) && j != jb;
       const unsigned long long km = __ballot(keep);
       if (keep) out[pos + __popcll(km & below)] = j;
       pos += __popcll(km);
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
 }
 
 int select_rows_per_group(int Nb) {
-  int R = 16384 / Nb;  // keys of R rows in at most 64 KiB of LDS
+  int R = 8192 / Nb;  // keys of R rows in at most 64 KiB of LDS (one row up to 128 KiB)
   return R < 1 ? 1 : (R > 8 ? 8 : R);
 }
 
@@ -210,7 +220,11 @@ hipError_t launch_select(const void* qbar, const void* kbart, int BH, int Nb, in
                          hipStream_t st) {
   const int R = select_rows_per_group(Nb);
   const int groups = (Nb + R - 1) / R;
-  size_t lds = (size_t)R * Nb * sizeof(uint32_t);
+  size_t lds = (size_t)R * Nb * sizeof(uint64_t);
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(select_kernel, dim3(BH * groups), dim3(kSelThreads), lds, st,
                      (const double*)qbar, (const double*)kbart, Nb, ksel, R, groups, (int32_t*)idx);
   return hipGetLastError();

@@ -181,3 +181,86 @@ def test_prepare_rejects_on_host():
     unaligned = C.c_void_p((1 << 20) + 2)
     st = L.sagesla_prepare(unaligned, p, p, 1e-6, 1, 2, 256, 128, 0.1, 64, 1, p, p, p, p, 1 << 30, None)
     assert st == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_export_list_is_the_documented_boundary():
+    # the boundary: the whole forward (plain and with tensor descriptors), the grouped
+    # stages, every single stage, the workspace queries, and the next-step workloads
+    want = {"sagesla_fwd", "sagesla_fwd_tensors", "sagesla_workspace_size", "sagesla_workspace_layout",
+            "sagesla_pool_select", "sagesla_quantize", "sagesla_linear_states", "sagesla_linear_complement",
+            "sagesla_sparse_attn", "sagesla_pool", "sagesla_head_stats", "sagesla_select", "sagesla_quant_kv",
+            "sagesla_linear_total", "sagesla_ksel", "sagesla_version", "sagesla_status_string"}
+    assert want <= set(declared_functions())
+
+
+def _desc(shape, dtype=_lib.DT_BF16, data=0x10000, stride=None):
+    d = _lib.Tensor()
+    d.data, d.dtype, d.ndim = data, dtype, len(shape)
+    st, acc = [0] * len(shape), 1
+    for a in range(len(shape) - 1, -1, -1):
+        st[a] = acc
+        acc *= shape[a]
+    for a in range(len(shape)):
+        d.shape[a] = shape[a]
+        d.stride[a] = (stride or st)[a]
+    return d
+
+
+def _fwd_tensors(q=None, k=None, v=None, proj=None, out=None, ws=None, topk=0.1, block=64):
+    shp = (1, 2, 2048, 128)
+    q = q or _desc(shp)
+    k = k or _desc(shp)
+    v = v or _desc(shp)
+    out = out or _desc(shp)
+    ws = ws or _desc((1 << 30,), _lib.DT_U8)
+    P = C.byref
+    return S.lib().sagesla_fwd_tensors(P(q), P(k), P(v), P(proj) if proj is not None else None, topk, block, P(out),
+                                       P(ws), None)
+
+
+@pytest.mark.parametrize("case", ["dtype", "rank", "stride", "shape", "proj-shape", "proj-dtype", "ws-dtype", "null"])
+def test_fwd_tensors_rejects_descriptors_on_host(case):
+    shp = (1, 2, 2048, 128)
+    kw = {}
+    if case == "dtype":
+        kw["q"] = _desc(shp, _lib.DT_F32)
+    elif case == "rank":
+        kw["k"] = _desc((2, 2048, 128))
+    elif case == "stride":  # a transposed (non-contiguous) view
+        kw["v"] = _desc(shp, stride=[2 * 2048 * 128, 2048 * 128, 1, 2048])
+    elif case == "shape":
+        kw["out"] = _desc((1, 2, 2047, 128))
+    elif case == "proj-shape":
+        kw["proj"] = _desc((128, 64))
+    elif case == "proj-dtype":
+        kw["proj"] = _desc((128, 128), _lib.DT_F32)
+    elif case == "ws-dtype":
+        kw["ws"] = _desc((1 << 30,), _lib.DT_BF16)
+    elif case == "null":
+        kw["q"] = _desc(shp, data=0)
+    assert _fwd_tensors(**kw) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_fwd_tensors_size_rules_match_fwd():
+    # sizes pass the descriptor checks and then meet the same rules as sagesla_fwd
+    assert _fwd_tensors(q=_desc((1, 2, 2048, 64)), k=_desc((1, 2, 2048, 64)), v=_desc((1, 2, 2048, 64)),
+                        out=_desc((1, 2, 2048, 64))) == _lib.ERR_UNSUPPORTED
+    assert _fwd_tensors(ws=_desc((100,), _lib.DT_U8)) == _lib.ERR_WORKSPACE
+    assert _fwd_tensors(topk=0.0) == _lib.ERR_INVALID_ARGUMENT
+
+
+def test_grouped_stage_entry_points_reject_bad_arguments():
+    L = S.lib()
+    p = 0x10000
+    assert L.sagesla_pool_select(p, p, p, 1, 1, 64, 128, 64, 0.0, *([p] * 9), None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_pool_select(p, p, p, 1, 1, 64, 128, 64, 0.5, *([p] * 8), None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_quantize(p, p, p, p, 1, 1, 64, 64, 64, p, p, p, None) == _lib.ERR_UNSUPPORTED
+    assert L.sagesla_quantize(p, p, p, p, 1, 1, 64, 128, 64, p, 0x3, p, None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_linear_states(p, p, p, p, 1, 1, 64, 128, 64, p, p, p, p, p, None, None) == \
+        _lib.ERR_INVALID_ARGUMENT
+
+
+def test_header_documents_the_kept_list_order():
+    text = open(HEADER).read()
+    assert "best first" in text and "stored ascending" not in text

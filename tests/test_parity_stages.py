@@ -8,6 +8,7 @@ fp32 with the same expressions); kept sets equal except near-ties (pooled-score 
 linear part y = O_l W within cos >= 0.9995 and max-abs <= 2e-2 per head, and the
 output within the same bars.
 """
+import ctypes as C
 import numpy as np
 import pytest
 import torch
@@ -215,3 +216,109 @@ def test_small_scores_partial_block(grid):
         r = O.sagesla_head(bits["q"][0, h], bits["k"][0, h], bits["v"][0, h], w, cfg.topk, quant=True)
         assert cos(o[0, h], r["out"][:cfg.N]) >= 0.9995
         assert np.max(np.abs(o[0, h] - r["out"][:cfg.N])) <= 2e-2
+
+
+def _planted_tie_inputs(nq=16, nk=16, v0=4.0):
+    """Scores near 180 whose planted gaps (about 1.2e-5, just over the 1e-5 near-tie
+    bound) are narrower than one fp32 step there (1.5e-5): every query token is
+    (w_i, v0 + e_i, v0, ..., v0) and every key token (1, v0, ..., v0), except that channel 0
+    of the first tokens of key block j adds 18 j bf16 steps of 2^-7, so the pooled
+    channel-0 mean grows by 18 j 2^-7 / 64 and s_ij by w_i times that over sqrt(128).
+    Query blocks differ in w_i and e_i, which moves where the fp32 roundings fall."""
+    N = 64 * max(nq, nk)
+    q = np.full((N, 128), v0, np.float32)
+    k = np.full((N, 128), v0, np.float32)
+    k[:, 0] = 1.0
+    for i in range(nq):
+        q[64 * i:64 * (i + 1), 0] = 0.0625 + (i % 4) * 2.0 ** -10
+        q[64 * i:64 * (i + 1), 1] = v0 + (i // 4) * 2.0 ** -5
+    for j in range(nk):
+        n, t = 18 * j, 0
+        while n > 0:
+            a = min(n, 120)
+            k[64 * j + t, 0] = 1.0 + a * 2.0 ** -7
+            n, t = n - a, t + 1
+    v = np.random.default_rng(33).standard_normal((N, 128)).astype(np.float32)
+    return q, k, v
+
+
+def test_select_exact_fp64_near_ties():
+    """The selection keys are the fp64 scores themselves: with planted score gaps of about
+    1.2e-5 at |s| ~ 180 (fp32 step 1.5e-5 there), the kept sets must equal the oracle's
+    exactly, up to the 1e-5 near-tie rule, which these gaps exceed."""
+    q, k, v = _planted_tie_inputs()
+    N = q.shape[0]
+    to = lambda a: torch.from_numpy(a).to(torch.bfloat16).reshape(1, 1, N, 128).cuda()
+    tq, tk, tv = to(q), to(k), to(v)
+    topk = 0.5
+    ws = S.alloc_workspace(tq, topk, False)
+    S.fwd(tq, tk, tv, None, topk=topk, workspace=ws)
+    torch.cuda.synchronize()
+    g = S.workspace_views(ws, 1, 1, N, topk=topk, linear=False)["idx"].cpu().numpy()[0]
+    qb, kb = O.pool(synth.bf16_bits(tq[0, 0])), O.pool(synth.bf16_bits(tk[0, 0]))
+    sc = O.scores(qb, kb)
+    Nb, ks = sc.shape[1], O.ksel(topk, sc.shape[1])
+    ora = np.stack([O.order_best_first(sc[i], row) for i, row in enumerate(O.select(sc, ks))])
+    # the case is hard for fp32 keys: in some row the boundary pair shares an fp32 value
+    srt = np.sort(sc, axis=1)[:, ::-1]
+    gap = srt[:, ks - 1] - srt[:, ks]
+    assert gap.min() > 1e-5 and np.abs(srt[0, 0]) > 128
+    assert np.any(np.float32(srt[:, ks - 1]) == np.float32(srt[:, ks]))
+    assert mask_mismatch(g, ora, sc) == []
+    assert np.array_equal(g, ora)
+
+
+def test_grouped_stages_and_descriptor_forward_equal_fwd():
+    """sagesla_pool_select + sagesla_linear_states (or sagesla_quantize) + the complement
+    and sparse stages, and sagesla_fwd_tensors, compute exactly what sagesla_fwd does."""
+    from sparse_attention_sagesla_amd import _lib
+    cfg = synth.scaled(synth.CONFIGS["wan14b-720p"], H=2, grid=(4, 20, 33), seed=22, name="grouped")
+    x = synth.make_inputs(cfg, device="cuda")
+    q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
+    B, H, N, topk = cfg.B, cfg.H, cfg.N, cfg.topk
+    L = S.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+    ref_ws = S.alloc_workspace(q, topk, True)
+    ref = S.fwd(q, k, v, proj, topk=topk, workspace=ref_ws)
+    for use_states in (True, False):
+        ws = S.alloc_workspace(q, topk, True)
+        ws.fill_(0xFF)
+        P = {n: ws.data_ptr() + o for n, o in S.workspace_layout(B, H, N, topk=topk, linear=True).items()}
+        out = torch.empty_like(q)
+        st = L.sagesla_pool_select(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, 128, 64, topk, P["qbar"],
+                                   P["kbart"], P["ksum"], P["vamax_blk"], P["q8"], P["sq"], P["kmean"], P["vamax"],
+                                   P["idx"], sp)
+        assert st == 0
+        if use_states:
+            st = L.sagesla_linear_states(k.data_ptr(), v.data_ptr(), P["kmean"], P["vamax"], B, H, N, 128, 64,
+                                         P["k8"], P["sk"], P["v8"], P["hs"], P["hpart"], P["htot"], sp)
+            assert st == 0
+            st = L.sagesla_linear_complement(q.data_ptr(), P["idx"], P["hs"], P["htot"], proj.data_ptr(), B, H, N,
+                                             128, 64, topk, P["ulist"], P["umask"], P["ucount"], P["hc"], P["y"], sp)
+            assert st == 0
+        else:
+            st = L.sagesla_quantize(k.data_ptr(), v.data_ptr(), P["kmean"], P["vamax"], B, H, N, 128, 64, P["k8"],
+                                    P["sk"], P["v8"], sp)
+            assert st == 0
+        st = L.sagesla_sparse_attn(P["q8"], P["sq"], P["k8"], P["sk"], P["v8"], P["vamax"], P["idx"],
+                                   P["y"] if use_states else None, B, H, N, 128, 64, topk, out.data_ptr(), sp)
+        assert st == 0
+        torch.cuda.synchronize()
+        gv, rv = S.workspace_views(ws, B, H, N, topk=topk), S.workspace_views(ref_ws, B, H, N, topk=topk)
+        for name in ("qbar", "kbart", "kmean", "vamax", "q8", "sq", "k8", "sk", "v8", "idx"):
+            assert torch.equal(gv[name], rv[name]), name
+        if use_states:
+            assert torch.equal(out, ref)
+        else:
+            ref_s = S.fwd(q, k, v, None, topk=topk)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_s)
+    # the descriptor forward
+    out = torch.empty_like(q)
+    ws = S.alloc_workspace(q, topk, True)
+    d = _lib.tensor_desc
+    st = L.sagesla_fwd_tensors(*(C.byref(d(t)) for t in (q, k, v, proj)), topk, 64, C.byref(d(out)),
+                               C.byref(d(ws)), sp)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
