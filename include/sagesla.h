@@ -146,6 +146,22 @@ sagesla_status sagesla_fwd_tensors(const sagesla_tensor *q, const sagesla_tensor
                                    int block, sagesla_tensor *out, const sagesla_tensor *workspace,
                                    sagesla_stream_t stream);
 
+/* ---- forward without allocation ---------------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sagesla_fwd with the workspace in a
+ * fixed device array of SAGESLA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on, until the process ends. The caller still passes q, k, v, proj, out. Shapes
+ * whose workspace (sagesla_workspace_size) exceeds the array return SAGESLA_ERR_WORKSPACE
+ * before anything is enqueued. No step needs the array cleared (every region is written
+ * before it is read). All calls on one GPU share its array, which keeps the last call's
+ * intermediates: calls that overlap on one GPU (other streams, other threads) race and
+ * must not be issued; calls on one stream are ordered and safe. */
+#define SAGESLA_NOALLOC_SCRATCH_BYTES (256u << 20) /* 256 MiB */
+
+sagesla_status sagesla_fwd_noalloc(const void *q, const void *k, const void *v, const void *proj,
+                                   int B, int H, int N, int d, double topk, int block, void *out,
+                                   sagesla_stream_t stream);
+
 /* ---- producer-side fusion -------------------------------------------------------------
  * The pages fuse the rewritten LayerNorm/RMSNorm kernels with their neighbours (news.qq.com
  * explainer, "Fourth key"). sagesla_prepare takes the QKV projection output qkv bf16

@@ -27,7 +27,7 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
            "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd",
            "sagesla_prepare", "sagesla_fwd_prepared", "sagesla_fwd_tensors", "sagesla_pool_select",
-           "sagesla_quantize", "sagesla_linear_states"]
+           "sagesla_quantize", "sagesla_linear_states", "sagesla_fwd_noalloc"]
 
 # sagesla_dtype values and the sagesla_tensor descriptor
 DT_BF16, DT_F32, DT_I8, DT_FP8E4M3, DT_I32, DT_U8 = range(6)
@@ -102,6 +102,7 @@ def lib():
             "sagesla_pool_select": (i32, [P, P, P] + dims + [i32, f64] + [P] * 9 + [P]),
             "sagesla_quantize": (i32, [P, P, P, P] + dims + [i32, P, P, P, P]),
             "sagesla_linear_states": (i32, [P, P, P, P] + dims + [i32] + [P] * 6 + [P]),
+            "sagesla_fwd_noalloc": (i32, [P, P, P, P] + dims + [f64, i32, P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)

@@ -337,6 +337,48 @@ sagesla_status sagesla_fwd_tensors(const sagesla_tensor* q, const sagesla_tensor
                  workspace->data, (size_t)workspace->shape[0], stream, false);
 }
 
+// ---------------------------------------------------------------- forward without allocation
+
+// The workspace of sagesla_fwd_noalloc: one fixed-size device array, which every GPU the
+// library runs on holds (its own copy) until the process ends. In host code the name is
+// only a stand-in for the symbol; the device address comes from hipGetSymbolAddress, once
+// per device, and only that address is ever passed on.
+static __device__ __align__(256) unsigned char scratch[SAGESLA_NOALLOC_SCRATCH_BYTES];
+
+static sagesla_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGESLA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return SAGESLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return SAGESLA_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_fwd_noalloc(const void* q, const void* k, const void* v, const void* proj, int B, int H,
+                                   int N, int d, double topk, int block, void* out, sagesla_stream_t stream) {
+  Geom gm;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_topk(topk, &gm)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, out})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
+  size_t off[SAGESLA_WS_COUNT], total;
+  layout(gm, proj != nullptr && gm.ksel < gm.Nb, off, &total);
+  if (total > (size_t)SAGESLA_NOALLOC_SCRATCH_BYTES) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  void* ws = nullptr;
+  if ((s = scratch_address(&ws)) != SAGESLA_OK) return s;
+  return run_fwd(q, k, v, proj, B, H, N, d, topk, block, out, ws, (size_t)SAGESLA_NOALLOC_SCRATCH_BYTES, stream,
+                 false);
+}
+
 // ---------------------------------------------------------------- grouped stages
 
 sagesla_status sagesla_pool_select(const void* q, const void* k, const void* v, int B, int H, int N, int d,
