@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--no-sla-train", action="store_true", help="skip the SLA training-path measurement")
     ap.add_argument("--no-topk-sweep", action="store_true", help="skip the top-k sweep")
     ap.add_argument("--no-prepare", action="store_true", help="skip the producer-side fusion measurement")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table (all five workloads)")
+    ap.add_argument("--config-steps", type=int, default=5, help="timed calls per workload in the table")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: the cores this process may use)")
     ap.add_argument("--w8a8-shape", default="75600,5120,5120", help="M,K,N of the W8A8 linear layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="before the warmup, run one plain device copy of this many MiB (a kernel of known "
@@ -209,15 +212,21 @@ def main():
         "staged_equals_fwd": same,
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_INT8_FP8_TOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_INT8_FP8_TOPS, 4), "traffic": traffic,
+                     "unit": "TOP/s", "frac": round(achieved / PEAK_INT8_FP8_TOPS, 4), "traffic": traffic,
                      "kernel": "sparse_attn_kernel", "work_per_launch_ops": exec_ops},
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks)
+        res["cpu_baseline"] = cpu_baseline(cfg, x, args.cpu_blocks, args.cpu_threads)
+    del x, q, k, v, proj, ws, out, idx, fwd_out
+    torch.cuda.empty_cache()
+    if not args.no_configs:
+        res["configs"] = configs_table(args)
     if not args.no_w8a8:
         res["w8a8"] = w8a8_measure(args)
+    if not args.no_topk_sweep or not args.no_sla_train:
+        x = synth.make_inputs(cfg, device=dev)
     if not args.no_topk_sweep:
         res["topk_sweep"] = topk_sweep(args, cfg, x)
     if not args.no_prepare:
@@ -228,6 +237,89 @@ def main():
 
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+TABLE_CONFIGS = ["tiny", "wan1.3b-480p", "wan14b-480p", "wan14b-720p", "i2v-a14b-720p", "i2v-a14b-720p-dense"]
+
+
+def executed_ops(S, ws, B, H, N, d, topk, linear, dev):
+    """Executed MFMA work of the sparse stage from the actual kept lists: sum over kept
+    (query block, key block) pairs of 4 n_i n_j d (QK^T and PV, valid tokens only)."""
+    idx = S.workspace_views(ws, B, H, N, topk=topk, linear=linear)["idx"].long()
+    Nb = (N + 63) // 64
+    nlen = torch.full((Nb,), 64, dtype=torch.int64, device=dev)
+    nlen[-1] = N - 64 * (Nb - 1)
+    return 4.0 * d * float((nlen[idx].sum(-1) * nlen[None, :]).sum().item())
+
+
+def configs_table(args):
+    """Every workload of the parity set, each timed on its own inputs: K calls of the
+    forward (sagesla_fwd), and K launches of the sparse stage alone on the forward's
+    workspace, each with HIP events on the launch stream; executed TOP/s from the actual
+    kept lists, dense-equivalent TFLOP/s (4 B H N^2 d over the call), and the sparse
+    stage's fraction of the 8-bit MFMA peak."""
+    import sparse_attention_sagesla_amd as S
+    from sparse_attention_sagesla_amd import synth
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    L = S.lib()
+    rows = {}
+    x = None
+    for name in TABLE_CONFIGS:
+        cfg = synth.CONFIGS[name]
+        B, H, N, d, topk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.topk
+        # the dense run uses the I2V inputs (same seed and shape)
+        if x is None or x.get("_seed") != (cfg.seed, cfg.grid, cfg.H):
+            x = None
+            torch.cuda.empty_cache()
+            x = synth.make_inputs(cfg, device=dev)
+            x["_seed"] = (cfg.seed, cfg.grid, cfg.H)
+        q, k, v = x["q"], x["k"], x["v"]
+        proj = x["proj"] if cfg.linear else None
+        linear = proj is not None
+        ws = S.alloc_workspace(q, topk, linear)
+        out = torch.empty_like(q)
+        for _ in range(2):
+            S.fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.config_steps):
+            S.fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.config_steps
+        Pw = {n: ws.data_ptr() + o for n, o in S.workspace_layout(B, H, N, topk=topk, linear=linear).items()}
+        use_lin = linear and S.ksel(N, topk) < (N + 63) // 64
+
+        def sparse():
+            st = L.sagesla_sparse_attn(Pw["q8"], Pw["sq"], Pw["k8"], Pw["sk"], Pw["v8"], Pw["vamax"], Pw["idx"],
+                                       Pw["y"] if use_lin else None, B, H, N, d, 64, topk, out.data_ptr(),
+                                       stream.cuda_stream)
+            if st != 0:
+                raise RuntimeError("sagesla_sparse_attn: " + S.status_string(st))
+        sparse()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.config_steps):
+            sparse()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_sa = e0.elapsed_time(e1) / args.config_steps
+        ops = executed_ops(S, ws, B, H, N, d, topk, linear, dev)
+        tops = ops / (ms_sa * 1e-3) / 1e12
+        rows[name] = {
+            "shape": "B=%d H=%d N=%d d=%d topk=%g%s" % (B, H, N, d, topk, "" if linear else " linear-branch off"),
+            "ksel": S.ksel(N, topk), "ms_per_call": round(ms, 4), "sparse_attn_ms": round(ms_sa, 4),
+            "executed_top": round(ops / 1e12, 4),
+            "executed_tops_sparse_attn": round(tops, 1),
+            "executed_tops_whole_call": round(ops / (ms * 1e-3) / 1e12, 1),
+            "dense_equiv_tflops_whole_call": round(4.0 * B * H * N * N * d / (ms * 1e-3) / 1e12, 1),
+            "sparse_attn_frac_of_mfma_peak": round(tops / PEAK_INT8_FP8_TOPS, 4),
+        }
+        del ws, out
+    del x
+    torch.cuda.empty_cache()
+    return {"steps": args.config_steps, "peak_tops": PEAK_INT8_FP8_TOPS, "rows": rows}
 
 
 def prepare_measure(args, cfg, eps=1e-6):
@@ -346,7 +438,9 @@ def topk_sweep(args, cfg, x, topks=(0.05, 0.1, 0.15, 0.2, 0.25), heads=(0, 1)):
 def sla_train_measure(args, cfg, x):
     """The trainable SLA path on the same inputs: the unquantized forward (saving what the
     backward needs) and the backward (dQ, dK, dV, dW) from a seeded dO, each timed with HIP
-    events on the launch stream over the same number of steps."""
+    events on the launch stream over the same number of steps; then the same backward
+    without the linear branch (proj = None: only the sparse part's kernels), so that the
+    sparse products are measured on their own."""
     import sparse_attention_sagesla_amd as S
     B, H, N, d, topk = cfg.B, cfg.H, cfg.N, cfg.d, cfg.topk
     q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
@@ -354,42 +448,49 @@ def sla_train_measure(args, cfg, x):
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed + 77)
     dout = torch.randn(q.shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-    ws = torch.empty(S.sla_workspace_size(B, H, N, d, 64, topk, proj is not None), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
     grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
-    dproj = torch.empty((d, d), dtype=torch.float32, device=dev) if proj is not None else None
     stream = torch.cuda.current_stream()
 
-    def fwd():
-        S.sla_fwd(q, k, v, proj, topk=topk, out=out, workspace=ws)
+    def measure(pj):
+        ws = torch.empty(S.sla_workspace_size(B, H, N, d, 64, topk, pj is not None), dtype=torch.uint8, device=dev)
+        dproj = torch.empty((d, d), dtype=torch.float32, device=dev) if pj is not None else None
 
-    def bwd():
-        S.sla_bwd(q, k, v, dout, ws, proj=proj, topk=topk, dq=grads[0], dk=grads[1], dv=grads[2], dproj=dproj)
+        def fwd():
+            S.sla_fwd(q, k, v, pj, topk=topk, out=out, workspace=ws)
 
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    steps = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for s_ in range(steps):
-        ev[s_][0].record(stream)
-        fwd()
-        ev[s_][1].record(stream)
-        bwd()
-        ev[s_][2].record(stream)
-    torch.cuda.synchronize()
-    ms_f = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
-    ms_b = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
-    # executed products from the actual kept lists: forward QK^T and PV, backward S, dP, dQ
-    # (query side) and S, dP, dV, dK (key side), each 2 n_i n_j d flops per kept pair
-    idx = S.sla_workspace_views(ws, B, H, N, topk=topk, linear=proj is not None)["idx"].long()
+        def bwd():
+            S.sla_bwd(q, k, v, dout, ws, proj=pj, topk=topk, dq=grads[0], dk=grads[1], dv=grads[2], dproj=dproj)
+
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s_ in range(args.steps):
+            ev[s_][0].record(stream)
+            fwd()
+            ev[s_][1].record(stream)
+            bwd()
+            ev[s_][2].record(stream)
+        torch.cuda.synchronize()
+        ms_f = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+        ms_b = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+        idx = S.sla_workspace_views(ws, B, H, N, topk=topk, linear=pj is not None)["idx"].long()
+        return ms_f, ms_b, idx
+
+    ms_f, ms_b, idx = measure(proj)
+    ms_f0, ms_b0, _ = measure(None)
     Nb = (N + 63) // 64
     nlen = torch.full((Nb,), 64, dtype=torch.int64, device=dev)
     nlen[-1] = N - 64 * (Nb - 1)
     pair_tok = float((nlen[idx].sum(-1) * nlen[None, :]).sum().item())
-    f_fwd, f_bwd = 4.0 * d * pair_tok, 14.0 * d * pair_tok
-    tf_f, tf_b = f_fwd / (ms_f * 1e-3) / 1e12, f_bwd / (ms_b * 1e-3) / 1e12
+    # the method's products, 2 n_i n_j d flops each per kept pair: forward QK^T and PV;
+    # backward S (recomputed), dP, dV, dK, dQ. The kernels form S and dP once more (both
+    # the dQ and the dK/dV kernel need them): executed work is 14 d sum n_i n_j, but only
+    # the method's 10 d sum n_i n_j is counted.
+    f_fwd, f_bwd, f_bwd_exec = 4.0 * d * pair_tok, 10.0 * d * pair_tok, 14.0 * d * pair_tok
+    tf_b_sparse = f_bwd / (ms_b0 * 1e-3) / 1e12
     return {
         "workload": "%s: B=%d H=%d N=%d d=%d topk=%g, linear branch %s; one step = forward + backward" % (
             cfg.name, B, H, N, d, topk, "on" if proj is not None else "off"),
@@ -397,11 +498,16 @@ def sla_train_measure(args, cfg, x):
         "ms_fwd": round(ms_f, 4),
         "ms_bwd": round(ms_b, 4),
         "ms_step": round(ms_f + ms_b, 4),
-        "fwd_sparse_tflops": round(tf_f, 1),
-        "bwd_sparse_tflops": round(tf_b, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tf_b, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf_b / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "backward pass (sparse products; the linear part's time included)",
+        "ms_fwd_sparse_only": round(ms_f0, 4),
+        "ms_bwd_sparse_only": round(ms_b0, 4),
+        "ms_bwd_linear_part": round(ms_b - ms_b0, 4),
+        "fwd_sparse_tflops": round(f_fwd / (ms_f0 * 1e-3) / 1e12, 1),
+        "bwd_sparse_tflops_method_products": round(tf_b_sparse, 1),
+        "bwd_sparse_tflops_executed_products": round(f_bwd_exec / (ms_b0 * 1e-3) / 1e12, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf_b_sparse, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf_b_sparse / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "backward without the linear branch (sla_bwd_dq + sla_kept_mask + sla_bwd_dkdv + "
+                               "relayouts); work = the method's 5 products, 10 d sum n_i n_j",
                      "work_per_launch_flops": f_bwd},
     }
 
@@ -525,28 +631,63 @@ def w8a8_cpu_baseline(xx, w, b, M, K, N, rows=16):
             "measured_s": round(t_w + rows * t_r, 2)}
 
 
-def cpu_baseline(cfg, x, nblocks):
-    """The oracle, as it is, on one head: once with no query blocks (the per-head part:
-    pooling, quantization, linear states) and once with `nblocks` query blocks; the call
-    time is extrapolated to all heads and blocks (heads and blocks are independent)."""
+def host_cpu():
+    """CPU model name and the number of cores this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
+def cpu_baseline(cfg, x, nblocks, threads=0):
+    """The oracle, as it is, on the host's cores: `threads` heads at once (one thread
+    each; the oracle releases the interpreter lock inside its C code), once with no query
+    blocks (the per-head part: pooling, quantization, linear states) and once with
+    `nblocks` query blocks per head. Heads and query blocks are independent, so the call
+    time is extrapolated to all heads and blocks from these two measurements."""
     import oracle as O
+    from concurrent.futures import ThreadPoolExecutor
     from sparse_attention_sagesla_amd import synth
-    q, k, v = (synth.bf16_bits(x[n][0, 0]) for n in ("q", "k", "v"))
+    model, avail = host_cpu()
+    env_cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    n_thr = threads or (min(avail, env_cap) if env_cap > 0 else avail)
+    n_thr = max(1, min(n_thr, cfg.B * cfg.H))
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)][:n_thr]
+    bits = {h: tuple(synth.bf16_bits(x[n][h[0], h[1]]) for n in ("q", "k", "v")) for h in heads}
     w = synth.bf16_bits(x["proj"]) if x["proj"] is not None else None
     Nb = (cfg.N + 63) // 64
-    t0 = time.perf_counter()
-    O.sagesla_head(q, k, v, w, cfg.topk, qblocks=[])
-    t_head = time.perf_counter() - t0
     blocks = list(range(0, Nb, max(1, Nb // nblocks)))[:nblocks]
-    t0 = time.perf_counter()
-    O.sagesla_head(q, k, v, w, cfg.topk, qblocks=blocks)
-    t_blk = max(0.0, (time.perf_counter() - t0 - t_head) / len(blocks))
-    est_ms = (cfg.B * cfg.H) * (t_head + Nb * t_blk) * 1e3
-    return {"value": round(est_ms, 1), "unit": "ms", "cores": 1, "kind": "oracle",
-            "sample": "one head of %s: per-head part %.2f s, %d of %d query blocks at %.3f s each; "
-                      "extrapolated to %d heads x %d blocks, single thread" % (
-                          cfg.name, t_head, len(blocks), Nb, t_blk, cfg.B * cfg.H, Nb),
-            "measured_s": round(t_head * 2 + t_blk * len(blocks), 2)}
+
+    def timed(qbl):
+        def one(h):
+            q, k, v = bits[h]
+            O.sagesla_head(q, k, v, w, cfg.topk, qblocks=qbl)
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(max_workers=n_thr) as ex:
+            list(ex.map(one, heads))
+        return time.perf_counter() - t0
+
+    t_head = timed([])                 # per-head part of n_thr heads at once
+    t_all = timed(blocks)              # the same plus len(blocks) query blocks per head
+    t_blk = max(0.0, (t_all - t_head) / len(blocks))
+    rounds = -(-cfg.B * cfg.H // n_thr)  # heads are processed n_thr at a time
+    est_ms = rounds * (t_head + Nb * t_blk) * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms", "cores": n_thr, "kind": "oracle",
+            "cpu_model": model, "cores_available": avail,
+            "sample": "%s: %d heads at once on %d threads; per-head part %.2f s, then %d of %d query blocks per "
+                      "head at %.4f s per block (all heads together); measured %.1f s, extrapolated to %d heads "
+                      "(%d rounds) x %d blocks" % (cfg.name, n_thr, n_thr, t_head, len(blocks), Nb, t_blk,
+                                                  t_head + t_all, cfg.B * cfg.H, rounds, Nb),
+            "measured_s": round(t_head + t_all, 2)}
 
 
 if __name__ == "__main__":
