@@ -51,6 +51,10 @@ def lib():
             "oracle_linear_block": (None, [P, P, P, P, i32, i32, i32, i32, i32, P]),
             "oracle_project": (None, [P, P, i32, i32, P]),
             "oracle_sagesla_head": (i32, [P, P, P, P, i32, i32, i32, f64, i32, P, i32, P, P, P, P]),
+            "oracle_adaptive_k": (None, [P, i32, i32, i32, i32, f64, P, P]),
+            "oracle_adaptive_ksel": (i32, [P, i32, i32, i32]),
+            "oracle_sagesla_head_adaptive": (i32, [P, P, P, P, i32, i32, i32, f64, f64, f64, i32, P, i32, P, P, P,
+                                                   P, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -124,6 +128,25 @@ def select(score_mat, k: int):
     idx = np.empty((nq, k), np.int32)
     lib().oracle_select(_p(s), nq, nk, k, _p(idx))
     return idx
+
+
+def adaptive_k(score_mat, N, tau, blk=64):
+    """Per query block: the fewest blocks (selection order) whose pooled attention mass
+    n_j exp(s_ij - max) reaches tau of the row's total. Returns (k [nq] int32, margin [nq])
+    where margin is the distance of tau from the nearer prefix mass around the decision,
+    relative to the row's total."""
+    s = _c(score_mat, np.float64)
+    nq, Nb = s.shape
+    k = np.empty(nq, np.int32)
+    margin = np.empty(nq, np.float64)
+    lib().oracle_adaptive_k(_p(s), nq, Nb, N, blk, float(tau), _p(k), _p(margin))
+    return k, margin
+
+
+def adaptive_ksel(k_rows, kmin, kmax):
+    """A head's count: clamp(ceil(mean k_i - 1e-9), kmin, kmax)."""
+    k = _c(k_rows, np.int32)
+    return lib().oracle_adaptive_ksel(_p(k), len(k), int(kmin), int(kmax))
 
 
 def order_best_first(score_row, kept):
@@ -254,6 +277,32 @@ def sagesla_head(q_bits, k_bits, v_bits, w_bits, topk, quant=True, qblocks=None,
     if r < 0:
         raise ValueError("oracle_sagesla_head: bad arguments")
     return dict(out=out, out_s=os_, out_l=ol, idx=idx, ksel=ks, qblocks=qbl)
+
+
+def sagesla_head_adaptive(q_bits, k_bits, v_bits, w_bits, topk_min, topk_max, tau, quant=True, qblocks=None,
+                          blk=64):
+    """SageSLA forward of one head with its content-adaptive count. Returns dict(out, out_s,
+    out_l, idx, ksel, k_rows, qblocks); idx is [Nb, kmax] (kmax = ksel(topk_max)), -1 past
+    the head's ksel."""
+    q = _c(q_bits, np.uint16)
+    k = _c(k_bits, np.uint16)
+    v = _c(v_bits, np.uint16)
+    w = None if w_bits is None else _c(w_bits, np.uint16)
+    N, d = q.shape
+    Nb = num_blocks(N, blk)
+    qbl = np.arange(Nb, dtype=np.int32) if qblocks is None else _c(qblocks, np.int32)
+    kmax = ksel(topk_max, Nb)
+    out = np.zeros((len(qbl) * blk, d), np.float64)
+    os_ = np.zeros_like(out)
+    ol = np.zeros_like(out)
+    idx = np.empty((Nb, kmax), np.int32)
+    k_rows = np.empty(Nb, np.int32)
+    r = lib().oracle_sagesla_head_adaptive(_p(q), _p(k), _p(v), _p(w), N, d, blk, float(topk_min),
+                                           float(topk_max), float(tau), int(bool(quant)), _p(qbl), len(qbl),
+                                           _p(out), _p(os_), _p(ol), _p(idx), _p(k_rows))
+    if r < 0:
+        raise ValueError("oracle_sagesla_head_adaptive: bad arguments")
+    return dict(out=out, out_s=os_, out_l=ol, idx=idx, ksel=r, k_rows=k_rows, qblocks=qbl)
 
 
 def sagesla(q_bits, k_bits, v_bits, w_bits, topk, quant=True, heads=None, qblocks=None, blk=64,

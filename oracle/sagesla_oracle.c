@@ -225,6 +225,99 @@ void oracle_order_best_first(const double *row, int ksel, int32_t *kept)
     kept[0] = jb;
 }
 
+/* ---------------------------------------------------------------- adaptive k_sel */
+
+/*
+ * Content-adaptive number of kept blocks per head. The pages list sparsity that adapts
+ * to the content as future work and give no rule (news.qq.com explainer, the section on
+ * the method's limits, sixth challenge; 0.1-0.15 of the blocks at inference, section
+ * "From training to deployment"). Reading: the block scores s_ij already estimate the
+ * attention logits of the block pair, so the pooled attention mass of key block j for
+ * query block i is w_ij = n_j exp(s_ij - max_j s_ij) (n_j valid tokens), and query block
+ * i needs k_i = the fewest blocks, taken in selection order (score descending, lower
+ * index on ties), whose mass reaches tau of its row's total sum_j w_ij. A head keeps
+ * k_sel = clamp(ceil(sum_i k_i / nq), kmin, kmax) blocks for every query block
+ * (the same count for all of a head's query blocks).
+ *
+ * scores: [nq][Nb] (the selection scores), n_j from N and blk. k_rows: [nq]. margin
+ * (may be NULL): [nq], the distance of tau from the nearer of the two prefix masses
+ * around the decision, |prefix(k_i) - tau W| and |prefix(k_i - 1) - tau W|, over W;
+ * a decision closer than rounding can change is a near-tie.
+ * Plain: a full sort of each row by (score desc, index asc), then a running sum.
+ */
+typedef struct {
+    double s;
+    int j;
+} scored_block;
+
+/* selection order: higher score first, lower index on equal scores */
+static int adaptive_cmp(const void *a, const void *b)
+{
+    const scored_block *x = (const scored_block *)a, *y = (const scored_block *)b;
+    if (x->s > y->s)
+        return -1;
+    if (x->s < y->s)
+        return 1;
+    return x->j < y->j ? -1 : (x->j > y->j ? 1 : 0);
+}
+
+void oracle_adaptive_k(const double *scores, int nq, int Nb, int N, int blk, double tau, int32_t *k_rows,
+                       double *margin)
+{
+    scored_block *order = (scored_block *)malloc(sizeof(scored_block) * (size_t)Nb);
+    double *w = (double *)malloc(sizeof(double) * (size_t)Nb);
+    for (int i = 0; i < nq; i++) {
+        const double *row = scores + (size_t)i * Nb;
+        double mx = -INFINITY;
+        for (int j = 0; j < Nb; j++)
+            if (row[j] > mx)
+                mx = row[j];
+        double W = 0.0;
+        for (int j = 0; j < Nb; j++) {
+            w[j] = (double)block_len(j, N, blk) * exp(row[j] - mx);
+            W += w[j];
+        }
+        for (int j = 0; j < Nb; j++) {
+            order[j].s = row[j];
+            order[j].j = j;
+        }
+        qsort(order, (size_t)Nb, sizeof(scored_block), adaptive_cmp);
+        const double T = tau * W;
+        double prefix = 0.0, before = 0.0;
+        int k = Nb;
+        for (int r = 0; r < Nb; r++) {
+            before = prefix;
+            prefix += w[order[r].j];
+            if (prefix >= T) {
+                k = r + 1;
+                break;
+            }
+        }
+        k_rows[i] = k;
+        if (margin) {
+            double a = fabs(prefix - T), b = fabs(before - T);
+            margin[i] = (a < b ? a : b) / W;
+        }
+    }
+    free(order);
+    free(w);
+}
+
+/* Per-head count from the rows' counts: clamp(ceil(sum k_i / nq), kmin, kmax), the
+ * ceiling taken on integers. */
+int oracle_adaptive_ksel(const int32_t *k_rows, int nq, int kmin, int kmax)
+{
+    long long sum = 0;
+    for (int i = 0; i < nq; i++)
+        sum += k_rows[i];
+    int k = (int)((sum + nq - 1) / nq);
+    if (k < kmin)
+        k = kmin;
+    if (k > kmax)
+        k = kmax;
+    return k;
+}
+
 /* ---------------------------------------------------------------- O4: K smoothing */
 
 /*
@@ -550,25 +643,23 @@ void oracle_project(const double *ol, const uint16_t *w, int rows, int d, double
 /* ---------------------------------------------------------------- whole head */
 
 /*
- * SageSLA forward of one head for the query blocks listed in qblocks:
+ * SageSLA forward of one head for the query blocks listed in qblocks, keeping ksel key
+ * blocks per query block:
  *   O = O_s + O_l W_proj,
  * O_s from the quantized sparse softmax (quant = 1) or its fp64 form (quant = 0),
  * O_l from the linear branch over the blocks that were not kept (skipped when w is
- * NULL). Outputs for listed block b go to rows [b_pos*blk, b_pos*blk + n_b) of out,
- * out_s, out_l (each [nqb*blk][d]; out_s / out_l may be NULL). idx_out (may be NULL,
- * [Nb][ksel]) receives the kept blocks of every listed query block in its row; rows of
- * query blocks that are not listed are set to -1. Scores and selection are evaluated
- * only for the listed query blocks. Returns ksel, or -1 on bad arguments.
+ * NULL or every block is kept). Outputs for listed block b go to rows
+ * [b_pos*blk, b_pos*blk + n_b) of out, out_s, out_l (each [nqb*blk][d]; out_s / out_l
+ * may be NULL). idx_out (may be NULL, [Nb][kstride], kstride >= ksel) receives the kept
+ * blocks of every listed query block in its row, -1 past ksel; rows of query blocks
+ * that are not listed are all -1. Scores and selection are evaluated only for the listed
+ * query blocks.
  */
-int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                        const uint16_t *w, int N, int d, int blk, double topk, int quant,
-                        const int32_t *qblocks, int nqb, double *out, double *out_s,
-                        double *out_l, int32_t *idx_out)
+static void head_core(const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *w,
+                      int N, int d, int blk, int ksel, int kstride, int quant, const int32_t *qblocks,
+                      int nqb, double *out, double *out_s, double *out_l, int32_t *idx_out)
 {
-    if (N < 1 || d < 1 || blk < 1 || !(topk > 0.0 && topk <= 1.0))
-        return -1;
     int Nb = oracle_num_blocks(N, blk);
-    int ksel = oracle_ksel(topk, Nb);
 
     /* O1-O3: pooling, scores and selection for the listed query blocks */
     double *qbar = (double *)malloc(sizeof(double) * (size_t)Nb * d);
@@ -588,7 +679,9 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         oracle_order_best_first(srow, ksel, idx + (size_t)qb * ksel);
     }
     if (idx_out)
-        memcpy(idx_out, idx, sizeof(int32_t) * (size_t)Nb * ksel);
+        for (int i = 0; i < Nb; i++)
+            for (int r = 0; r < kstride; r++)
+                idx_out[(size_t)i * kstride + r] = r < ksel ? idx[(size_t)i * ksel + r] : -1;
     free(qbar);
     free(kbar);
     free(srow);
@@ -669,6 +762,56 @@ int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     free(sv);
     free(H);
     free(z);
+}
+
+/* The forward of one head at the Top-K ratio topk (ksel = oracle_ksel(topk, Nb)); outputs
+ * as for head_core with kstride = ksel. Returns ksel, or -1 on bad arguments. */
+int oracle_sagesla_head(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        const uint16_t *w, int N, int d, int blk, double topk, int quant,
+                        const int32_t *qblocks, int nqb, double *out, double *out_s,
+                        double *out_l, int32_t *idx_out)
+{
+    if (N < 1 || d < 1 || blk < 1 || !(topk > 0.0 && topk <= 1.0))
+        return -1;
+    int ksel = oracle_ksel(topk, oracle_num_blocks(N, blk));
+    head_core(q, k, v, w, N, d, blk, ksel, ksel, quant, qblocks, nqb, out, out_s, out_l, idx_out);
+    return ksel;
+}
+
+/*
+ * The forward of one head with its content-adaptive count: scores of every query block
+ * (oracle_pool, oracle_scores), k_rows = oracle_adaptive_k at tau, the head's count
+ * ksel = oracle_adaptive_ksel(k_rows, oracle_ksel(topk_min), oracle_ksel(topk_max)),
+ * then head_core with kstride = oracle_ksel(topk_max). k_rows (may be NULL): [Nb].
+ * Returns ksel, or -1 on bad arguments.
+ */
+int oracle_sagesla_head_adaptive(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                 const uint16_t *w, int N, int d, int blk, double topk_min,
+                                 double topk_max, double tau, int quant, const int32_t *qblocks,
+                                 int nqb, double *out, double *out_s, double *out_l,
+                                 int32_t *idx_out, int32_t *k_rows)
+{
+    if (N < 1 || d < 1 || blk < 1 || !(topk_min > 0.0 && topk_min <= topk_max && topk_max <= 1.0) ||
+        !(tau > 0.0 && tau <= 1.0))
+        return -1;
+    int Nb = oracle_num_blocks(N, blk);
+    int kmin = oracle_ksel(topk_min, Nb), kmax = oracle_ksel(topk_max, Nb);
+    double *qbar = (double *)malloc(sizeof(double) * (size_t)Nb * d);
+    double *kbar = (double *)malloc(sizeof(double) * (size_t)Nb * d);
+    double *S = (double *)malloc(sizeof(double) * (size_t)Nb * Nb);
+    int32_t *kr = (int32_t *)malloc(sizeof(int32_t) * (size_t)Nb);
+    oracle_pool(q, N, d, blk, qbar);
+    oracle_pool(k, N, d, blk, kbar);
+    oracle_scores(qbar, kbar, Nb, Nb, d, S);
+    oracle_adaptive_k(S, Nb, Nb, N, blk, tau, kr, NULL);
+    int ksel = oracle_adaptive_ksel(kr, Nb, kmin, kmax);
+    if (k_rows)
+        memcpy(k_rows, kr, sizeof(int32_t) * (size_t)Nb);
+    free(qbar);
+    free(kbar);
+    free(S);
+    free(kr);
+    head_core(q, k, v, w, N, d, blk, ksel, kmax, quant, qblocks, nqb, out, out_s, out_l, idx_out);
     return ksel;
 }
 
