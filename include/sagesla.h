@@ -162,6 +162,48 @@ sagesla_status sagesla_fwd_noalloc(const void *q, const void *k, const void *v, 
                                    int B, int H, int N, int d, double topk, int block, void *out,
                                    sagesla_stream_t stream);
 
+/* ---- content-adaptive kept-block count ------------------------------------------------
+ * The pages fix a Top-K ratio (0.1-0.15 at inference: news.qq.com explainer, "From training
+ * to deployment") and name sparsity that follows the input as open work, without a rule
+ * (same page, "The limits of the technique", sixth challenge). Here the count follows the
+ * scores: with s_ij the block scores and n_j the valid tokens of key block j, query block i
+ * needs k_i = the fewest blocks, in selection order (score descending, lower index on
+ * ties), whose mass n_j exp(s_ij - max_j s_ij) reaches tau of its row's total; a head keeps
+ * k_head = clamp(ceil(sum_i k_i / Nb), kmin, kmax) blocks for every query block, where kmin
+ * and kmax are sagesla_ksel of topk_min and topk_max. The masses are fp64; a row whose
+ * prefix mass lies within rounding of tau times its total may resolve either way.
+ * Requires 0 < topk_min <= topk_max <= 1, 0 < tau <= 1 and Nb <= 8192 (N <= 524288;
+ * SAGESLA_ERR_UNSUPPORTED beyond).
+ *
+ * sagesla_adaptive_ksel: from the pooled means (QBAR, KBART as sagesla_pool writes them),
+ * k_rows int32 [BH][Nb] and k_head int32 [BH] (device, written).
+ *
+ * sagesla_fwd_adaptive: the forward with each head at its own count: the same steps as
+ * sagesla_fwd, with the counts computed after pooling. k_rows and k_head as above (device,
+ * written). The workspace holds the SAGESLA_WS_* regions at the offsets of
+ * sagesla_adaptive_workspace_layout; its IDX region is int32 [BH][Nb][kmax] with the head's
+ * k_head entries first in each row (best first, then ascending) and -1 after them. With
+ * proj, the linear branch runs for every head that leaves blocks out; a head at k_head = Nb
+ * adds nothing. Each head's output equals sagesla_fwd's on that head alone with
+ * topk = k_head / Nb. */
+sagesla_status sagesla_adaptive_workspace_size(int B, int H, int N, int d, int block, double topk_min,
+                                               double topk_max, int linear, size_t *bytes);
+
+sagesla_status sagesla_adaptive_workspace_layout(int B, int H, int N, int d, int block,
+                                                 double topk_min, double topk_max, int linear,
+                                                 size_t offsets[SAGESLA_WS_COUNT]);
+
+sagesla_status sagesla_adaptive_ksel(const void *qbar, const void *kbart, int B, int H, int N,
+                                     int d, int block, double topk_min, double topk_max,
+                                     double tau, void *k_rows, void *k_head,
+                                     sagesla_stream_t stream);
+
+sagesla_status sagesla_fwd_adaptive(const void *q, const void *k, const void *v, const void *proj,
+                                    int B, int H, int N, int d, double topk_min, double topk_max,
+                                    double tau, int block, void *out, void *k_rows, void *k_head,
+                                    void *workspace, size_t workspace_bytes,
+                                    sagesla_stream_t stream);
+
 /* ---- producer-side fusion -------------------------------------------------------------
  * The pages fuse the rewritten LayerNorm/RMSNorm kernels with their neighbours (news.qq.com
  * explainer, "Fourth key"). sagesla_prepare takes the QKV projection output qkv bf16

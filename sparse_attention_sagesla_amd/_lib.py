@@ -27,7 +27,8 @@ EXPORTS = ["sagesla_version", "sagesla_status_string", "sagesla_ksel", "sagesla_
            "sagesla_w8a8_sizes", "sagesla_w8a8_quant_weight", "sagesla_w8a8_quant_act", "sagesla_w8a8_gemm",
            "sagesla_sla_workspace_size", "sagesla_sla_workspace_layout", "sagesla_sla_fwd", "sagesla_sla_bwd",
            "sagesla_prepare", "sagesla_fwd_prepared", "sagesla_fwd_tensors", "sagesla_pool_select",
-           "sagesla_quantize", "sagesla_linear_states", "sagesla_fwd_noalloc"]
+           "sagesla_quantize", "sagesla_linear_states", "sagesla_fwd_noalloc", "sagesla_adaptive_workspace_size",
+           "sagesla_adaptive_workspace_layout", "sagesla_adaptive_ksel", "sagesla_fwd_adaptive"]
 
 # sagesla_dtype values and the sagesla_tensor descriptor
 DT_BF16, DT_F32, DT_I8, DT_FP8E4M3, DT_I32, DT_U8 = range(6)
@@ -103,6 +104,10 @@ def lib():
             "sagesla_quantize": (i32, [P, P, P, P] + dims + [i32, P, P, P, P]),
             "sagesla_linear_states": (i32, [P, P, P, P] + dims + [i32] + [P] * 6 + [P]),
             "sagesla_fwd_noalloc": (i32, [P, P, P, P] + dims + [f64, i32, P, P]),
+            "sagesla_adaptive_workspace_size": (i32, dims + [i32, f64, f64, i32, C.POINTER(sz)]),
+            "sagesla_adaptive_workspace_layout": (i32, dims + [i32, f64, f64, i32, C.POINTER(sz * WS_COUNT)]),
+            "sagesla_adaptive_ksel": (i32, [P, P] + dims + [i32, f64, f64, f64, P, P, P]),
+            "sagesla_fwd_adaptive": (i32, [P, P, P, P] + dims + [f64, f64, f64, i32, P, P, P, P, sz, P]),
         }
         for name, (res, args) in sigs.items():
             fn = getattr(L, name)
@@ -190,8 +195,11 @@ def fwd(q, k, v, proj=None, topk=0.1, block=64, out=None, workspace=None, stream
 def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict:
     """Typed torch views of the intermediates left in a workspace by fwd()."""
     lay = workspace_layout(B, H, N, d, block, topk, linear)
-    BH, Nb = B * H, (N + block - 1) // block
-    k = ksel(N, topk, block)
+    return _views(ws, lay, B * H, N, d, block, ksel(N, topk, block))
+
+
+def _views(ws, lay, BH, N, d, block, k):
+    Nb = (N + block - 1) // block
     Nc = (Nb + 15) // 16
     Ng = (Nb + GROUP - 1) // GROUP
     SE = 129 * d
@@ -216,6 +224,70 @@ def workspace_views(ws, B, H, N, d=128, block=64, topk=0.1, linear=True) -> dict
             continue
         out[name] = ws[off:off + nbytes].view(dt).view(shape)
     return out
+
+
+# ---------------------------------------------------------------- content-adaptive count
+
+def adaptive_workspace_size(B, H, N, d=128, block=64, topk_min=0.05, topk_max=0.25, linear=True) -> int:
+    out = C.c_size_t()
+    _check(lib().sagesla_adaptive_workspace_size(B, H, N, d, block, float(topk_min), float(topk_max),
+                                                 int(bool(linear)), C.byref(out)), "sagesla_adaptive_workspace_size")
+    return out.value
+
+
+def adaptive_workspace_layout(B, H, N, d=128, block=64, topk_min=0.05, topk_max=0.25, linear=True) -> dict:
+    arr = (C.c_size_t * WS_COUNT)()
+    _check(lib().sagesla_adaptive_workspace_layout(B, H, N, d, block, float(topk_min), float(topk_max),
+                                                   int(bool(linear)), C.byref(arr)),
+           "sagesla_adaptive_workspace_layout")
+    return {name: arr[i] for i, name in enumerate(WS_REGIONS)}
+
+
+def adaptive_workspace_views(ws, B, H, N, d=128, block=64, topk_min=0.05, topk_max=0.25, linear=True) -> dict:
+    """Typed views of what fwd_adaptive() leaves in its workspace; idx is [BH, Nb, kmax]."""
+    lay = adaptive_workspace_layout(B, H, N, d, block, topk_min, topk_max, linear)
+    return _views(ws, lay, B * H, N, d, block, ksel(N, topk_max, block))
+
+
+def adaptive_ksel(qbar, kbart, B, H, N, topk_min=0.05, topk_max=0.25, tau=0.9, d=128, block=64, k_rows=None,
+                  k_head=None, stream=None):
+    """Per-row and per-head content-adaptive counts from the pooled means. Returns (k_rows
+    int32 [B*H, Nb], k_head int32 [B*H])."""
+    Nb = (N + block - 1) // block
+    if k_rows is None:
+        k_rows = torch.empty(B * H, Nb, dtype=torch.int32, device=qbar.device)
+    if k_head is None:
+        k_head = torch.empty(B * H, dtype=torch.int32, device=qbar.device)
+    _check(lib().sagesla_adaptive_ksel(_ptr(qbar), _ptr(kbart), B, H, N, d, block, float(topk_min),
+                                       float(topk_max), float(tau), _ptr(k_rows), _ptr(k_head), _stream(stream)),
+           "sagesla_adaptive_ksel")
+    return k_rows, k_head
+
+
+def fwd_adaptive(q, k, v, proj=None, topk_min=0.05, topk_max=0.25, tau=0.9, block=64, out=None, k_rows=None,
+                 k_head=None, workspace=None, stream=None):
+    """The forward with a content-adaptive count per head. Returns (out, k_rows, k_head)."""
+    B, H, N, d = _shape(q)
+    for x in (k, v):
+        if _shape(x) != q.shape:
+            raise ValueError("q, k, v shapes differ")
+    if proj is not None and (proj.shape != (d, d) or proj.dtype != torch.bfloat16 or not proj.is_contiguous()):
+        raise ValueError("proj must be a contiguous bf16 [d, d] tensor")
+    Nb = (N + block - 1) // block
+    if out is None:
+        out = torch.empty_like(q)
+    if k_rows is None:
+        k_rows = torch.empty(B * H, Nb, dtype=torch.int32, device=q.device)
+    if k_head is None:
+        k_head = torch.empty(B * H, dtype=torch.int32, device=q.device)
+    if workspace is None:
+        n = adaptive_workspace_size(B, H, N, d, block, topk_min, topk_max, proj is not None)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    st = lib().sagesla_fwd_adaptive(_ptr(q), _ptr(k), _ptr(v), _ptr(proj), B, H, N, d, float(topk_min),
+                                    float(topk_max), float(tau), block, _ptr(out), _ptr(k_rows), _ptr(k_head),
+                                    _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "sagesla_fwd_adaptive")
+    return out, k_rows, k_head
 
 
 # ---------------------------------------------------------------- W8A8 linear layer

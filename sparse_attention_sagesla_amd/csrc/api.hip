@@ -14,13 +14,20 @@ hipError_t launch_pool(const void*, const void*, const void*, int, int, int, voi
                        void*, void*, hipStream_t);
 hipError_t launch_head_stats(const void*, const void*, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_select(const void*, const void*, int, int, int, void*, hipStream_t);
+hipError_t launch_select(const void*, const void*, int, int, int, const void*, int, void*, hipStream_t);
+int adaptive_max_blocks();
+hipError_t launch_adaptive_ksel(const void*, const void*, int, int, int, double, int, int, void*, void*, hipStream_t);
 hipError_t launch_quant_kv(const void*, const void*, const void*, const void*, int, int, int, void*, void*,
                            void*, void*, void*, hipStream_t);
 hipError_t launch_linear_total(const void*, int, int, void*, hipStream_t);
 hipError_t launch_linear_complement(const void*, const void*, const void*, const void*, const void*, int, int,
                                     int, int, void*, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_linear_complement(const void*, const void*, const void*, int, const void*, const void*, const void*,
+                                    int, int, int, int, void*, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
                               const void*, const void*, int, int, int, int, void*, hipStream_t);
+hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
+                              const void*, const void*, int, const void*, int, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_relayout(const void*, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_kept_mask(const void*, int, int, int, void*, hipStream_t);
 hipError_t launch_sla_relayout_hd(const void*, int, int, int, void*, hipStream_t);
@@ -88,6 +95,18 @@ sagesla_status check_sizes(int B, int H, int N, int d, int block, Geom* gm) {
 sagesla_status check_topk(double topk, Geom* gm) {
   if (!(topk > 0.0 && topk <= 1.0)) return SAGESLA_ERR_INVALID_ARGUMENT;
   gm->ksel = ksel_of(gm->Nb, topk);
+  return SAGESLA_OK;
+}
+
+// Content-adaptive counts: 0 < topk_min <= topk_max <= 1, 0 < tau <= 1, and at most
+// adaptive_max_blocks() key blocks. gm->ksel becomes the largest count (the row stride of
+// the kept lists); *kmin the smallest.
+sagesla_status check_adaptive(double topk_min, double topk_max, double tau, Geom* gm, int* kmin) {
+  if (!(topk_min > 0.0 && topk_min <= topk_max && topk_max <= 1.0) || !(tau > 0.0 && tau <= 1.0))
+    return SAGESLA_ERR_INVALID_ARGUMENT;
+  if (gm->Nb > adaptive_max_blocks()) return SAGESLA_ERR_UNSUPPORTED;
+  *kmin = ksel_of(gm->Nb, topk_min);
+  gm->ksel = ksel_of(gm->Nb, topk_max);
   return SAGESLA_OK;
 }
 
@@ -168,7 +187,8 @@ const char* sagesla_status_string(sagesla_status s) {
   switch (s) {
     case SAGESLA_OK: return "ok";
     case SAGESLA_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case SAGESLA_ERR_UNSUPPORTED: return "unsupported (d must be 128, block 64, device gfx950)";
+    case SAGESLA_ERR_UNSUPPORTED:
+      return "unsupported (d must be 128, block 64, device gfx950; the adaptive count takes at most 8192 blocks)";
     case SAGESLA_ERR_WORKSPACE: return "workspace too small";
     case SAGESLA_ERR_HIP: return "HIP runtime error";
   }
@@ -377,6 +397,102 @@ sagesla_status sagesla_fwd_noalloc(const void* q, const void* k, const void* v, 
   if ((s = scratch_address(&ws)) != SAGESLA_OK) return s;
   return run_fwd(q, k, v, proj, B, H, N, d, topk, block, out, ws, (size_t)SAGESLA_NOALLOC_SCRATCH_BYTES, stream,
                  false);
+}
+
+// ---------------------------------------------------------------- content-adaptive count
+
+// The adaptive forward's workspace: the fixed-count layout at the largest count, with the
+// linear regions whenever some head may leave blocks out (kmin < Nb).
+static sagesla_status adaptive_layout(int B, int H, int N, int d, int block, double topk_min, double topk_max,
+                                      double tau, int linear, Geom* gm, int* kmin, size_t off[SAGESLA_WS_COUNT],
+                                      size_t* total) {
+  sagesla_status s = check_sizes(B, H, N, d, block, gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_adaptive(topk_min, topk_max, tau, gm, kmin)) != SAGESLA_OK) return s;
+  layout(*gm, linear != 0 && *kmin < gm->Nb, off, total);
+  return SAGESLA_OK;
+}
+
+sagesla_status sagesla_adaptive_workspace_size(int B, int H, int N, int d, int block, double topk_min,
+                                               double topk_max, int linear, size_t* bytes) {
+  Geom gm;
+  int kmin;
+  size_t off[SAGESLA_WS_COUNT];
+  if (!bytes) return SAGESLA_ERR_INVALID_ARGUMENT;
+  return adaptive_layout(B, H, N, d, block, topk_min, topk_max, 1.0, linear, &gm, &kmin, off, bytes);
+}
+
+sagesla_status sagesla_adaptive_workspace_layout(int B, int H, int N, int d, int block, double topk_min,
+                                                 double topk_max, int linear, size_t offsets[SAGESLA_WS_COUNT]) {
+  Geom gm;
+  int kmin;
+  size_t total;
+  if (!offsets) return SAGESLA_ERR_INVALID_ARGUMENT;
+  return adaptive_layout(B, H, N, d, block, topk_min, topk_max, 1.0, linear, &gm, &kmin, offsets, &total);
+}
+
+sagesla_status sagesla_adaptive_ksel(const void* qbar, const void* kbart, int B, int H, int N, int d, int block,
+                                     double topk_min, double topk_max, double tau, void* k_rows, void* k_head,
+                                     sagesla_stream_t stream) {
+  Geom gm;
+  int kmin;
+  sagesla_status s = check_sizes(B, H, N, d, block, &gm);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_adaptive(topk_min, topk_max, tau, &gm, &kmin)) != SAGESLA_OK) return s;
+  if ((s = check_ptrs({qbar, kbart, k_rows, k_head})) != SAGESLA_OK) return s;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  return from_hip(launch_adaptive_ksel(qbar, kbart, gm.BH, gm.N, gm.Nb, tau, kmin, gm.ksel, k_rows, k_head,
+                                       (hipStream_t)stream));
+}
+
+sagesla_status sagesla_fwd_adaptive(const void* q, const void* k, const void* v, const void* proj, int B, int H,
+                                    int N, int d, double topk_min, double topk_max, double tau, int block, void* out,
+                                    void* k_rows, void* k_head, void* workspace, size_t workspace_bytes,
+                                    sagesla_stream_t stream) {
+  Geom gm;
+  int kmin;
+  size_t off[SAGESLA_WS_COUNT], total;
+  sagesla_status s =
+      adaptive_layout(B, H, N, d, block, topk_min, topk_max, tau, proj != nullptr, &gm, &kmin, off, &total);
+  if (s != SAGESLA_OK) return s;
+  if ((s = check_ptrs({q, k, v, out, k_rows, k_head, workspace})) != SAGESLA_OK) return s;
+  if ((s = check_opt_ptr(proj)) != SAGESLA_OK) return s;
+  if (workspace_bytes < total) return SAGESLA_ERR_WORKSPACE;
+  if ((s = check_device()) != SAGESLA_OK) return s;
+  const bool linear = proj != nullptr && kmin < gm.Nb;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  auto P = [&](int r) { return (void*)(ws + off[r]); };
+  const int kmax = gm.ksel;
+  hipError_t e;
+  if ((e = launch_pool(q, k, v, gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), P(SAGESLA_WS_KSUM),
+                       P(SAGESLA_WS_VAMAXB), P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_KMEAN),
+                             P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_adaptive_ksel(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.N, gm.Nb, tau, kmin, kmax, k_rows,
+                                k_head, st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, kmax, k_head, kmax,
+                         P(SAGESLA_WS_IDX), st)) != hipSuccess)
+    return from_hip(e);
+  if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_K8),
+                           P(SAGESLA_WS_SK), P(SAGESLA_WS_V8), linear ? P(SAGESLA_WS_HS) : nullptr,
+                           linear ? P(SAGESLA_WS_HPART) : nullptr, st)) != hipSuccess)
+    return from_hip(e);
+  if (linear) {
+    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st)) != hipSuccess)
+      return from_hip(e);
+    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), k_head, kmax, P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj,
+                                      gm.BH, gm.N, gm.Nb, kmax, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
+                                      P(SAGESLA_WS_UCOUNT), P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
+      return from_hip(e);
+  }
+  return from_hip(launch_sparse_attn(P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), P(SAGESLA_WS_K8), P(SAGESLA_WS_SK),
+                                     P(SAGESLA_WS_V8), P(SAGESLA_WS_VAMAX), P(SAGESLA_WS_IDX), k_head, kmax,
+                                     linear ? P(SAGESLA_WS_Y) : nullptr, gm.BH, gm.N, gm.Nb, kmax, out, st));
 }
 
 // ---------------------------------------------------------------- grouped stages

@@ -30,8 +30,11 @@ constexpr int kUnionRange = 1024;  // key blocks per LDS pass of the union kerne
 // complement != 0 (more than half the blocks kept): the same for the blocks NOT kept,
 // so that the complement is summed directly instead of as total - kept (which would
 // cancel almost all of the total and leave the bf16 rounding of the kept states).
+// With khead the head keeps khead[bh] blocks (rows of idx kstride apart) and takes the
+// complement form on its own count; else every head keeps ksel.
 __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __restrict__ idx, int Nb, int ksel,
-                                                           int ngroups, int complement,
+                                                           const int32_t* __restrict__ khead, int kstride,
+                                                           int ngroups, int complement_all,
                                                            int32_t* __restrict__ ulist,
                                                            uint32_t* __restrict__ umask,
                                                            int32_t* __restrict__ ucount) {
@@ -42,6 +45,8 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
   const int q0 = grp * kGroup, nq = min(kGroup, Nb - q0);
   const size_t gbase = (size_t)bh * ngroups + grp;
   const int nw = (Nb + 31) / 32;
+  const int ks = khead ? khead[bh] : ksel;
+  const int complement = khead ? (2 * ks > Nb) : complement_all;
   uint32_t* mrow = umask + gbase * kGroup * nw;
   for (int e = t; e < kGroup * nw; e += 256) mrow[e] = 0u;
   int count = 0;
@@ -49,10 +54,10 @@ __global__ __launch_bounds__(256) void linear_union_kernel(const int32_t* __rest
     const int rl = min(kUnionRange, Nb - r0);
     for (int e = t; e < rl * kMaskWords; e += 256) (&s_flags[0][0])[e] = 0u;
     __syncthreads();
-    const int32_t* src = idx + ((size_t)bh * Nb + q0) * ksel;
-    for (int e = t; e < nq * ksel; e += 256) {
-      const int j = src[e] - r0;
-      const int qb = e / ksel;
+    const int32_t* src = idx + ((size_t)bh * Nb + q0) * kstride;
+    for (int e = t; e < nq * ks; e += 256) {
+      const int qb = e / ks;
+      const int j = src[(size_t)qb * kstride + e % ks] - r0;
       if (j >= 0 && j < rl) atomicOr(&s_flags[j][qb >> 5], 1u << (qb & 31));
     }
     __syncthreads();
@@ -202,8 +207,8 @@ __device__ __forceinline__ int mg_pos(int r, int cc) { return cc ^ (2 * ((r & 3)
 // 256-byte row slice of the states run together on one XCD and share its L2.
 __global__ __launch_bounds__(256, 2) void linear_mask_gemm_kernel(
     const uint16_t* __restrict__ hs, const float* __restrict__ htot, const int32_t* __restrict__ ulist,
-    const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, int Nb, int ngroups,
-    int complement, int ntiles, int per_xcd, uint16_t* __restrict__ hc) {
+    const uint32_t* __restrict__ umask, const int32_t* __restrict__ ucount, const int32_t* __restrict__ khead,
+    int Nb, int ngroups, int complement_all, int ntiles, int per_xcd, uint16_t* __restrict__ hc) {
   __shared__ __attribute__((aligned(16))) MgSlot s0, s1, s2, s3;
   __shared__ __attribute__((aligned(8))) uint2 s_nib[16];  // nibble -> its 4 bits as bf16 0.0 / 1.0
 
@@ -212,6 +217,7 @@ __global__ __launch_bounds__(256, 2) void linear_mask_gemm_kernel(
   const int per_bh = ngroups * 129;
   const int bh = tile / per_bh, rem = tile % per_bh;
   const int grp = rem % ngroups, c = rem / ngroups;
+  const int complement = khead ? (2 * khead[bh] > Nb) : complement_all;
   const size_t gbase = (size_t)bh * ngroups + grp;
   const int U = ucount[gbase];
   const int32_t* ul = ulist + gbase * Nb;
@@ -397,9 +403,11 @@ __device__ __forceinline__ void out_load(OutLoads& L, const uint16_t* q, const u
 // contiguous row (S^c from memory, phi and O_l from LDS) or a transposing LDS read of
 // row-major W, and each lane ends with 4 consecutive channels of one row.
 // Wave w owns channels 32 w .. 32 w + 31 of both products, for all 64 rows.
+// A head that keeps every block (khead[bh] = Nb) has no complement: its y is zero.
 __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ hc,
-                                                         const uint16_t* __restrict__ proj, int N, int Nb,
+                                                         const uint16_t* __restrict__ proj,
+                                                         const int32_t* __restrict__ khead, int N, int Nb,
                                                          int groups, int per_xcd, uint16_t* __restrict__ y) {
   __shared__ __attribute__((aligned(16))) uint16_t s_w[kD * kLs];    // W_proj [a][c]
   __shared__ __attribute__((aligned(16))) uint16_t s_a[kBlk * kLs];  // phi(Q) [m][a], then O_l [m][c]
@@ -412,6 +420,12 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
   const int bh = gid / nqb, i0 = (gid % nqb) * kOutQB, i1 = min(Nb, i0 + kOutQB);
   const int t = threadIdx.x, lane = t & 63, g = lane >> 5, r = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  if (khead && khead[bh] >= Nb) {
+    const size_t r0 = (size_t)i0 * kBlk, r1 = min((size_t)i1 * kBlk, (size_t)N);
+    uint4* dst = (uint4*)(y + ((size_t)bh * N + r0) * kD);
+    for (size_t e = t; e < (r1 - r0) * (kD / 8); e += 256) dst[e] = make_uint4(0u, 0u, 0u, 0u);
+    return;
+  }
 
   OutLoads la, lb;
   out_load(la, q, hc, bh, i0, N, Nb, t, w, lane);
@@ -541,49 +555,71 @@ int linear_groups(int Nb) { return (Nb + kGroup - 1) / kGroup; }
 static int use_complement_sets(int Nb, int ksel) { return 2 * ksel > Nb; }
 
 static void launch_mask_gemm(const void* hs, const void* htot, const void* ulist, const void* umask,
-                             const void* ucount, int BH, int Nb, int ksel, void* hc, hipStream_t st) {
+                             const void* ucount, const void* khead, int BH, int Nb, int ksel, void* hc,
+                             hipStream_t st) {
   const int ng = linear_groups(Nb);
   const int ntiles = BH * ng * 129, per_xcd = (ntiles + 7) / 8;
   hipLaunchKernelGGL(linear_mask_gemm_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)hs,
                      (const float*)htot, (const int32_t*)ulist, (const uint32_t*)umask, (const int32_t*)ucount,
-                     Nb, ng, use_complement_sets(Nb, ksel), ntiles, per_xcd, (uint16_t*)hc);
+                     (const int32_t*)khead, Nb, ng, use_complement_sets(Nb, ksel), ntiles, per_xcd, (uint16_t*)hc);
+}
+
+static hipError_t launch_union(const void* idx, const void* khead, int kstride, int BH, int Nb, int ksel,
+                               void* ulist, void* umask, void* ucount, hipStream_t st) {
+  const int ng = linear_groups(Nb);
+  hipLaunchKernelGGL(linear_union_kernel, dim3(BH * ng), dim3(256), 0, st, (const int32_t*)idx, Nb, ksel,
+                     (const int32_t*)khead, kstride, ng, use_complement_sets(Nb, ksel), (int32_t*)ulist,
+                     (uint32_t*)umask, (int32_t*)ucount);
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_union(const void* idx, int BH, int Nb, int ksel, void* ulist, void* umask, void* ucount,
                               hipStream_t st) {
-  const int ng = linear_groups(Nb);
-  hipLaunchKernelGGL(linear_union_kernel, dim3(BH * ng), dim3(256), 0, st, (const int32_t*)idx, Nb, ksel, ng,
-                     use_complement_sets(Nb, ksel), (int32_t*)ulist, (uint32_t*)umask, (int32_t*)ucount);
+  return launch_union(idx, nullptr, ksel, BH, Nb, ksel, ulist, umask, ucount, st);
+}
+
+static hipError_t launch_masked(const void* q, const void* hs, const void* htot, const void* proj,
+                                const void* khead, int BH, int N, int Nb, int ksel, const void* ulist,
+                                const void* umask, const void* ucount, void* hc, void* y, hipStream_t st) {
+  launch_mask_gemm(hs, htot, ulist, umask, ucount, khead, BH, Nb, ksel, hc, st);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
+  const int per_xcd = (groups + 7) / 8;
+  hipLaunchKernelGGL(linear_out_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q,
+                     (const uint16_t*)hc, (const uint16_t*)proj, (const int32_t*)khead, N, Nb, groups, per_xcd,
+                     (uint16_t*)y);
   return hipGetLastError();
 }
 
 hipError_t launch_linear_masked(const void* q, const void* hs, const void* htot, const void* proj, int BH, int N,
                                 int Nb, int ksel, const void* ulist, const void* umask, const void* ucount, void* hc,
                                 void* y, hipStream_t st) {
-  launch_mask_gemm(hs, htot, ulist, umask, ucount, BH, Nb, ksel, hc, st);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int groups = BH * ((Nb + kOutQB - 1) / kOutQB);
-  const int per_xcd = (groups + 7) / 8;
-  hipLaunchKernelGGL(linear_out_kernel, dim3(per_xcd * 8), dim3(256), 0, st, (const uint16_t*)q,
-                     (const uint16_t*)hc, (const uint16_t*)proj, N, Nb, groups, per_xcd, (uint16_t*)y);
-  return hipGetLastError();
+  return launch_masked(q, hs, htot, proj, nullptr, BH, N, Nb, ksel, ulist, umask, ucount, hc, y, st);
 }
 
 // The masked complement product alone, on lists built elsewhere (the backward passes
 // state gradients through it with the kept relation transposed).
 hipError_t launch_linear_mask_gemm(const void* hs, const void* htot, const void* ulist, const void* umask,
                                    const void* ucount, int BH, int Nb, int ksel, void* hc, hipStream_t st) {
-  launch_mask_gemm(hs, htot, ulist, umask, ucount, BH, Nb, ksel, hc, st);
+  launch_mask_gemm(hs, htot, ulist, umask, ucount, nullptr, BH, Nb, ksel, hc, st);
   return hipGetLastError();
+}
+
+// khead: per-head counts (int32 [BH]) or NULL for ksel everywhere; idx rows are kstride apart.
+hipError_t launch_linear_complement(const void* q, const void* idx, const void* khead, int kstride, const void* hs,
+                                    const void* htot, const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
+                                    void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
+  hipError_t e = launch_union(idx, khead, kstride, BH, Nb, ksel, ulist, umask, ucount, st);
+  if (e != hipSuccess) return e;
+  return launch_masked(q, hs, htot, proj, khead, BH, N, Nb, ksel, ulist, umask, ucount, hc, y, st);
 }
 
 hipError_t launch_linear_complement(const void* q, const void* idx, const void* hs, const void* htot,
                                     const void* proj, int BH, int N, int Nb, int ksel, void* ulist,
                                     void* umask, void* ucount, void* hc, void* y, hipStream_t st) {
-  hipError_t e = launch_linear_union(idx, BH, Nb, ksel, ulist, umask, ucount, st);
-  if (e != hipSuccess) return e;
-  return launch_linear_masked(q, hs, htot, proj, BH, N, Nb, ksel, ulist, umask, ucount, hc, y, st);
+  return launch_linear_complement(q, idx, nullptr, ksel, hs, htot, proj, BH, N, Nb, ksel, ulist, umask, ucount, hc,
+                                  y, st);
 }
 
 }  // namespace sagesla

@@ -225,8 +225,8 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
 __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
     const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
-    const int32_t* __restrict__ idx, const uint16_t* __restrict__ y, int N, int Nb, int ksel, int tiles,
-    int per_xcd, float c0, uint16_t* __restrict__ out) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ khead, const uint16_t* __restrict__ y, int N,
+    int Nb, int ksel, int kstride, int tiles, int per_xcd, float c0, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kBlkBytes];
@@ -237,8 +237,9 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   const int t = threadIdx.x, l = t & 63, g = l >> 5, r = l & 31;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // wave index (uniform)
   const size_t hb = (size_t)bh * Nb;
-  const int32_t* crit = idx + (hb + i) * ksel;
-  const int last = ksel - 1;
+  const int nk = khead ? khead[bh] : ksel;  // kept blocks of this head
+  const int32_t* crit = idx + (hb + i) * kstride;
+  const int last = nk - 1;
   const int nlast = block_len(Nb - 1, N);  // valid keys in the last block
   const bool has_partial = nlast < kBlk;
   // wave 0 streams K code tiles, wave 1 V code tiles, by buffer loads into LDS: the
@@ -344,11 +345,11 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   // even steps: K(u) in s_k0, V(u) to s_v0; odd steps the other slots
   step(0, s_k0, s_k1, s_v0, s_v1, SA, SB, PB, PA, std::false_type{});
   int u = 1;
-  for (; u + 1 < ksel; u += 2) {
+  for (; u + 1 < nk; u += 2) {
     step(u, s_k1, s_k0, s_v1, s_v0, SB, SA, PA, PB, std::true_type{});
     step(u + 1, s_k0, s_k1, s_v0, s_v1, SA, SB, PB, PA, std::true_type{});
   }
-  if (u < ksel) step(u, s_k1, s_k0, s_v1, s_v0, SB, SA, PA, PB, std::true_type{});
+  if (u < nk) step(u, s_k1, s_k0, s_v1, s_v0, SB, SA, PA, PB, std::true_type{});
   // the last block's PV: V(last) and its weights (PA if last is even, PB if odd)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -397,16 +398,23 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
   }
 }
 
+// khead: per-head counts (int32 [BH]) or NULL for ksel everywhere; idx rows are kstride apart.
 hipError_t launch_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk,
-                              const void* v8, const void* vamax, const void* idx, const void* y, int BH,
-                              int N, int Nb, int ksel, void* out, hipStream_t st) {
+                              const void* v8, const void* vamax, const void* idx, const void* khead, int kstride,
+                              const void* y, int BH, int N, int Nb, int ksel, void* out, hipStream_t st) {
   const int tiles = BH * Nb;
   const int per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const int8_t*)q8,
                      (const float*)sq, (const int8_t*)k8, (const float*)sk, (const uint8_t*)v8,
-                     (const float*)vamax, (const int32_t*)idx, (const uint16_t*)y, N, Nb, ksel, tiles,
-                     per_xcd, log2e_over_sqrt_d(), (uint16_t*)out);
+                     (const float*)vamax, (const int32_t*)idx, (const int32_t*)khead, (const uint16_t*)y, N, Nb,
+                     ksel, kstride, tiles, per_xcd, log2e_over_sqrt_d(), (uint16_t*)out);
   return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk,
+                              const void* v8, const void* vamax, const void* idx, const void* y, int BH,
+                              int N, int Nb, int ksel, void* out, hipStream_t st) {
+  return launch_sparse_attn(q8, sq, k8, sk, v8, vamax, idx, nullptr, ksel, y, BH, N, Nb, ksel, out, st);
 }
 
 }  // namespace sagesla

@@ -264,3 +264,37 @@ def test_grouped_stage_entry_points_reject_bad_arguments():
 def test_header_documents_the_kept_list_order():
     text = open(HEADER).read()
     assert "best first" in text and "stored ascending" not in text
+
+
+def test_adaptive_entry_points_reject_on_host():
+    L = S.lib()
+    p = 0x10000
+    sz = C.c_size_t()
+    # topk_min <= topk_max within (0, 1]; tau within (0, 1]
+    for tmin, tmax, tau in [(0.0, 0.5, 0.5), (0.6, 0.5, 0.5), (0.1, 1.5, 0.5), (0.1, 0.5, 0.0), (0.1, 0.5, 1.01)]:
+        assert L.sagesla_adaptive_ksel(p, p, 1, 1, 4096, 128, 64, tmin, tmax, tau, p, p, None) == \
+            _lib.ERR_INVALID_ARGUMENT
+        assert L.sagesla_fwd_adaptive(p, p, p, None, 1, 1, 4096, 128, tmin, tmax, tau, 64, p, p, p, p, 1 << 30,
+                                      None) == _lib.ERR_INVALID_ARGUMENT
+    # more than 8192 key blocks is not supported; 8192 is
+    assert L.sagesla_adaptive_workspace_size(1, 1, 8193 * 64, 128, 64, 0.1, 0.2, 1, C.byref(sz)) == \
+        _lib.ERR_UNSUPPORTED
+    assert L.sagesla_fwd_adaptive(p, p, p, None, 1, 1, 8193 * 64, 128, 0.1, 0.2, 0.5, 64, p, p, p, p, 1 << 40,
+                                  None) == _lib.ERR_UNSUPPORTED
+    assert L.sagesla_adaptive_workspace_size(1, 1, 8192 * 64, 128, 64, 0.1, 0.2, 1, C.byref(sz)) == _lib.OK
+    # missing outputs, small workspace
+    assert L.sagesla_fwd_adaptive(p, p, p, None, 1, 1, 4096, 128, 0.1, 0.2, 0.5, 64, p, None, p, p, 1 << 30,
+                                  None) == _lib.ERR_INVALID_ARGUMENT
+    assert L.sagesla_fwd_adaptive(p, p, p, None, 1, 1, 4096, 128, 0.1, 0.2, 0.5, 64, p, p, p, p, 100, None) == \
+        _lib.ERR_WORKSPACE
+
+
+def test_adaptive_workspace_is_the_fixed_layout_at_the_largest_count():
+    # the same regions as the fixed-count forward at topk_max, with the linear regions
+    # whenever some head may leave blocks out
+    assert S.adaptive_workspace_layout(1, 3, 5000, topk_min=0.05, topk_max=0.25) == \
+        S.workspace_layout(1, 3, 5000, topk=0.25)
+    lay = S.adaptive_workspace_layout(1, 2, 1000, topk_min=0.1, topk_max=1.0)
+    assert lay["hs"] < S.adaptive_workspace_size(1, 2, 1000, topk_min=0.1, topk_max=1.0)
+    assert S.adaptive_workspace_size(1, 2, 1000, topk_min=1.0, topk_max=1.0) == \
+        S.workspace_size(1, 2, 1000, topk=1.0)
