@@ -431,8 +431,60 @@ def topk_sweep(args, cfg, x, topks=(0.05, 0.1, 0.15, 0.2, 0.25), heads=(0, 1)):
                      "executed_tops": round(ops / (ms * 1e-3) / 1e12, 1),
                      "rel_l2_vs_dense": [round(e, 4) for e in err]})
         del ws
+    adaptive = adaptive_sweep(args, x, dense, heads, out)
     return {"workload": "%s inputs, SageSLA forward at each top-k; dense fp32 attention of heads %s as the "
-                        "accuracy reference" % (cfg.name, list(heads)), "points": rows}
+                        "accuracy reference" % (cfg.name, list(heads)), "points": rows, "adaptive": adaptive}
+
+
+def adaptive_sweep(args, x, dense, heads, out, taus=(0.2, 0.3, 0.4, 0.5, 0.6), tmin=0.05, tmax=0.25):
+    """The forward with a content-adaptive count per head (k_head from the pooled masses at
+    tau, clamped to the top-k range [tmin, tmax]): ms per call, the counts it chose, the
+    count stage's own time, and the distance from dense attention on the same heads."""
+    import sparse_attention_sagesla_amd as S
+    q, k, v, proj = x["q"], x["k"], x["v"], x["proj"]
+    B, H, N, d = q.shape
+    Nb = (N + 63) // 64
+    nlen = torch.full((Nb,), 64, dtype=torch.int64, device=q.device)
+    nlen[-1] = N - 64 * (Nb - 1)
+    ws = torch.empty(S.adaptive_workspace_size(B, H, N, topk_min=tmin, topk_max=tmax, linear=proj is not None),
+                     dtype=torch.uint8, device=q.device)
+    k_rows = torch.empty(B * H, Nb, dtype=torch.int32, device=q.device)
+    k_head = torch.empty(B * H, dtype=torch.int32, device=q.device)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    rows = []
+    for tau in taus:
+        def fwd():
+            S.fwd_adaptive(q, k, v, proj, topk_min=tmin, topk_max=tmax, tau=tau, out=out, k_rows=k_rows,
+                           k_head=k_head, workspace=ws)
+        ms = timed(fwd)
+        views = S.adaptive_workspace_views(ws, B, H, N, topk_min=tmin, topk_max=tmax, linear=proj is not None)
+
+        def count_stage():
+            S.adaptive_ksel(views["qbar"], views["kbart"], B, H, N, topk_min=tmin, topk_max=tmax, tau=tau,
+                            k_rows=k_rows, k_head=k_head)
+        ms_count = timed(count_stage)
+        idx = views["idx"].long()
+        ops = 4.0 * d * float(((nlen[idx.clamp(min=0)] * (idx >= 0)).sum(-1) * nlen[None, :]).sum().item())
+        kh = k_head.cpu().numpy()
+        err = [float((out[0, h].float() - dense[n]).norm() / dense[n].norm()) for n, h in enumerate(heads)]
+        rows.append({"tau": tau, "ms": round(ms, 4), "count_stage_ms": round(ms_count, 4),
+                     "mean_topk": round(float(kh.mean()) / Nb, 4), "k_head_min": int(kh.min()),
+                     "k_head_max": int(kh.max()), "executed_tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                     "rel_l2_vs_dense": [round(e, 4) for e in err]})
+    del ws
+    return {"topk_range": [tmin, tmax], "points": rows}
 
 
 def sla_train_measure(args, cfg, x):

@@ -80,6 +80,9 @@ enum {
     SAGESLA_WS_UCOUNT,    /* int32 [BH][Ng]     union sizes                     (linear)   */
     SAGESLA_WS_HC,        /* bf16 [BH][Nb][129][d] complement states total - kept (linear) */
     SAGESLA_WS_Y,         /* bf16 [BH][N][d]    O_l W_proj                      (linear)   */
+    SAGESLA_WS_KEYS,      /* u64 [BH][Nb][Nb]   block scores as order-preserving keys (the
+                             fp64 bits, negatives complemented, positives with the sign bit
+                             set); only in the adaptive forward's workspace               */
     SAGESLA_WS_COUNT
 };
 /*

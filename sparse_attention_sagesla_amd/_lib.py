@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libsagesla.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 
 WS_REGIONS = ["qbar", "kbart", "ksum", "vamax_blk", "kmean", "vamax", "q8", "sq", "k8", "sk", "v8", "idx",
-              "hs", "hpart", "htot", "ulist", "umask", "ucount", "hc", "y"]
+              "hs", "hpart", "htot", "ulist", "umask", "ucount", "hc", "y", "keys"]
 WS_COUNT = len(WS_REGIONS)
 GROUP = 256  # query blocks per group of the linear-branch complement (union lists, masks)
 
@@ -214,6 +214,7 @@ def _views(ws, lay, BH, N, d, block, k):
         "htot": (torch.float32, (BH, 129, d)), "ulist": (torch.int32, (BH, Ng, Nb)),
         "umask": (torch.int32, (BH, Ng, (Nb + 31) // 32, GROUP)), "ucount": (torch.int32, (BH, Ng)),
         "hc": (torch.bfloat16, (BH, Nb, 129, d)), "y": (torch.bfloat16, (BH, N, d)),
+        "keys": (torch.int64, (BH, Nb, Nb)),
     }
     total = ws.numel()
     out = {}

@@ -14,9 +14,10 @@ hipError_t launch_pool(const void*, const void*, const void*, int, int, int, voi
                        void*, void*, hipStream_t);
 hipError_t launch_head_stats(const void*, const void*, int, int, int, void*, void*, hipStream_t);
 hipError_t launch_select(const void*, const void*, int, int, int, void*, hipStream_t);
-hipError_t launch_select(const void*, const void*, int, int, int, const void*, int, void*, hipStream_t);
+hipError_t launch_select(const void*, const void*, int, int, int, const void*, int, const void*, void*, hipStream_t);
 int adaptive_max_blocks();
-hipError_t launch_adaptive_ksel(const void*, const void*, int, int, int, double, int, int, void*, void*, hipStream_t);
+hipError_t launch_adaptive_ksel(const void*, const void*, int, int, int, double, int, int, void*, void*, void*,
+                                hipStream_t);
 hipError_t launch_quant_kv(const void*, const void*, const void*, const void*, int, int, int, void*, void*,
                            void*, void*, void*, hipStream_t);
 hipError_t launch_linear_total(const void*, int, int, void*, hipStream_t);
@@ -140,7 +141,8 @@ sagesla_status from_hip(hipError_t e) { return e == hipSuccess ? SAGESLA_OK : SA
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* total) {
+// keys: the score-key region of the adaptive forward
+void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* total, bool keys = false) {
   const size_t BH = gm.BH, Nb = gm.Nb, N = gm.N, D = kD, Nc = gm.Nc, Ng = gm.Ng, ks = gm.ksel;
   const size_t SE = kStateElems;
   size_t sz[SAGESLA_WS_COUNT] = {};
@@ -166,6 +168,7 @@ void layout(const Geom& gm, bool linear, size_t off[SAGESLA_WS_COUNT], size_t* t
     sz[SAGESLA_WS_HC] = BH * Nb * SE * 2;
     sz[SAGESLA_WS_Y] = BH * N * D * 2;
   }
+  if (keys) sz[SAGESLA_WS_KEYS] = BH * Nb * Nb * 8;
   size_t o = 0;
   for (int r = 0; r < SAGESLA_WS_COUNT; r++) {
     if (sz[r] == 0) continue;
@@ -409,7 +412,7 @@ static sagesla_status adaptive_layout(int B, int H, int N, int d, int block, dou
   sagesla_status s = check_sizes(B, H, N, d, block, gm);
   if (s != SAGESLA_OK) return s;
   if ((s = check_adaptive(topk_min, topk_max, tau, gm, kmin)) != SAGESLA_OK) return s;
-  layout(*gm, linear != 0 && *kmin < gm->Nb, off, total);
+  layout(*gm, linear != 0 && *kmin < gm->Nb, off, total, true);
   return SAGESLA_OK;
 }
 
@@ -441,7 +444,7 @@ sagesla_status sagesla_adaptive_ksel(const void* qbar, const void* kbart, int B,
   if ((s = check_adaptive(topk_min, topk_max, tau, &gm, &kmin)) != SAGESLA_OK) return s;
   if ((s = check_ptrs({qbar, kbart, k_rows, k_head})) != SAGESLA_OK) return s;
   if ((s = check_device()) != SAGESLA_OK) return s;
-  return from_hip(launch_adaptive_ksel(qbar, kbart, gm.BH, gm.N, gm.Nb, tau, kmin, gm.ksel, k_rows, k_head,
+  return from_hip(launch_adaptive_ksel(qbar, kbart, gm.BH, gm.N, gm.Nb, tau, kmin, gm.ksel, k_rows, k_head, nullptr,
                                        (hipStream_t)stream));
 }
 
@@ -473,10 +476,10 @@ sagesla_status sagesla_fwd_adaptive(const void* q, const void* k, const void* v,
                              P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_adaptive_ksel(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.N, gm.Nb, tau, kmin, kmax, k_rows,
-                                k_head, st)) != hipSuccess)
+                                k_head, P(SAGESLA_WS_KEYS), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, kmax, k_head, kmax,
-                         P(SAGESLA_WS_IDX), st)) != hipSuccess)
+                         P(SAGESLA_WS_KEYS), P(SAGESLA_WS_IDX), st)) != hipSuccess)
     return from_hip(e);
   if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_K8),
                            P(SAGESLA_WS_SK), P(SAGESLA_WS_V8), linear ? P(SAGESLA_WS_HS) : nullptr,

@@ -197,8 +197,8 @@ __device__ __forceinline__ void score_rows(const double* __restrict__ qbar, cons
 __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __restrict__ qbar,
                                                              const double* __restrict__ kbart, int Nb,
                                                              int ksel, const int32_t* __restrict__ khead,
-                                                             int kstride, int R, int groups,
-                                                             int32_t* __restrict__ idx) {
+                                                             int kstride, const uint64_t* __restrict__ keys_in,
+                                                             int R, int groups, int32_t* __restrict__ idx) {
   extern __shared__ uint64_t s_keys[];  // [R][Nb]
   __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
   __shared__ uint32_t s_hist[4][256];
@@ -207,7 +207,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
   const int nr = min(R, Nb - g0);
   const int t = threadIdx.x;
   const int ks = khead ? khead[bh] : ksel;
-  score_rows(qbar, kbart, Nb, bh, g0, nr, s_qb, s_keys);
+  if (keys_in) {  // the scores' keys, already computed for these rows
+    const uint64_t* src = keys_in + ((size_t)bh * Nb + g0) * Nb;
+    for (int e = t; e < nr * Nb; e += kSelThreads) s_keys[e] = src[e];
+    __syncthreads();
+  } else {
+    score_rows(qbar, kbart, Nb, bh, g0, nr, s_qb, s_keys);
+  }
 
   // ---- phase 2: one wave per row
   const int lane = t & 63, w = t >> 6;
@@ -253,66 +259,215 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
 }
 
 // Content-adaptive count, per row: the fewest blocks, in selection order, whose pooled
-// mass n_j exp(s_j - max s) reaches tau of the row's total. R rows per workgroup as in
-// select_kernel; dynamic LDS: keys [R][Nb] uint64, then the masses [R][Nb] fp64. Each
-// wave finds its row's count by bisection on k: the mass of the k largest keys is a sum
-// over the lanes' kept blocks in index order (the same order for every k, so it never
-// decreases as k grows, and at k = Nb it is the row total bit for bit).
-__global__ __launch_bounds__(kSelThreads) void adaptive_k_kernel(const double* __restrict__ qbar,
-                                                                 const double* __restrict__ kbart, int N, int Nb,
-                                                                 double tau, int R, int groups,
-                                                                 int32_t* __restrict__ k_rows) {
-  extern __shared__ uint64_t s_keys[];  // [R][Nb], then masses [R][Nb]
-  __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
-  __shared__ uint32_t s_hist[4][256];
+// mass n_j exp(s_j - max s) reaches T = tau * (row total). The row's keys and masses sit
+// in registers of a team of threads (one wave, or the whole workgroup for long rows):
+// team member p holds key blocks p + P m (m < M, P the team size).
+// With mass_ge(x) = the mass of the keys >= x (each member's sum in m order, then the
+// team's fixed reduction tree: every member gets the same bits, and the sum never grows
+// as x grows), the last block taken has the largest key x* with mass_ge(x*) >= T.
+// Bisection on the 64-bit key space finds it: the interval [lo, hi] holds x*,
+// mass_ge(lo) >= T and mass_ge(hi + 1) < T, and the search stops as soon as one key is
+// left in it. Then k = #(keys > x*) + r, where r counts the blocks with key x* that are
+// needed, in index order (1 unless scores are exactly equal).
 
+// Reductions over one wave.
+struct WaveTeam {
+  static constexpr int P = 64;
+  int lane;
+  __device__ int member() const { return lane; }
+  __device__ void sum(double& a, int& c) {
+    a = wave_sum(a);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  }
+  __device__ void max2(uint64_t& x, uint64_t& y) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      x = max(x, (uint64_t)__shfl_xor((long long)x, o));
+      y = max(y, (uint64_t)__shfl_xor((long long)y, o));
+    }
+  }
+  __device__ int from_leader(int v) { return __shfl(v, 0); }
+};
+
+// Reductions over the workgroup's four waves: the waves' butterflies, then the four
+// partial results in wave order from LDS. Two sets of slots used in turn, so one barrier
+// per reduction suffices.
+struct GroupTeam {
+  static constexpr int P = kSelThreads;
+  int t, lane, w, par;
+  double (*rd)[4];
+  int (*ri)[4];
+  uint64_t (*ru)[4][2];
+  __device__ int member() const { return t; }
+  __device__ void sum(double& a, int& c) {
+    a = wave_sum(a);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+    if (lane == 0) {
+      rd[par][w] = a;
+      ri[par][w] = c;
+    }
+    __syncthreads();
+    a = ((rd[par][0] + rd[par][1]) + rd[par][2]) + rd[par][3];
+    c = ri[par][0] + ri[par][1] + ri[par][2] + ri[par][3];
+    par ^= 1;
+  }
+  __device__ void max2(uint64_t& x, uint64_t& y) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      x = max(x, (uint64_t)__shfl_xor((long long)x, o));
+      y = max(y, (uint64_t)__shfl_xor((long long)y, o));
+    }
+    if (lane == 0) {
+      ru[par][w][0] = x;
+      ru[par][w][1] = y;
+    }
+    __syncthreads();
+    x = max(max(ru[par][0][0], ru[par][1][0]), max(ru[par][2][0], ru[par][3][0]));
+    y = max(max(ru[par][0][1], ru[par][1][1]), max(ru[par][2][1], ru[par][3][1]));
+    par ^= 1;
+  }
+  __device__ int from_leader(int v) {
+    if (t == 0) ri[par][0] = v;
+    __syncthreads();
+    v = ri[par][0];
+    par ^= 1;
+    return v;
+  }
+};
+
+// The count of one row (keys in LDS), the same value on every team member.
+template <int M, class Team>
+__device__ int row_count(const uint64_t* keys, int Nb, int N, double tau, Team& tm) {
+  const int p = tm.member();
+  // keys of absent blocks are 0, below the key of every finite score, with mass 0
+  uint64_t kv[M];
+  double mv[M];
+  uint64_t kmax = 0u, nmin = 0u;  // nmin: the largest ~key, i.e. ~(smallest key)
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    const int j = p + Team::P * m;
+    kv[m] = j < Nb ? keys[j] : 0u;
+    kmax = max(kmax, kv[m]);
+    if (j < Nb) nmin = max(nmin, ~kv[m]);
+  }
+  tm.max2(kmax, nmin);
+  const double mx = key_value(kmax);
+  double W = 0.0;
+  int cnt = 0;
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    const int j = p + Team::P * m;
+    mv[m] = j < Nb ? (double)block_len(j, N) * exp(key_value(kv[m]) - mx) : 0.0;
+    W += mv[m];
+  }
+  tm.sum(W, cnt);
+  const double T = tau * W;
+  uint64_t lo = ~nmin, hi = kmax;
+  cnt = Nb;  // keys in [lo, hi]
+  while (cnt > 1 && lo < hi) {
+    const uint64_t mid = hi - ((hi - lo) >> 1);  // in (lo, hi]
+    double a = 0.0;
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+      const bool ge = kv[m] >= mid;
+      a += ge ? mv[m] : 0.0;
+      c += (ge && kv[m] <= hi) ? 1 : 0;
+    }
+    tm.sum(a, c);
+    if (a >= T) {
+      lo = mid;
+      cnt = c;
+    } else {
+      hi = mid - 1;
+      cnt -= c;
+    }
+  }
+  // x*: the key in [lo, hi] (the only one, or lo == hi)
+  uint64_t xs = 0u, unused = 0u;
+#pragma unroll
+  for (int m = 0; m < M; m++)
+    if (kv[m] >= lo && kv[m] <= hi) xs = max(xs, kv[m]);
+  tm.max2(xs, unused);
+  double mgt = 0.0;
+  int cpk = 0;
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    mgt += kv[m] > xs ? mv[m] : 0.0;
+    cpk += (kv[m] > xs ? 1 : 0) + (kv[m] == xs ? 65536 : 0);
+  }
+  tm.sum(mgt, cpk);
+  const int cgt = cpk & 0xFFFF, neq = cpk >> 16;
+  int r = 1;
+  if (neq > 1) {
+    // equal scores at the boundary: taken in index order until the mass reaches T
+    if (p == 0) {
+      double run = mgt;
+      r = 0;
+      for (int j = 0; j < Nb && r < neq; j++) {
+        if (keys[j] != xs) continue;
+        r++;
+        run += (double)block_len(j, N) * exp(key_value(keys[j]) - mx);
+        if (run >= T) break;
+      }
+    }
+    r = tm.from_leader(r);
+  }
+  return cgt + r;
+}
+
+// One wave per row (rows of up to 64 M key blocks). R rows per workgroup as in
+// select_kernel; dynamic LDS: keys [R][Nb]. keys_out (may be NULL): the rows' keys
+// [BH][Nb][Nb], for the selection that follows.
+template <int M>
+__global__ __launch_bounds__(kSelThreads) void adaptive_k_wave_kernel(const double* __restrict__ qbar,
+                                                                      const double* __restrict__ kbart, int N,
+                                                                      int Nb, double tau, int R, int groups,
+                                                                      int32_t* __restrict__ k_rows,
+                                                                      uint64_t* __restrict__ keys_out) {
+  extern __shared__ uint64_t s_keys[];  // [R][Nb]
+  __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
   const int bh = blockIdx.x / groups, g0 = (blockIdx.x % groups) * R;
   const int nr = min(R, Nb - g0);
   const int t = threadIdx.x;
   score_rows(qbar, kbart, Nb, bh, g0, nr, s_qb, s_keys);
+  if (keys_out) {
+    uint64_t* dst = keys_out + ((size_t)bh * Nb + g0) * Nb;
+    for (int e = t; e < nr * Nb; e += kSelThreads) dst[e] = s_keys[e];
+  }
+  WaveTeam tm{t & 63};
+  for (int r = t >> 6; r < nr; r += 4) {
+    const int k = row_count<M>(s_keys + r * Nb, Nb, N, tau, tm);
+    if (tm.lane == 0) k_rows[(size_t)bh * Nb + g0 + r] = k;
+  }
+}
 
-  const int lane = t & 63, w = t >> 6;
-  uint32_t* hist = s_hist[w];
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int r = w; r < nr; r += 4) {
-    const uint64_t* keys = s_keys + r * Nb;
-    double* mass = (double*)(s_keys + (size_t)R * Nb) + (size_t)r * Nb;
-    uint64_t kmax = 0u;
-    for (int j = lane; j < Nb; j += 64) kmax = max(kmax, keys[j]);
-    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint64_t)__shfl_xor((long long)kmax, o));
-    const double mx = key_value(kmax);
-    double part = 0.0;
-    for (int j = lane; j < Nb; j += 64) {
-      const double m = (double)block_len(j, N) * exp(key_value(keys[j]) - mx);
-      mass[j] = m;
-      part += m;
-    }
-    const double T = tau * wave_sum(part);
-    // mass of the k largest keys (ties: the lower indices)
-    auto top_mass = [&](int k) {
-      const Threshold th = radix_threshold(keys, Nb, k, hist, lane);
-      double acc = 0.0;
-      int eq_seen = 0;
-      for (int j0 = 0; j0 < Nb; j0 += 64) {
-        const int j = j0 + lane;
-        const uint64_t um = j < Nb ? (keys[j] & th.mask) : 0u;
-        const bool eq = j < Nb && um == th.prefix;
-        const unsigned long long eqm = __ballot(eq);
-        const int eq_rank = eq_seen + __popcll(eqm & below);
-        if (j < Nb && (um > th.prefix || (eq && eq_rank < th.kk))) acc += mass[j];
-        eq_seen += __popcll(eqm);
-      }
-      return wave_sum(acc);
-    };
-    int lo = 1, hi = Nb;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (top_mass(mid) >= T)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    if (lane == 0) k_rows[(size_t)bh * Nb + g0 + r] = lo;
+// The whole workgroup per row (rows of up to 256 M key blocks), rows one after another.
+template <int M>
+__global__ __launch_bounds__(kSelThreads) void adaptive_k_group_kernel(const double* __restrict__ qbar,
+                                                                       const double* __restrict__ kbart, int N,
+                                                                       int Nb, double tau, int R, int groups,
+                                                                       int32_t* __restrict__ k_rows,
+                                                                       uint64_t* __restrict__ keys_out) {
+  extern __shared__ uint64_t s_keys[];  // [R][Nb]
+  __shared__ __attribute__((aligned(16))) double s_qb[8][kD];
+  __shared__ double s_rd[2][4];
+  __shared__ int s_ri[2][4];
+  __shared__ uint64_t s_ru[2][4][2];
+  const int bh = blockIdx.x / groups, g0 = (blockIdx.x % groups) * R;
+  const int nr = min(R, Nb - g0);
+  const int t = threadIdx.x;
+  score_rows(qbar, kbart, Nb, bh, g0, nr, s_qb, s_keys);
+  if (keys_out) {
+    uint64_t* dst = keys_out + ((size_t)bh * Nb + g0) * Nb;
+    for (int e = t; e < nr * Nb; e += kSelThreads) dst[e] = s_keys[e];
+  }
+  GroupTeam tm{t, t & 63, t >> 6, 0, s_rd, s_ri, s_ru};
+  for (int r = 0; r < nr; r++) {
+    const int k = row_count<M>(s_keys + r * Nb, Nb, N, tau, tm);
+    if (t == 0) k_rows[(size_t)bh * Nb + g0 + r] = k;
   }
 }
 
@@ -340,8 +495,9 @@ int select_rows_per_group(int Nb) {
 }
 
 // khead: per-head counts (int32 [BH]) or NULL for ksel everywhere; kstride >= every count.
+// keys_in: the rows' score keys (uint64 [BH][Nb][Nb], from the adaptive count) or NULL.
 hipError_t launch_select(const void* qbar, const void* kbart, int BH, int Nb, int ksel, const void* khead,
-                         int kstride, void* idx, hipStream_t st) {
+                         int kstride, const void* keys_in, void* idx, hipStream_t st) {
   const int R = select_rows_per_group(Nb);
   const int groups = (Nb + R - 1) / R;
   size_t lds = (size_t)R * Nb * sizeof(uint64_t);
@@ -350,32 +506,52 @@ hipError_t launch_select(const void* qbar, const void* kbart, int BH, int Nb, in
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(select_kernel, dim3(BH * groups), dim3(kSelThreads), lds, st, (const double*)qbar,
-                     (const double*)kbart, Nb, ksel, (const int32_t*)khead, kstride, R, groups, (int32_t*)idx);
+                     (const double*)kbart, Nb, ksel, (const int32_t*)khead, kstride, (const uint64_t*)keys_in, R,
+                     groups, (int32_t*)idx);
   return hipGetLastError();
 }
 
 hipError_t launch_select(const void* qbar, const void* kbart, int BH, int Nb, int ksel, void* idx,
                          hipStream_t st) {
-  return launch_select(qbar, kbart, BH, Nb, ksel, nullptr, ksel, idx, st);
+  return launch_select(qbar, kbart, BH, Nb, ksel, nullptr, ksel, nullptr, idx, st);
 }
 
-// The largest Nb the adaptive count supports: one row's keys and masses in 128 KiB of LDS.
-int adaptive_max_blocks() { return 8192; }
+// The largest Nb the adaptive count supports: 32 key blocks per thread.
+int adaptive_max_blocks() { return 32 * kSelThreads; }
 
-hipError_t launch_adaptive_ksel(const void* qbar, const void* kbart, int BH, int N, int Nb, double tau, int kmin,
-                                int kmax, void* k_rows, void* khead, hipStream_t st) {
-  int R = 4096 / Nb;
-  R = R < 1 ? 1 : (R > 8 ? 8 : R);
+template <class K>
+static hipError_t launch_adaptive_k(K kernel, const void* qbar, const void* kbart, int BH, int N, int Nb, double tau,
+                                    void* k_rows, void* keys_out, hipStream_t st) {
+  const int R = select_rows_per_group(Nb);
   const int groups = (Nb + R - 1) / R;
-  const size_t lds = (size_t)R * Nb * 16;
+  const size_t lds = (size_t)R * Nb * sizeof(uint64_t);
   if (lds > 65536) {
-    hipError_t e =
-        hipFuncSetAttribute((const void*)adaptive_k_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(adaptive_k_kernel, dim3(BH * groups), dim3(kSelThreads), lds, st, (const double*)qbar,
-                     (const double*)kbart, N, Nb, tau, R, groups, (int32_t*)k_rows);
-  hipError_t e = hipGetLastError();
+  hipLaunchKernelGGL(kernel, dim3(BH * groups), dim3(kSelThreads), lds, st, (const double*)qbar,
+                     (const double*)kbart, N, Nb, tau, R, groups, (int32_t*)k_rows, (uint64_t*)keys_out);
+  return hipGetLastError();
+}
+
+// keys_out: uint64 [BH][Nb][Nb] or NULL
+hipError_t launch_adaptive_ksel(const void* qbar, const void* kbart, int BH, int N, int Nb, double tau, int kmin,
+                                int kmax, void* k_rows, void* khead, void* keys_out, hipStream_t st) {
+  hipError_t e;
+#define SAGESLA_ADAPTIVE_K(KER) e = launch_adaptive_k(KER, qbar, kbart, BH, N, Nb, tau, k_rows, keys_out, st)
+  if (Nb <= 64 * 4)
+    SAGESLA_ADAPTIVE_K(adaptive_k_wave_kernel<4>);
+  else if (Nb <= 64 * 8)
+    SAGESLA_ADAPTIVE_K(adaptive_k_wave_kernel<8>);
+  else if (Nb <= 64 * 16)
+    SAGESLA_ADAPTIVE_K(adaptive_k_wave_kernel<16>);
+  else if (Nb <= 64 * 32)
+    SAGESLA_ADAPTIVE_K(adaptive_k_wave_kernel<32>);
+  else if (Nb <= kSelThreads * 16)
+    SAGESLA_ADAPTIVE_K(adaptive_k_group_kernel<16>);
+  else
+    SAGESLA_ADAPTIVE_K(adaptive_k_group_kernel<32>);
+#undef SAGESLA_ADAPTIVE_K
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(adaptive_head_kernel, dim3(BH), dim3(256), 0, st, (const int32_t*)k_rows, Nb, kmin, kmax,
                      (int32_t*)khead);

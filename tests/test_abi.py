@@ -67,7 +67,8 @@ def test_workspace_size_rejects(args, status):
 def test_workspace_layout_regions():
     lay = S.workspace_layout(1, 4, 1000, topk=0.2, linear=True)
     total = S.workspace_size(1, 4, 1000, topk=0.2, linear=True)
-    offs = sorted(lay.values())
+    assert lay["keys"] == total  # the score keys are the adaptive forward's alone
+    offs = sorted(o for name, o in lay.items() if name != "keys")
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs)  # every region present and distinct
     assert max(offs) < total
@@ -146,7 +147,7 @@ def test_w8a8_sizes():
 def test_sla_workspace_regions():
     lay = S.sla_workspace_layout(1, 4, 1000, topk=0.2, linear=True)
     total = S.sla_workspace_size(1, 4, 1000, topk=0.2, linear=True)
-    offs = sorted(lay.values())
+    offs = sorted(o for name, o in lay.items() if name != "keys")  # no score keys in training
     assert all(o % 256 == 0 for o in offs)
     assert len(set(offs)) == len(offs) and max(offs) < total
     # the training workspace holds the forward's regions at the same offsets
@@ -291,10 +292,16 @@ def test_adaptive_entry_points_reject_on_host():
 
 def test_adaptive_workspace_is_the_fixed_layout_at_the_largest_count():
     # the same regions as the fixed-count forward at topk_max, with the linear regions
-    # whenever some head may leave blocks out
-    assert S.adaptive_workspace_layout(1, 3, 5000, topk_min=0.05, topk_max=0.25) == \
-        S.workspace_layout(1, 3, 5000, topk=0.25)
+    # whenever some head may leave blocks out, plus the score keys [BH][Nb][Nb] at the end
+    B, H, N = 1, 3, 5000
+    Nb = (N + 63) // 64
+    ada = S.adaptive_workspace_layout(B, H, N, topk_min=0.05, topk_max=0.25)
+    fix = S.workspace_layout(B, H, N, topk=0.25)
+    fixed_total = S.workspace_size(B, H, N, topk=0.25)
+    assert fix["keys"] == fixed_total
+    assert {k: v for k, v in ada.items() if k != "keys"} == {k: v for k, v in fix.items() if k != "keys"}
+    assert ada["keys"] == fixed_total
+    keys_bytes = B * H * Nb * Nb * 8
+    assert S.adaptive_workspace_size(B, H, N, topk_min=0.05, topk_max=0.25) == fixed_total + (keys_bytes + 255) // 256 * 256
     lay = S.adaptive_workspace_layout(1, 2, 1000, topk_min=0.1, topk_max=1.0)
-    assert lay["hs"] < S.adaptive_workspace_size(1, 2, 1000, topk_min=0.1, topk_max=1.0)
-    assert S.adaptive_workspace_size(1, 2, 1000, topk_min=1.0, topk_max=1.0) == \
-        S.workspace_size(1, 2, 1000, topk=1.0)
+    assert lay["hs"] < lay["keys"] < S.adaptive_workspace_size(1, 2, 1000, topk_min=0.1, topk_max=1.0)

@@ -67,6 +67,7 @@ def test_adaptive_parity(name):
     kmin, kmax = O.ksel(tmin, Nb), O.ksel(tmax, Nb)
     kr_g, kh_g = k_rows.cpu().numpy(), k_head.cpu().numpy()
     idx_g = views["idx"].cpu().numpy()
+    keys_g = views["keys"].cpu().numpy()
     out_g = out.float().cpu().numpy()
     bits = {n: synth.bf16_bits(x[n]) for n in ("q", "k", "v")}
     wbits = synth.bf16_bits(x["proj"]) if linear else None
@@ -82,6 +83,11 @@ def test_adaptive_parity(name):
         kr_o, margin, kh_o, sc = _oracle_counts(q, k, N, tau, kmin, kmax)
         sure = margin > 1e-12
         assert np.array_equal(kr_g[bh][sure], kr_o[sure]), (bh, np.nonzero(kr_g[bh] != kr_o)[0])
+        # the score keys the selection reused decode to the oracle's fp64 scores
+        u = keys_g[bh].view(np.uint64)
+        top = np.uint64(1 << 63)
+        s_g = np.where(u & top, u & ~top, ~u).view(np.float64)
+        assert np.allclose(s_g, sc, rtol=1e-12, atol=1e-12)
         if sure.all():
             assert kh_g[bh] == kh_o, (bh, kh_g[bh], kh_o)
         ks = int(kh_g[bh])
@@ -154,3 +160,40 @@ def test_full_size_adaptive_wan14b_720p():
         assert torch.equal(of[0, 0], out[0, h]), h
     del out, x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("tau", [0.05, 0.2, 0.5])
+def test_adaptive_equal_scores_at_the_boundary(tau):
+    # key blocks 0..7 are one block repeated, shifted along a direction shared with every
+    # query: they carry the top scores of every row, all exactly equal, so the count
+    # crosses tau inside a run of equal scores and those blocks are taken in index order
+    rng = np.random.default_rng(61)
+    N, d = 64 * 40, 128
+    u = rng.normal(0, 1, d)
+    u *= 3.0 / np.linalg.norm(u)
+    q = rng.normal(0, 1, (N, d)) + u
+    k = rng.normal(0, 1, (N, d))
+    blk = rng.normal(0, 1, (64, d)) + u
+    k[:512] = np.tile(blk, (8, 1))
+    v = rng.normal(0, 1, (N, d))
+    to = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).reshape(1, 1, N, d).cuda()  # noqa
+    tq, tk, tv = to(q), to(k), to(v)
+    print("\n[case] equal scores at the boundary: N=%d tau %g" % (N, tau), flush=True)
+    out, k_rows, k_head = S.fwd_adaptive(tq, tk, tv, None, topk_min=0.01, topk_max=1.0, tau=tau)
+    torch.cuda.synchronize()
+    qb, kb, vb = (synth.bf16_bits(t[0, 0]) for t in (tq, tk, tv))
+    Nb = O.num_blocks(N)
+    kr_o, margin, kh_o, sc = _oracle_counts(qb, kb, N, tau, O.ksel(0.01, Nb), O.ksel(1.0, Nb))
+    # the planted ties are exact on both sides
+    top = np.argsort(-sc, axis=1, kind="stable")[:, :8]
+    assert (np.sort(top, axis=1) == np.arange(8)).all()
+    assert (sc[:, :8] == sc[:, :1]).all()
+    kr_g = k_rows[0].cpu().numpy()
+    sure = margin > 1e-12
+    assert sure.mean() > 0.9
+    assert np.array_equal(kr_g[sure], kr_o[sure])
+    if sure.all():
+        assert int(k_head[0]) == kh_o
+    # the counts land inside the run of equal scores for the smaller tau
+    if tau <= 0.2:
+        assert ((kr_o > 1) & (kr_o <= 8)).any()
