@@ -44,7 +44,7 @@ def lib():
             "oracle_quant_blocks": (None, [P, i32, i32, i32, P, P]),
             "oracle_quant_v": (None, [P, i32, i32, P, P]),
             "oracle_dot_i8": (C.c_int32, [P, P, i32]),
-            "oracle_sparse_block": (None, [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P]),
+            "oracle_sparse_block": (None, [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P]),
             "oracle_sparse_block_fp64": (None, [P, P, P, P, i32, i32, i32, i32, i32, P]),
             "oracle_phi": (None, [P, i32, P]),
             "oracle_linear_states": (None, [P, P, i32, i32, i32, P, P]),
@@ -202,15 +202,18 @@ def quantize_head(q_bits, k_bits, v_bits, blk=64):
     return dict(q8=q8, sq=sq, k8=k8, sk=sk, v8=v8, sv=sv, kmean=mu)
 
 
-def sparse_block(qz, idx, N, blk, qb):
-    """O_s rows of query block qb from the quantized tensors in qz (quantize_head)."""
+def sparse_block(qz, idx, N, blk, qb, stats=False):
+    """O_s rows of query block qb from the quantized tensors in qz (quantize_head). With
+    stats, also each row's final FP8 row sum l and reference m: (out, l, m)."""
     d = qz["q8"].shape[1]
     k = idx.shape[1]
     out = np.zeros((blk, d), np.float64)
     idx = _c(idx, np.int32)
+    l = np.zeros(blk, np.float64) if stats else None
+    m = np.zeros(blk, np.float32) if stats else None
     lib().oracle_sparse_block(_p(qz["q8"]), _p(qz["k8"]), _p(qz["v8"]), _p(qz["sq"]), _p(qz["sk"]),
-                              _p(qz["sv"]), _p(idx), k, N, d, blk, qb, _p(out))
-    return out
+                              _p(qz["sv"]), _p(idx), k, N, d, blk, qb, _p(out), _p(l), _p(m))
+    return (out, l, m) if stats else out
 
 
 def phi(x_bits):

@@ -414,23 +414,26 @@ int32_t oracle_dot_i8(const int8_t *a, const int8_t *b, int d)
  * Quantized sparse attention for the rows of query block qb (reading of SageAttention
  * on the kept blocks): for each kept key block j in the row's processing order,
  *   S = q8 . k8 (int32), a = (s_q[i]*s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
- *   x = fp32(S)*a, m' = max(m, max x), alpha = exp2f(m - m'),
+ *   x = fp32(S)*a, the reference m' = max(m, ceil(max x)): the running row maximum
+ *     rounded up to an integer (in log2 units), so that every change of reference is an
+ *     exact power of two, alpha = exp2f(m - m') (0 for the first block),
  *   w = exp2f(fmaf(F, a, c)) with F = 1.5*2^23 + S (an integer below 2^24, exact in
  *     fp32), c = (L - m') - fp32(1.5*2^23 * a) and L = fp32(log2(448)); in exact
  *     arithmetic F*a + c = S*a + L - m', so w = 448 p for p = 2^(x - m') up to the fp32
  *     roundings of c and of the fused product (the exponent argument is formed in fp32
  *     exactly as the FP8 code decision is taken on the GPU, whose integer accumulators
- *     start from the bit pattern of 1.5*2^23),
+ *     start from the bit pattern of 1.5*2^23); the row maximum gets a weight in (224, 448],
  *   p8 = e4m3(w) (saturating),
  *   l = l*alpha + sum dec(p8), acc = acc*alpha + sum dec(p8)*dec(v8) (fp64), m = m'.
  * Output row: acc[c] * sv[c] / l, i.e. the average of the dequantized V rows weighted by
  * the FP8 probabilities actually used. Keys past N are skipped.
- * out: [blk][d] (rows past N left untouched).
+ * out: [blk][d] (rows past N left untouched). l_out, ref_out (may be NULL): [blk], each
+ * row's final l and reference m.
  */
 void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
                          const float *sq, const float *sk, const float *sv,
                          const int32_t *idx, int ksel, int N, int d, int blk, int qb,
-                         double *out)
+                         double *out, double *l_out, float *ref_out)
 {
     const float c0 = (float)(1.4426950408889634 / sqrt((double)d));
     const float L = (float)log2(448.0);
@@ -455,7 +458,8 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
                 if (x > mb)
                     mb = x;
             }
-            float mn = m > mb ? m : mb;
+            float mbr = ceilf(mb);
+            float mn = m > mbr ? m : mbr;
             float alpha = exp2f(m - mn);
             float c = (L - mn) - 12582912.0f * a;
             l *= (double)alpha;
@@ -472,6 +476,10 @@ void oracle_sparse_block(const int8_t *q8, const int8_t *k8, const uint8_t *v8,
         }
         for (int c = 0; c < d; c++)
             out[(size_t)r * d + c] = acc[c] * (double)sv[c] / l;
+        if (l_out)
+            l_out[r] = l;
+        if (ref_out)
+            ref_out[r] = m;
     }
     free(sf);
     free(acc);
@@ -730,7 +738,7 @@ static void head_core(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
             continue;
         int nq = block_len(qb, N, blk);
         if (quant)
-            oracle_sparse_block(q8, k8, v8, sq, sk, sv, idx, ksel, N, d, blk, qb, os);
+            oracle_sparse_block(q8, k8, v8, sq, sk, sv, idx, ksel, N, d, blk, qb, os, NULL, NULL);
         else
             oracle_sparse_block_fp64(q, k, v, idx, ksel, N, d, blk, qb, os);
         if (linear) {

@@ -187,3 +187,32 @@ def test_subset_of_query_blocks_matches_full_run():
     part = O.sagesla_head(q, k, v, w, 0.3, quant=True, qblocks=[6, 2])
     assert np.array_equal(part["out"][:64], full["out"][6 * 64:7 * 64])
     assert np.array_equal(part["out"][64:128], full["out"][2 * 64:3 * 64])
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.25, 3.0])
+def test_fp8_reference_is_the_running_max_rounded_up(scale):
+    # The FP8 weights of a row are taken against the running row maximum rounded up to an
+    # integer (log2 units). Checked against the logits formed here from the INT8 codes and
+    # scales: the final reference is an integer m with m - 1 < max x <= m, and the row sum
+    # of the weights holds the maximum's own weight, e4m3(448 * 2^(max x - m)) >= 224.
+    N = 64 * 6 + 21
+    q, k, v, _ = _rand_head(N, seed=21)
+    q = _bits(O.bf16_to_f64(q).astype(np.float32) * scale)
+    qz = O.quantize_head(q, k, v)
+    r = O.sagesla_head(q, k, v, None, 0.5, quant=True)
+    idx = r["idx"]
+    c0 = np.float32(1.4426950408889634 / np.sqrt(128.0))
+    Nb = O.num_blocks(N)
+    for qb in range(Nb):
+        _, l, m = O.sparse_block(qz, idx, N, 64, qb, stats=True)
+        nq = min(64, N - 64 * qb)
+        xmax = np.full(nq, -np.inf, np.float32)
+        for j in idx[qb]:
+            nk = min(64, N - 64 * j)
+            S = qz["q8"][64 * qb:64 * qb + nq].astype(np.int64) @ qz["k8"][64 * j:64 * j + nk].astype(np.int64).T
+            a = np.float32(np.float32(qz["sq"][qb] * qz["sk"][j]) * c0)
+            xmax = np.maximum(xmax, (S.astype(np.float32) * a).max(1))
+        m = m[:nq]
+        assert np.array_equal(m, np.floor(m))
+        assert np.all(m - 1 < xmax) and np.all(xmax <= m)
+        assert np.all(l[:nq] >= 224.0)
