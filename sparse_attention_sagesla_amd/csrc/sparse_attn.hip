@@ -9,7 +9,9 @@
 //
 // Per query block i (64 rows) and kept key block j, for each row:
 //   S = q8 . k8 (int32), a = (s_q[i] * s_k[j]) * c0 with c0 = fp32(log2(e)/sqrt(d)),
-//   m' = max(m, max float(S)*a), alpha = 2^(m - m'),
+//   the reference m' = max(m, ceil(max float(S)*a)) (an integer, in log2 units: it moves
+//   less often than the maximum itself, and each move is an exact power of two),
+//   alpha = 2^(m - m'),
 //   P8 = e4m3(2^x) with x = fma(F, a, c), F = 1.5*2^23 + S (exact in fp32) and
 //        c = (log2(448) - m') - fp32(1.5*2^23 * a): 448 * 2^(S a - m') up to the fp32
 //        roundings of c and of the fused product,
@@ -46,8 +48,12 @@ constexpr float kLog2_448 = 8.807354922057604f;  // fp32(log2(448))
 constexpr float kMagicF = 12582912.0f;           // 1.5 * 2^23
 constexpr int kMagicI = 0x4B400000;              // its bit pattern
 
-// c0 = fp32(log2(e) / sqrt(d)), rounded once from double
-static float log2e_over_sqrt_d() { return (float)(1.4426950408889634 / sqrt((double)kD)); }
+// c0 = fp32(log2(e) / sqrt(d)), rounded once from double; a compile-time constant, so that
+// the loop holds no kernel argument it would have to reload (sqrt(128) as a double literal,
+// checked against the library's sqrt at launch)
+constexpr double kSqrtD = 11.313708498984760390;
+constexpr float kC0 = (float)(1.4426950408889634 / kSqrtD);
+static bool c0_matches() { return kC0 == (float)(1.4426950408889634 / sqrt((double)kD)) && kSqrtD == sqrt((double)kD); }
 
 __device__ __forceinline__ int key_of_slot(int g, int t, int v) { return 32 * t + 8 * (v >> 2) + 4 * g + (v & 3); }
 
@@ -66,7 +72,7 @@ __device__ __forceinline__ void dma_part(__amdgpu_buffer_rsrc_t r, uint8_t* dst,
 
 // Online-softmax state of the wave's 32 queries.
 struct RowAcc {
-  float m;      // running max of S * a
+  float m;      // reference: running max of S * a, rounded up to an integer
   v16f acc[4];  // O^T accumulators (4 tiles of 32 channels)
   v4f lacc;     // running row sums: lanes 0..15, element 0 (query l), 1 (query l + 16)
 };
@@ -161,9 +167,10 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
     auto sw = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
     mx = max((int)sw[0], (int)sw[1]);
   }
-  // float(S_max) = F_max - 1.5*2^23 exactly
+  // float(S_max) = F_max - 1.5*2^23 exactly; the reference is its product with a rounded
+  // up to an integer, never below the previous one
   const float mold = st.m;
-  const float mn = fmaxf(mold, (__int_as_float(mx) - kMagicF) * a);
+  const float mn = fmaxf(mold, __builtin_ceilf((__int_as_float(mx) - kMagicF) * a));
   const bool moved = __builtin_amdgcn_ballot_w64(mn > mold) != 0;
   st.m = mn;
   // exponentials and FP8 packing, 4 scores per group. For the row maximum the fused
@@ -203,7 +210,7 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
         pb[4 * tt + v4] &= (int)keep;
       }
   }
-  // rescale only when some row's running max moved (alpha == 1 otherwise)
+  // rescale only when some row's reference moved (alpha == 1 otherwise; a power of two)
   if (moved) {
     const float alpha = __builtin_amdgcn_exp2f(mold - mn);
 #pragma unroll
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     const int8_t* __restrict__ q8, const float* __restrict__ sq, const int8_t* __restrict__ k8,
     const float* __restrict__ sk, const uint8_t* __restrict__ v8, const float* __restrict__ vamax,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ khead, const uint16_t* __restrict__ y, int N,
-    int Nb, int ksel, int kstride, int tiles, int per_xcd, float c0, uint16_t* __restrict__ out) {
+    int Nb, int ksel, int kstride, int tiles, int per_xcd, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_k0[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_k1[kBlkBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_v0[kBlkBytes];
@@ -277,8 +284,8 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     dma(s_k0, ju);
     dma(s_k1, ju1);
   }
-  const v16i magic = {kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI,
-                      kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI};
+  v16i magic = {kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI,
+                kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI, kMagicI};
   // row-sum selector: e4m3 1.0 in row 0 over the key ranges of lanes 0..15 and 32..47
   // (queries 0..15), in row 1 over those of lanes 16..31 and 48..63
   const int lr = l & 15, lq = (l >> 4) & 1;
@@ -322,6 +329,8 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
     // the other's), and no wave reads K(u) or V(u - 2) any more
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    // the accumulator bias stays in VGPRs (rebuilding it from scalars costs 8 moves a block)
+    asm volatile("" : "+v"(magic));
     if (u > 0) {
       ju = ju1;
       ju1 = ju2;
@@ -334,7 +343,7 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
       dma(ks, ju2);
     else
       dma(vc, ju);
-    const float a = (sqi * sku) * c0;
+    const float a = (sqi * sku) * kC0;
     const float ba = kMagicF * a;
     const bool partial = has_partial && ju == Nb - 1;
     pp.vt = vp;
@@ -402,12 +411,13 @@ __global__ __launch_bounds__(128, 2) void sparse_attn_kernel(
 hipError_t launch_sparse_attn(const void* q8, const void* sq, const void* k8, const void* sk,
                               const void* v8, const void* vamax, const void* idx, const void* khead, int kstride,
                               const void* y, int BH, int N, int Nb, int ksel, void* out, hipStream_t st) {
+  if (!c0_matches()) return hipErrorInvalidValue;
   const int tiles = BH * Nb;
   const int per_xcd = (tiles + 7) / 8;
   hipLaunchKernelGGL(sparse_attn_kernel, dim3(per_xcd * 8), dim3(128), 0, st, (const int8_t*)q8,
                      (const float*)sq, (const int8_t*)k8, (const float*)sk, (const uint8_t*)v8,
                      (const float*)vamax, (const int32_t*)idx, (const int32_t*)khead, (const uint16_t*)y, N, Nb,
-                     ksel, kstride, tiles, per_xcd, log2e_over_sqrt_d(), (uint16_t*)out);
+                     ksel, kstride, tiles, per_xcd, (uint16_t*)out);
   return hipGetLastError();
 }
 
