@@ -13,6 +13,7 @@
 // S_j[c][a] = H_j[a][c] for c < 128 and S_j[128][a] = z_j[a] (129 x 128), which is the
 // operand order of the complement kernels; fp32 sums of 16 consecutive blocks feed the
 // exact totals.
+#include "buffer.h"
 #include "common.h"
 
 namespace sagesla {
@@ -46,6 +47,9 @@ constexpr int kQkThreads = 512;
 // One workgroup (512 threads, 8 waves) per (bh, chunk of 16 key blocks). Thread t
 // covers rows t/16 + 32m (m = 0, 1) and channels 8*(t%16) .. +7 of each block. In the
 // state product wave w owns rows c in [32(w%4), +32) and column tiles 2(w/4), 2(w/4)+1.
+// All of one head's traffic goes through buffer resources with 32-bit offsets: the
+// 128-register budget (two workgroups per CU) then holds without spills, whose reloads
+// would wait on the prefetched rows.
 __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ kmean,
     const float* __restrict__ vamax, int N, int Nb, int Nc, int8_t* __restrict__ k8,
@@ -56,7 +60,10 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
   __shared__ float s_z[8][kD];
   __shared__ float s_amax[8];
 
-  const int bh = blockIdx.x / Nc, chunk = blockIdx.x % Nc;
+  // the head and chunk are kept in scalar registers, so that every address derived
+  // from them is scalar too
+  const int bh = __builtin_amdgcn_readfirstlane(blockIdx.x / Nc);
+  const int chunk = __builtin_amdgcn_readfirstlane(blockIdx.x - bh * Nc);
   const int t = threadIdx.x, rg = t >> 4, ch = t & 15;
   const int lane = t & 63, g = lane >> 5, r = lane & 31, hl = (lane >> 4) & 1;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -77,22 +84,24 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
   part[1] = (v16f){};
 
   const int j0 = chunk * kChunk, j1 = min(Nb, j0 + kChunk);
-  // raw K and V rows of block jj (zeros past N); each block's are fetched while the
-  // previous block is processed
+  const size_t tok0 = scalar_off((size_t)bh * N * kD), blk0 = scalar_off((size_t)bh * Nb);
+  const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + tok0, (uint32_t)N * kD * 2);
+  const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + tok0, (uint32_t)N * kD * 2);
+  const __amdgpu_buffer_rsrc_t rk8 = buf_rsrc(k8 + blk0 * kBlkBytes, (uint32_t)Nb * kBlkBytes);
+  const __amdgpu_buffer_rsrc_t rv8 = buf_rsrc(v8 + blk0 * kBlkBytes, (uint32_t)Nb * kBlkBytes);
+  const __amdgpu_buffer_rsrc_t rhs = buf_rsrc(states ? hs + blk0 * kStateElems : hs, (uint32_t)Nb * kStateElems * 2);
+  // Raw K and V rows of block jj; rows past N lie past the resource's end and read zero.
+  // Each block's rows are fetched while the previous block is processed; every fetch is
+  // unconditional (the chunk's last block is fetched again after itself), so that the
+  // wait before a block's first use counts exactly the loads issued after it.
   uint4 kn[2], vn[2];
   auto fetch = [&](int jj) {
-    const int nn = block_len(jj, N);
-    const size_t bb = ((size_t)bh * N + (size_t)jj * kBlk) * kD;
+    const int sb = jj * kBlk * kD * 2;
 #pragma unroll
     for (int m = 0; m < 2; m++) {
-      const int row = rg + 32 * m;
-      kn[m] = make_uint4(0, 0, 0, 0);
-      vn[m] = make_uint4(0, 0, 0, 0);
-      if (row < nn) {
-        const size_t off = bb + (size_t)row * kD + ch * 8;
-        kn[m] = *(const uint4*)(k + off);
-        vn[m] = *(const uint4*)(v + off);
-      }
+      const int off = (rg + 32 * m) * kD * 2 + ch * 16;
+      kn[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, sb, 0));
+      vn[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, sb, 0));
     }
   };
   fetch(j0);
@@ -101,7 +110,7 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
     uint4 kraw[2], vraw[2];
 #pragma unroll
     for (int m = 0; m < 2; m++) { kraw[m] = kn[m]; vraw[m] = vn[m]; }
-    if (j + 1 < j1) fetch(j + 1);
+    fetch(min(j + 1, j1 - 1));
     float amax = 0.f;
 #pragma unroll
     for (int m = 0; m < 2; m++) {
@@ -169,8 +178,7 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
 #pragma unroll
     for (int q = 1; q < 8; q++) amax = fmaxf(amax, s_amax[q]);
     const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-    if (t == 0) sk[(size_t)bh * Nb + j] = amax > 0.f ? amax / 127.0f : 0.f;
-    int8_t* kdst = k8 + ((size_t)bh * Nb + j) * kBlkBytes;
+    if (t == 0) sk[blk0 + j] = amax > 0.f ? amax / 127.0f : 0.f;
 #pragma unroll
     for (int m = 0; m < 2; m++) {
       const int row = rg + 32 * m;
@@ -182,13 +190,12 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
 #pragma unroll
         for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q_int8(bf16_to_f32(kh[e + 4]) - mu[e + 4], inv) << (8 * e);
       }
-      *(uint2*)(kdst + qk_code_offset(row, ch * 8)) = make_uint2(lo, hi);
+      __builtin_amdgcn_raw_buffer_store_b64((v2u){lo, hi}, rk8, qk_code_offset(row, ch * 8), j * kBlkBytes, 0);
     }
     // V: FP8 codes straight in operand order. Chunk (dt, half, lane) holds channel
     // 32*dt + r at tokens 32*half + 4*g + {0..3, 8..11, 16..19, 24..27}: four
     // transposing reads of 4 consecutive tokens each.
     {
-      uint8_t* vdst = v8 + ((size_t)bh * Nb + j) * kBlkBytes;
       const int c0 = 32 * vdt + 16 * hl, jj = lane & 15, a = jj >> 2, b = jj & 3;
       uint32_t wd[4];
 #pragma unroll
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
         pk = __builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, pk, true);
         wd[qd] = (uint32_t)pk;
       }
-      *(uint4*)(vdst + (w * 64 + lane) * 16) = make_uint4(wd[0], wd[1], wd[2], wd[3]);
+      __builtin_amdgcn_raw_buffer_store_b128((v4u){wd[0], wd[1], wd[2], wd[3]}, rv8, t * 16, j * kBlkBytes, 0);
     }
     if (states) {
       float zsum_t = 0.f;
@@ -240,10 +247,10 @@ __global__ __launch_bounds__(kQkThreads, 4) void quant_kv_kernel(
         }
       if (t < kD) s_st[kD * kSp + t] = f32_to_bf16(zsum_t);
       __syncthreads();
-      uint16_t* hdst = hs + ((size_t)bh * Nb + j) * kStateElems;
       for (int e = t; e < (kD + 1) * 16; e += kQkThreads) {
         const int row = e >> 4, c8 = (e & 15) * 8;
-        *(uint4*)(hdst + row * kD + c8) = *(const uint4*)(s_st + row * kSp + c8);
+        __builtin_amdgcn_raw_buffer_store_b128(*(const v4u*)(s_st + row * kSp + c8), rhs, (row * kD + c8) * 2,
+                                               j * kStateElems * 2, 0);
       }
     }
     __syncthreads();
@@ -276,6 +283,8 @@ __global__ __launch_bounds__(256) void linear_total_kernel(const float* __restri
 
 hipError_t launch_quant_kv(const void* k, const void* v, const void* kmean, const void* vamax, int BH,
                            int N, int Nb, void* k8, void* sk, void* v8, void* hs, void* hpart, hipStream_t st) {
+  // one head's rows, codes and states are each addressed by 32-bit buffer offsets
+  if ((uint64_t)N * kD * 2 > UINT32_MAX || (uint64_t)Nb * kStateElems * 2 > UINT32_MAX) return hipErrorInvalidValue;
   const int Nc = (Nb + kChunk - 1) / kChunk;
   hipLaunchKernelGGL(quant_kv_kernel, dim3(BH * Nc), dim3(kQkThreads), 0, st, (const uint16_t*)k,
                      (const uint16_t*)v, (const float*)kmean, (const float*)vamax, N, Nb, Nc,
