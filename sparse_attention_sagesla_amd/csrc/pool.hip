@@ -5,6 +5,7 @@
 // attention"); here that estimate is made on 64-token block means. SageAttention's
 // 8-bit quantization with one scale per small block (same page, "First key" and
 // "Third key") is applied to Q in the same pass, since Q needs no smoothing.
+#include "buffer.h"
 #include "common.h"
 
 namespace sagesla {
@@ -37,85 +38,153 @@ __device__ __forceinline__ uint4 rms_apply(uint4 x, float r, uint4 g) {
   return o;
 }
 
+// x summed with the value of lane l ^ 16 and then of l ^ 32 (the wave's four row groups of
+// one channel), through the VALU lane swaps: every lane ends with the same total.
+__device__ __forceinline__ double wave_rows_sum(double x) {
+  int lo = __double2loint(x), hi = __double2hiint(x);
+  {
+    const auto sl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto sh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    x = __hiloint2double((int)sh[0], (int)sl[0]) + __hiloint2double((int)sh[1], (int)sl[1]);
+  }
+  lo = __double2loint(x);
+  hi = __double2hiint(x);
+  const auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return __hiloint2double((int)sh[0], (int)sl[0]) + __hiloint2double((int)sh[1], (int)sl[1]);
+}
+__device__ __forceinline__ float wave_rows_max(float x) {
+  {
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_int(x), __float_as_int(x), false, false);
+    x = fmaxf(__int_as_float((int)s[0]), __int_as_float((int)s[1]));
+  }
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+  return fmaxf(__int_as_float((int)s[0]), __int_as_float((int)s[1]));
+}
+
 // One workgroup (256 threads) per (bh, block). Thread t covers rows t/16 + 16m
-// (m = 0..3) and channels 8*(t%16) .. +7.
+// (m = 0..3) and channels 8*(t%16) .. +7. The channel sums (fp64: exact for bf16 inputs
+// of moderate range, so their order is immaterial) and maxima are reduced within each
+// wave by lane swaps and across the 4 waves through LDS.
 template <bool kFromProj>
 __global__ __launch_bounds__(256) void pool_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     ProjSrc ps, int N, int Nb, double* __restrict__ qbar, double* __restrict__ kbart, double* __restrict__ ksum,
     float* __restrict__ vamax_blk, int8_t* __restrict__ q8, float* __restrict__ sq) {
-  __shared__ double s_q[16][kD];
-  __shared__ double s_k[16][kD];
-  __shared__ float s_v[16][kD];
+  __shared__ double s_q[4][kD];
+  __shared__ double s_k[4][kD];
+  __shared__ float s_v[4][kD];
   __shared__ float s_amax[4];
 
   const int tile = blockIdx.x;
-  const int bh = tile / Nb, i = tile % Nb;
+  const int bh = __builtin_amdgcn_readfirstlane(tile / Nb), i = __builtin_amdgcn_readfirstlane(tile - bh * Nb);
   const int n = block_len(i, N);
-  const int t = threadIdx.x, rg = t >> 4, ch = t & 15;
+  const int t = threadIdx.x, rg = t >> 4, ch = t & 15, w = t >> 6;
   const size_t base = ((size_t)bh * N + (size_t)i * kBlk) * kD;
 
-  double sumq[8], sumk[8];
-  float mv[8];
-  float qv[4][8];
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; e++) { sumq[e] = 0.0; sumk[e] = 0.0; mv[e] = 0.f; }
+  uint4 qa[4], ka[4], va[4];
 #pragma unroll
   for (int m = 0; m < 4; m++) {
-    int row = rg + 16 * m;
-    uint4 qa = {0, 0, 0, 0}, ka = {0, 0, 0, 0}, va = {0, 0, 0, 0};
-    if (row < n) {
-      size_t off = base + (size_t)row * kD + ch * 8;
+    const int row = rg + 16 * m;
+    qa[m] = ka[m] = va[m] = make_uint4(0, 0, 0, 0);
+    if (kFromProj && row < n) {
+      const size_t off = base + (size_t)row * kD + ch * 8;
       if (kFromProj) {
         const int b = bh / ps.H, h = bh % ps.H, tok = i * kBlk + row, D = ps.H * kD;
         const uint16_t* src = ps.qkv + ((size_t)b * N + tok) * 3 * D + h * kD + ch * 8;
         const size_t rr = (size_t)b * N + tok, BN = (size_t)(gridDim.x / Nb / ps.H) * N;
-        qa = rms_apply(*(const uint4*)src, ps.rs[rr], *(const uint4*)(ps.gq + h * kD + ch * 8));
-        ka = rms_apply(*(const uint4*)(src + D), ps.rs[BN + rr], *(const uint4*)(ps.gk + h * kD + ch * 8));
-        va = *(const uint4*)(src + 2 * D);
-        *(uint4*)(ps.q + off) = qa;
-        *(uint4*)(ps.k + off) = ka;
-        *(uint4*)(ps.v + off) = va;
-      } else {
-        qa = *(const uint4*)(q + off);
-        ka = *(const uint4*)(k + off);
-        va = *(const uint4*)(v + off);
+        qa[m] = rms_apply(*(const uint4*)src, ps.rs[rr], *(const uint4*)(ps.gq + h * kD + ch * 8));
+        ka[m] = rms_apply(*(const uint4*)(src + D), ps.rs[BN + rr], *(const uint4*)(ps.gk + h * kD + ch * 8));
+        va[m] = *(const uint4*)(src + 2 * D);
+        *(uint4*)(ps.q + off) = qa[m];
+        *(uint4*)(ps.k + off) = ka[m];
+        *(uint4*)(ps.v + off) = va[m];
       }
     }
-    const uint16_t* qh = (const uint16_t*)&qa;
-    const uint16_t* kh = (const uint16_t*)&ka;
-    const uint16_t* vh = (const uint16_t*)&va;
+  }
+  if (!kFromProj) {
+    // one head's rows through buffer resources: 32-bit lane offsets, and rows past N
+    // (past the resource's end) read zero
+    const size_t h0 = scalar_off((size_t)bh * N * kD);
+    const __amdgpu_buffer_rsrc_t rq = buf_rsrc(q + h0, (uint32_t)N * kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(k + h0, (uint32_t)N * kD * 2);
+    const __amdgpu_buffer_rsrc_t rv = buf_rsrc(v + h0, (uint32_t)N * kD * 2);
+    const int sb = i * kBlk * kD * 2;
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      float xq = bf16_to_f32(qh[e]);
-      qv[m][e] = xq;
-      sumq[e] += (double)xq;
-      sumk[e] += (double)bf16_to_f32(kh[e]);
-      mv[e] = fmaxf(mv[e], fabsf(bf16_to_f32(vh[e])));
-      amax = fmaxf(amax, fabsf(xq));
+    for (int m = 0; m < 4; m++) {
+      const int off = (rg + 16 * m) * kD * 2 + ch * 16;
+      qa[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, sb, 0));
+      ka[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, sb, 0));
+      va[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, sb, 0));
     }
   }
+  // K, then Q, then V: one set of per-channel partials live at a time
+  float amax = 0.f;
+  {
+    double sk_[8];
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    s_q[rg][ch * 8 + e] = sumq[e];
-    s_k[rg][ch * 8 + e] = sumk[e];
-    s_v[rg][ch * 8 + e] = mv[e];
+    for (int e = 0; e < 8; e++) sk_[e] = 0.0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const uint16_t* kh = (const uint16_t*)&ka[m];
+#pragma unroll
+      for (int e = 0; e < 8; e++) sk_[e] += (double)bf16_to_f32(kh[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) sk_[e] = wave_rows_sum(sk_[e]);
+    if (rg % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) s_k[w][ch * 8 + e] = sk_[e];
+    }
+  }
+  {
+    double sq_[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) sq_[e] = 0.0;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const uint16_t* qh = (const uint16_t*)&qa[m];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float xq = bf16_to_f32(qh[e]);
+        sq_[e] += (double)xq;
+        amax = fmaxf(amax, fabsf(xq));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) sq_[e] = wave_rows_sum(sq_[e]);
+    if (rg % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) s_q[w][ch * 8 + e] = sq_[e];
+    }
+  }
+  {
+    float mv[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) mv[e] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; m++) {
+      const uint16_t* vh = (const uint16_t*)&va[m];
+#pragma unroll
+      for (int e = 0; e < 8; e++) mv[e] = fmaxf(mv[e], fabsf(bf16_to_f32(vh[e])));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; e++) mv[e] = wave_rows_max(mv[e]);
+    if (rg % 4 == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) s_v[w][ch * 8 + e] = mv[e];
+    }
   }
   // block-wide max |q|
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
-  if ((t & 63) == 0) s_amax[t >> 6] = amax;
+  if ((t & 63) == 0) s_amax[w] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
 
   if (t < kD) {
-    double a = 0.0, b = 0.0;
-    float mx = 0.f;
-    for (int r = 0; r < 16; r++) {  // fixed order: exact for bf16 inputs of moderate range
-      a += s_q[r][t];
-      b += s_k[r][t];
-      mx = fmaxf(mx, s_v[r][t]);
-    }
+    const double a = (s_q[0][t] + s_q[1][t]) + (s_q[2][t] + s_q[3][t]);
+    const double b = (s_k[0][t] + s_k[1][t]) + (s_k[2][t] + s_k[3][t]);
+    const float mx = fmaxf(fmaxf(s_v[0][t], s_v[1][t]), fmaxf(s_v[2][t], s_v[3][t]));
     size_t o = ((size_t)bh * Nb + i) * kD + t;
     qbar[o] = a / n;
     ksum[o] = b;
@@ -129,13 +198,14 @@ __global__ __launch_bounds__(256) void pool_kernel(
   int8_t* dst = q8 + ((size_t)bh * Nb + i) * kBlkBytes;
 #pragma unroll
   for (int m = 0; m < 4; m++) {
-    int row = rg + 16 * m;
+    const int row = rg + 16 * m;
+    const uint16_t* qh = (const uint16_t*)&qa[m];
     uint32_t lo = 0, hi = 0;
     if (row < n) {
 #pragma unroll
-      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q_int8(qv[m][e], inv) << (8 * e);
+      for (int e = 0; e < 4; e++) lo |= (uint32_t)(uint8_t)q_int8(bf16_to_f32(qh[e]), inv) << (8 * e);
 #pragma unroll
-      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q_int8(qv[m][e + 4], inv) << (8 * e);
+      for (int e = 0; e < 4; e++) hi |= (uint32_t)(uint8_t)q_int8(bf16_to_f32(qh[e + 4]), inv) << (8 * e);
     }
     *(uint2*)(dst + qk_code_offset(row, ch * 8)) = make_uint2(lo, hi);
   }
