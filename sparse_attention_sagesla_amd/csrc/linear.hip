@@ -371,7 +371,7 @@ __device__ __forceinline__ v8bf tile_col8(const uint16_t* tile, int a0, int c0, 
   return __builtin_bit_cast(v8bf, v);
 }
 
-// Per-block inputs held in registers (the next block's are fetched during this one).
+// Per-block inputs held in registers.
 struct OutLoads {
   uint4 q[4];    // raw q: rows t/16 + 16 mm, channels 8 (t%16) .. +7
   v8bf sa[8];    // S^c rows 32 w + l%32, k-steps s: the A operands of num^T
@@ -381,8 +381,7 @@ struct OutLoads {
 __device__ __forceinline__ void out_load(OutLoads& L, const uint16_t* q, const uint16_t* hc, int bh, int i, int N,
                                          int Nb, int t, int w, int lane) {
   // Every load is unconditional (rows past the block's end repeat its last row; their
-  // results are never stored), so that the compiler's wait counts stay exact and the
-  // loads of the next block overlap this one's work.
+  // results are never stored).
   const int n = block_len(i, N), rg = t >> 4, ch = t & 15;
 #pragma unroll
   for (int mm = 0; mm < 4; mm++) {
@@ -404,7 +403,7 @@ __device__ __forceinline__ void out_load(OutLoads& L, const uint16_t* q, const u
 // row-major W, and each lane ends with 4 consecutive channels of one row.
 // Wave w owns channels 32 w .. 32 w + 31 of both products, for all 64 rows.
 // A head that keeps every block (khead[bh] = Nb) has no complement: its y is zero.
-__global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 3) void linear_out_kernel(const uint16_t* __restrict__ q,
                                                          const uint16_t* __restrict__ hc,
                                                          const uint16_t* __restrict__ proj,
                                                          const int32_t* __restrict__ khead, int N, int Nb,
@@ -427,7 +426,7 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
     return;
   }
 
-  OutLoads la, lb;
+  OutLoads la;
   out_load(la, q, hc, bh, i0, N, Nb, t, w, lane);
   {
     // W_proj: all of this thread's loads in flight before its stores
@@ -536,15 +535,12 @@ __global__ __launch_bounds__(256) void linear_out_kernel(const uint16_t* __restr
       }
     }
   };
-  // two load sets in turn: the next block's loads fly while this one is processed, and no
-  // register whose load is in flight is copied
-  for (int i = i0; i < i1; i += 2) {
-    if (i + 1 < i1) out_load(lb, q, hc, bh, i + 1, N, Nb, t, w, lane);
+  // One load set: at 150 registers three workgroups share a CU (the LDS allows three as
+  // well), and the other workgroups' work covers a block's load latency; that runs faster
+  // than two workgroups with the next block's loads in flight in a second set.
+  for (int i = i0; i < i1; i++) {
+    if (i > i0) out_load(la, q, hc, bh, i, N, Nb, t, w, lane);
     process(la, i);
-    if (i + 1 < i1) {
-      if (i + 2 < i1) out_load(la, q, hc, bh, i + 2, N, Nb, t, w, lane);
-      process(lb, i + 1);
-    }
   }
 }
 
