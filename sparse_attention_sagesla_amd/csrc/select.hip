@@ -86,6 +86,107 @@ __device__ Threshold radix_threshold(const uint64_t* keys, int Nb, int k, uint32
   return th;
 }
 
+// The same selection with a row's keys in registers: lane l holds keys l + 64 m (m < M;
+// entries at or past Nb are excluded), so no pass waits on an LDS read of the keys.
+template <int M>
+__device__ Threshold radix_threshold_regs(const uint64_t (&key)[M], int Nb, int k, uint32_t* hist, int lane) {
+  Threshold th = {0u, 0u, k};
+  for (int pass = 0; pass < 8; pass++) {
+    const int shift = 56 - 8 * pass;
+#pragma unroll
+    for (int b = 0; b < 4; b++) hist[4 * lane + b] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int m = 0; m < M; m++) {
+      if (64 * m >= Nb) break;  // uniform: the row's last key slot
+      if (lane + 64 * m < Nb && (key[m] & th.mask) == th.prefix)
+        atomicAdd(&hist[(uint32_t)(key[m] >> shift) & 255u], 1u);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+    const int loc = h0 + h1 + h2 + h3;
+    int suf = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_down(suf, o);
+      if (lane + o < 64) suf += y;
+    }
+    int above = suf - loc;
+    const int hs[4] = {h0, h1, h2, h3};
+    int sel_bin = -1, sel_k = 0, sel_n = 0;
+#pragma unroll
+    for (int b = 3; b >= 0; b--) {
+      if (above < th.kk && above + hs[b] >= th.kk) {
+        sel_bin = 4 * lane + b;
+        sel_k = th.kk - above;
+        sel_n = hs[b];
+      }
+      above += hs[b];
+    }
+    const unsigned long long who = __ballot(sel_bin >= 0);
+    const int src = __ffsll((long long)who) - 1;
+    sel_bin = __shfl(sel_bin, src);
+    sel_k = __shfl(sel_k, src);
+    sel_n = __shfl(sel_n, src);
+    th.prefix |= (uint64_t)sel_bin << shift;
+    th.mask |= (uint64_t)255u << shift;
+    th.kk = sel_k;
+    __builtin_amdgcn_wave_barrier();
+    if (sel_n == sel_k) break;
+  }
+  return th;
+}
+
+// One row's selection by one wave, its keys in registers (Nb <= 64 M): the kept indices
+// best first, then ascending; positions from ks to kstride are set to -1.
+template <int M>
+__device__ void select_row_regs(const uint64_t* keys, int Nb, int ks, int kstride, uint32_t* hist, int lane,
+                                int32_t* out) {
+  const unsigned long long below = (1ull << lane) - 1ull;
+  uint64_t key[M];
+#pragma unroll
+  for (int m = 0; m < M; m++) key[m] = lane + 64 * m < Nb ? keys[lane + 64 * m] : 0u;
+  const Threshold th = radix_threshold_regs<M>(key, Nb, ks, hist, lane);
+  const uint64_t prefix = th.prefix, mask = th.mask;
+  const int kk = th.kk;
+  // best block: highest key, lowest index (each lane's candidate, then the wave's)
+  uint64_t kbest = 0u;
+  int jb = INT_MAX;
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    if (64 * m >= Nb) break;
+    if (lane + 64 * m < Nb && key[m] > kbest) {
+      kbest = key[m];
+      jb = lane + 64 * m;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t ko = (uint64_t)__shfl_xor((long long)kbest, o);
+    const int jo = __shfl_xor(jb, o);
+    if (ko > kbest || (ko == kbest && jo < jb)) {
+      kbest = ko;
+      jb = jo;
+    }
+  }
+  if (lane == 0) out[0] = jb;
+  for (int p = ks + lane; p < kstride; p += 64) out[p] = -1;
+  int pos = 1, eq_seen = 0;
+#pragma unroll
+  for (int m = 0; m < M; m++) {
+    if (64 * m >= Nb) break;
+    const int j = 64 * m + lane;
+    const uint64_t um = j < Nb ? (key[m] & mask) : 0u;
+    const bool eq = j < Nb && um == prefix;
+    const unsigned long long eqm = __ballot(eq);
+    const int eq_rank = eq_seen + __popcll(eqm & below);
+    const bool keep = j < Nb && (um > prefix || (eq && eq_rank < kk)) && j != jb;
+    const unsigned long long km = __ballot(keep);
+    if (keep) out[pos + __popcll(km & below)] = j;
+    pos += __popcll(km);
+    eq_seen += __popcll(eqm);
+  }
+}
+
 // Sum of a wave's values, the same butterfly on every lane (every lane ends with the
 // same bits: each step adds the same two values)
 __device__ __forceinline__ double wave_sum(double x) {
@@ -221,6 +322,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(const double* __res
   const unsigned long long below = (1ull << lane) - 1ull;
   for (int r = w; r < nr; r += 4) {
     const uint64_t* keys = s_keys + r * Nb;
+    int32_t* orow = idx + ((size_t)bh * Nb + g0 + r) * kstride;
+    if (Nb <= 64 * 32) {  // keys in registers (the branch is uniform)
+      if (Nb <= 64 * 8)
+        select_row_regs<8>(keys, Nb, ks, kstride, hist, lane, orow);
+      else if (Nb <= 64 * 16)
+        select_row_regs<16>(keys, Nb, ks, kstride, hist, lane, orow);
+      else
+        select_row_regs<32>(keys, Nb, ks, kstride, hist, lane, orow);
+      continue;
+    }
     const Threshold th = radix_threshold(keys, Nb, ks, hist, lane);
     const uint64_t prefix = th.prefix, mask = th.mask;
     const int kk = th.kk;
