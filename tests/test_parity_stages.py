@@ -268,6 +268,36 @@ def test_select_exact_fp64_near_ties():
     assert np.array_equal(g, ora)
 
 
+@pytest.mark.parametrize("Nb", [37, 300, 700, 1500, 2300])
+def test_select_stage_every_row_length(Nb):
+    """The selection stage alone, on pooled means drawn directly, at row lengths that take
+    each of its paths: the keys held in registers (up to 8, 16 or 32 per lane: rows of up
+    to 512, 1024 and 2048 blocks) and read from LDS (longer rows). Kept sets and their
+    processing order equal the oracle's, up to near-ties."""
+    rng = np.random.default_rng(40 + Nb)
+    H, d, topk = 2, 128, 0.1
+    N = 64 * Nb - 5  # a ragged last block
+    qbar = rng.standard_normal((H, Nb, d)) + rng.standard_normal((H, 1, d))
+    kbar = rng.standard_normal((H, Nb, d)) * 0.5 + rng.standard_normal((H, 1, d))
+    ks = O.ksel(topk, Nb)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tq, tk = dev(qbar), dev(np.transpose(kbar, (0, 2, 1)))  # kbart: [BH][d][Nb]
+    idx = torch.full((H, Nb, ks), -7, dtype=torch.int32, device="cuda")
+    st = S.lib().sagesla_select(tq.data_ptr(), tk.data_ptr(), 1, H, N, d, 64, topk, idx.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    g = idx.cpu().numpy()
+    for h in range(H):
+        sc = O.scores(qbar[h], kbar[h])
+        ora = np.stack([O.order_best_first(sc[i], row) for i, row in enumerate(O.select(sc, ks))])
+        near = set(mask_mismatch(g[h], ora, sc))
+        for r in range(Nb):
+            if r in near:
+                continue
+            assert np.array_equal(g[h, r], ora[r]), (h, r)
+
+
 def test_grouped_stages_and_descriptor_forward_equal_fwd():
     """sagesla_pool_select + sagesla_linear_states (or sagesla_quantize) + the complement
     and sparse stages, and sagesla_fwd_tensors, compute exactly what sagesla_fwd does."""
