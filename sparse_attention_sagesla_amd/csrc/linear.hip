@@ -162,24 +162,33 @@ struct MgSlot {
   int32_t ul[4 * 64];
 };
 
-// The 8 transposing reads of four column tiles (rows r and r + 4 of each; a0..a3 are LDS
-// byte addresses), waited for in the same block. Written out so that the compiler, which
-// cannot tell which ring slot's DMAs a read depends on, adds no wait of its own: the slot
-// is complete by the explicit wait and barrier of the step.
+// The 16 transposing reads of a step (rows r and r + 4 of each of the eight column tiles; a
+// holds their LDS byte addresses), waited for in the same block. Written out so that the
+// compiler, which cannot tell which ring slot's DMAs a read depends on, adds no wait of its
+// own: the slot is complete by the explicit wait and barrier of the step.
 typedef int v2i_ __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void mg_tr_reads(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, v2i_ (&x)[8]) {
+__device__ __forceinline__ void mg_tr_reads16(const uint32_t (&a)[8], v2i_ (&x)[16]) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %2, %9\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %4, %10\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
-      "ds_read_b64_tr_b16 %6, %11\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:1024\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7])
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3]), "=&v"(x[4]), "=&v"(x[5]), "=&v"(x[6]), "=&v"(x[7]),
+        "=&v"(x[8]), "=&v"(x[9]), "=&v"(x[10]), "=&v"(x[11]), "=&v"(x[12]), "=&v"(x[13]), "=&v"(x[14]), "=&v"(x[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
       : "memory");
 }
 
@@ -283,18 +292,18 @@ __global__ __launch_bounds__(256, 2) void linear_mask_gemm_kernel(
       bop[m] = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
     }
     const uint32_t base = lds_addr(d.st);
+    uint32_t ad[8];
 #pragma unroll
-    for (int h = 0; h < 2; h++) {
-      v2i_ x[8];
-      mg_tr_reads(base + toff[4 * h], base + toff[4 * h + 1], base + toff[4 * h + 2], base + toff[4 * h + 3], x);
+    for (int n = 0; n < 8; n++) ad[n] = base + toff[n];
+    v2i_ x[16];
+    mg_tr_reads16(ad, x);
 #pragma unroll
-      for (int n = 0; n < 4; n++) {
-        const v4i aop4 = {x[2 * n][0], x[2 * n][1], x[2 * n + 1][0], x[2 * n + 1][1]};
-        const v8bf aop = __builtin_bit_cast(v8bf, aop4);
+    for (int n = 0; n < 8; n++) {
+      const v4i aop4 = {x[2 * n][0], x[2 * n][1], x[2 * n + 1][0], x[2 * n + 1][1]};
+      const v8bf aop = __builtin_bit_cast(v8bf, aop4);
 #pragma unroll
-        for (int m = 0; m < 4; m++)
-          acc[m][4 * h + n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[m], acc[m][4 * h + n], 0, 0, 0);
-      }
+      for (int m = 0; m < 4; m++)
+        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[m], acc[m][n], 0, 0, 0);
     }
   };
   // Ring: step s lives in slot s % 4. At the top of step s this wave has issued, after
