@@ -83,13 +83,13 @@ __global__ __launch_bounds__(256) void pool_kernel(
   const size_t base = ((size_t)bh * N + (size_t)i * kBlk) * kD;
 
   uint4 qa[4], ka[4], va[4];
+  if constexpr (kFromProj) {
 #pragma unroll
-  for (int m = 0; m < 4; m++) {
-    const int row = rg + 16 * m;
-    qa[m] = ka[m] = va[m] = make_uint4(0, 0, 0, 0);
-    if (kFromProj && row < n) {
-      const size_t off = base + (size_t)row * kD + ch * 8;
-      if (kFromProj) {
+    for (int m = 0; m < 4; m++) {
+      const int row = rg + 16 * m;
+      qa[m] = ka[m] = va[m] = make_uint4(0, 0, 0, 0);
+      if (row < n) {
+        const size_t off = base + (size_t)row * kD + ch * 8;
         const int b = bh / ps.H, h = bh % ps.H, tok = i * kBlk + row, D = ps.H * kD;
         const uint16_t* src = ps.qkv + ((size_t)b * N + tok) * 3 * D + h * kD + ch * 8;
         const size_t rr = (size_t)b * N + tok, BN = (size_t)(gridDim.x / Nb / ps.H) * N;
@@ -101,8 +101,7 @@ __global__ __launch_bounds__(256) void pool_kernel(
         *(uint4*)(ps.v + off) = va[m];
       }
     }
-  }
-  if (!kFromProj) {
+  } else {
     // one head's rows through buffer resources: 32-bit lane offsets, and rows past N
     // (past the resource's end) read zero
     const size_t h0 = scalar_off((size_t)bh * N * kD);
@@ -245,6 +244,8 @@ __global__ __launch_bounds__(256) void head_stats_kernel(const double* __restric
 
 hipError_t launch_pool(const void* q, const void* k, const void* v, int BH, int N, int Nb, void* qbar,
                        void* kbart, void* ksum, void* vamax_blk, void* q8, void* sq, hipStream_t st) {
+  // one head's rows are addressed by 32-bit buffer offsets
+  if ((uint64_t)N * kD * 2 > UINT32_MAX) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pool_kernel<false>, dim3(BH * Nb), dim3(256), 0, st, (const uint16_t*)q,
                      (const uint16_t*)k, (const uint16_t*)v, ProjSrc{}, N, Nb, (double*)qbar, (double*)kbart,
                      (double*)ksum, (float*)vamax_blk, (int8_t*)q8, (float*)sq);

@@ -33,6 +33,43 @@ struct Threshold {
   int kk;
 };
 
+// The second half of a radix pass, from the wave's 256-bin histogram of the keys still
+// matching th: the bin (digits at shift) that holds the kk-th largest, counted from the top
+// bin down. Returns whether that whole bin is kept (the selection is then complete).
+__device__ __forceinline__ bool radix_pick(const uint32_t* hist, int lane, int shift, Threshold& th) {
+  // lane owns bins 4*lane .. 4*lane+3; suffix counts from the top bin down
+  const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const int loc = h0 + h1 + h2 + h3;
+  int suf = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_down(suf, o);
+    if (lane + o < 64) suf += y;
+  }
+  int above = suf - loc;
+  const int hs[4] = {h0, h1, h2, h3};
+  int sel_bin = -1, sel_k = 0, sel_n = 0;
+#pragma unroll
+  for (int b = 3; b >= 0; b--) {
+    if (above < th.kk && above + hs[b] >= th.kk) {
+      sel_bin = 4 * lane + b;
+      sel_k = th.kk - above;
+      sel_n = hs[b];
+    }
+    above += hs[b];
+  }
+  const unsigned long long who = __ballot(sel_bin >= 0);
+  const int src = __ffsll((long long)who) - 1;
+  sel_bin = __shfl(sel_bin, src);
+  sel_k = __shfl(sel_k, src);
+  sel_n = __shfl(sel_n, src);
+  th.prefix |= (uint64_t)sel_bin << shift;
+  th.mask |= (uint64_t)255u << shift;
+  th.kk = sel_k;
+  __builtin_amdgcn_wave_barrier();
+  return sel_n == sel_k;  // every key of the bin is kept
+}
+
 // Radix select of the k-th largest key of a row (one wave, hist: its 256-bin LDS
 // histogram), 8 bits per pass from the top. After a pass the keys whose selected bits
 // exceed the prefix are kept, and kk more are wanted from those equal to it; when that
@@ -51,37 +88,7 @@ __device__ Threshold radix_threshold(const uint64_t* keys, int Nb, int k, uint32
       if ((u & th.mask) == th.prefix) atomicAdd(&hist[(uint32_t)(u >> shift) & 255u], 1u);
     }
     __builtin_amdgcn_wave_barrier();
-    // lane owns bins 4*lane .. 4*lane+3; suffix counts from the top bin down
-    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const int loc = h0 + h1 + h2 + h3;
-    int suf = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_down(suf, o);
-      if (lane + o < 64) suf += y;
-    }
-    int above = suf - loc;
-    const int hs[4] = {h0, h1, h2, h3};
-    int sel_bin = -1, sel_k = 0, sel_n = 0;
-#pragma unroll
-    for (int b = 3; b >= 0; b--) {
-      if (above < th.kk && above + hs[b] >= th.kk) {
-        sel_bin = 4 * lane + b;
-        sel_k = th.kk - above;
-        sel_n = hs[b];
-      }
-      above += hs[b];
-    }
-    const unsigned long long who = __ballot(sel_bin >= 0);
-    const int src = __ffsll((long long)who) - 1;
-    sel_bin = __shfl(sel_bin, src);
-    sel_k = __shfl(sel_k, src);
-    sel_n = __shfl(sel_n, src);
-    th.prefix |= (uint64_t)sel_bin << shift;
-    th.mask |= (uint64_t)255u << shift;
-    th.kk = sel_k;
-    __builtin_amdgcn_wave_barrier();
-    if (sel_n == sel_k) break;  // every key of the bin is kept
+    if (radix_pick(hist, lane, shift, th)) break;
   }
   return th;
 }
@@ -103,36 +110,7 @@ __device__ Threshold radix_threshold_regs(const uint64_t (&key)[M], int Nb, int 
         atomicAdd(&hist[(uint32_t)(key[m] >> shift) & 255u], 1u);
     }
     __builtin_amdgcn_wave_barrier();
-    const int h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
-    const int loc = h0 + h1 + h2 + h3;
-    int suf = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_down(suf, o);
-      if (lane + o < 64) suf += y;
-    }
-    int above = suf - loc;
-    const int hs[4] = {h0, h1, h2, h3};
-    int sel_bin = -1, sel_k = 0, sel_n = 0;
-#pragma unroll
-    for (int b = 3; b >= 0; b--) {
-      if (above < th.kk && above + hs[b] >= th.kk) {
-        sel_bin = 4 * lane + b;
-        sel_k = th.kk - above;
-        sel_n = hs[b];
-      }
-      above += hs[b];
-    }
-    const unsigned long long who = __ballot(sel_bin >= 0);
-    const int src = __ffsll((long long)who) - 1;
-    sel_bin = __shfl(sel_bin, src);
-    sel_k = __shfl(sel_k, src);
-    sel_n = __shfl(sel_n, src);
-    th.prefix |= (uint64_t)sel_bin << shift;
-    th.mask |= (uint64_t)255u << shift;
-    th.kk = sel_k;
-    __builtin_amdgcn_wave_barrier();
-    if (sel_n == sel_k) break;
+    if (radix_pick(hist, lane, shift, th)) break;
   }
   return th;
 }
