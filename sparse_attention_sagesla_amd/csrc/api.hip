@@ -139,6 +139,42 @@ sagesla_status check_device() {
 
 sagesla_status from_hip(hipError_t e) { return e == hipSuccess ? SAGESLA_OK : SAGESLA_ERR_HIP; }
 
+// A second stream per device on which the forward runs the key-block selection beside the
+// K/V quantization and the linear-state totals: both need only the pooling and the head
+// statistics, and the selection is bound by fp64 and LDS work where the quantization is
+// bound by HBM. The stream and its two events are created on first use (not while the
+// caller's stream is being captured) and kept until the process ends; the stream has the
+// default priority. fork_mu is held from the fork to the join, so that concurrent callers
+// never interleave their uses of the two events.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool ready = false, failed = false;
+};
+static std::mutex side_mu, fork_mu;
+static SideStream side_streams[64];
+
+static SideStream* side_stream(hipStream_t caller) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(side_mu);
+  SideStream& ss = side_streams[dev];
+  if (ss.ready) return &ss;
+  if (ss.failed) return nullptr;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
+  if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+    ss.failed = true;  // the forward then runs on the caller's stream alone
+    return nullptr;
+  }
+  ss.ready = true;
+  return &ss;
+}
+
+
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // keys: the score-key region of the adaptive forward
@@ -234,7 +270,7 @@ sagesla_status sagesla_workspace_size(int B, int H, int N, int d, int block, dou
 
 static sagesla_status run_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
                               int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
-                              sagesla_stream_t stream, bool pooled);
+                              sagesla_stream_t stream, bool pooled, bool fork = true);
 
 sagesla_status sagesla_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
                            int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
@@ -273,7 +309,7 @@ sagesla_status sagesla_prepare(const void* qkv, const void* gq, const void* gk, 
 
 static sagesla_status run_fwd(const void* q, const void* k, const void* v, const void* proj, int B, int H, int N,
                               int d, double topk, int block, void* out, void* workspace, size_t workspace_bytes,
-                              sagesla_stream_t stream, bool pooled) {
+                              sagesla_stream_t stream, bool pooled, bool fork) {
   Geom gm;
   sagesla_status s = check_sizes(B, H, N, d, block, &gm);
   if (s != SAGESLA_OK) return s;
@@ -297,17 +333,31 @@ static sagesla_status run_fwd(const void* q, const void* k, const void* v, const
   if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb,
                              P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
     return from_hip(e);
-  if ((e = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_IDX),
-                         st)) != hipSuccess)
-    return from_hip(e);
-  if ((e = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb,
-                           P(SAGESLA_WS_K8), P(SAGESLA_WS_SK), P(SAGESLA_WS_V8),
-                           linear ? P(SAGESLA_WS_HS) : nullptr, linear ? P(SAGESLA_WS_HPART) : nullptr,
-                           st)) != hipSuccess)
-    return from_hip(e);
+  // the selection on the side stream when there is one, beside the quantization and the
+  // totals; every later stage waits for both
+  SideStream* side = fork ? side_stream(st) : nullptr;
+  std::unique_lock<std::mutex> fork_lk(fork_mu, std::defer_lock);
+  if (side) {
+    fork_lk.lock();
+    if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return SAGESLA_ERR_HIP;
+  }
+  hipStream_t sel_st = side ? side->s : st;
+  hipError_t es = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_IDX),
+                                sel_st);
+  if (es == hipSuccess)
+    es = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_K8),
+                         P(SAGESLA_WS_SK), P(SAGESLA_WS_V8), linear ? P(SAGESLA_WS_HS) : nullptr,
+                         linear ? P(SAGESLA_WS_HPART) : nullptr, st);
+  if (es == hipSuccess && linear)
+    es = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st);
+  if (side) {  // the join, also after a failed launch: the caller's stream never runs ahead
+    if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
+      return SAGESLA_ERR_HIP;
+    fork_lk.unlock();
+  }
+  if (es != hipSuccess) return from_hip(es);
   if (linear) {
-    if ((e = launch_linear_total(P(SAGESLA_WS_HPART), gm.BH, gm.Nb, P(SAGESLA_WS_HTOT), st)) != hipSuccess)
-      return from_hip(e);
     if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj, gm.BH,
                                       gm.N, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
                                       P(SAGESLA_WS_UCOUNT), P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
@@ -399,7 +449,7 @@ sagesla_status sagesla_fwd_noalloc(const void* q, const void* k, const void* v, 
   void* ws = nullptr;
   if ((s = scratch_address(&ws)) != SAGESLA_OK) return s;
   return run_fwd(q, k, v, proj, B, H, N, d, topk, block, out, ws, (size_t)SAGESLA_NOALLOC_SCRATCH_BYTES, stream,
-                 false);
+                 false, false);
 }
 
 // ---------------------------------------------------------------- content-adaptive count
