@@ -23,6 +23,9 @@ hipError_t launch_quant_kv(const void*, const void*, const void*, const void*, i
 hipError_t launch_linear_total(const void*, int, int, void*, hipStream_t);
 hipError_t launch_linear_complement(const void*, const void*, const void*, const void*, const void*, int, int,
                                     int, int, void*, void*, void*, void*, void*, hipStream_t);
+hipError_t launch_linear_union(const void*, int, int, int, void*, void*, void*, hipStream_t);
+hipError_t launch_linear_masked(const void*, const void*, const void*, const void*, int, int, int, int, const void*,
+                                const void*, const void*, void*, void*, hipStream_t);
 hipError_t launch_linear_complement(const void*, const void*, const void*, int, const void*, const void*, const void*,
                                     int, int, int, int, void*, void*, void*, void*, void*, hipStream_t);
 hipError_t launch_sparse_attn(const void*, const void*, const void*, const void*, const void*, const void*,
@@ -333,8 +336,9 @@ static sagesla_status run_fwd(const void* q, const void* k, const void* v, const
   if ((e = launch_head_stats(P(SAGESLA_WS_KSUM), P(SAGESLA_WS_VAMAXB), gm.BH, gm.N, gm.Nb,
                              P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), st)) != hipSuccess)
     return from_hip(e);
-  // the selection on the side stream when there is one, beside the quantization and the
-  // totals; every later stage waits for both
+  // the selection (and the union of the kept lists, which needs nothing else) on the side
+  // stream when there is one, beside the quantization and the totals; every later stage
+  // waits for both
   SideStream* side = fork ? side_stream(st) : nullptr;
   std::unique_lock<std::mutex> fork_lk(fork_mu, std::defer_lock);
   if (side) {
@@ -345,6 +349,9 @@ static sagesla_status run_fwd(const void* q, const void* k, const void* v, const
   hipStream_t sel_st = side ? side->s : st;
   hipError_t es = launch_select(P(SAGESLA_WS_QBAR), P(SAGESLA_WS_KBART), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_IDX),
                                 sel_st);
+  if (es == hipSuccess && linear)
+    es = launch_linear_union(P(SAGESLA_WS_IDX), gm.BH, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
+                             P(SAGESLA_WS_UCOUNT), sel_st);
   if (es == hipSuccess)
     es = launch_quant_kv(k, v, P(SAGESLA_WS_KMEAN), P(SAGESLA_WS_VAMAX), gm.BH, gm.N, gm.Nb, P(SAGESLA_WS_K8),
                          P(SAGESLA_WS_SK), P(SAGESLA_WS_V8), linear ? P(SAGESLA_WS_HS) : nullptr,
@@ -358,9 +365,9 @@ static sagesla_status run_fwd(const void* q, const void* k, const void* v, const
   }
   if (es != hipSuccess) return from_hip(es);
   if (linear) {
-    if ((e = launch_linear_complement(q, P(SAGESLA_WS_IDX), P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj, gm.BH,
-                                      gm.N, gm.Nb, gm.ksel, P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK),
-                                      P(SAGESLA_WS_UCOUNT), P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
+    if ((e = launch_linear_masked(q, P(SAGESLA_WS_HS), P(SAGESLA_WS_HTOT), proj, gm.BH, gm.N, gm.Nb, gm.ksel,
+                                  P(SAGESLA_WS_ULIST), P(SAGESLA_WS_UMASK), P(SAGESLA_WS_UCOUNT),
+                                  P(SAGESLA_WS_HC), P(SAGESLA_WS_Y), st)) != hipSuccess)
       return from_hip(e);
   }
   e = launch_sparse_attn(P(SAGESLA_WS_Q8), P(SAGESLA_WS_SQ), P(SAGESLA_WS_K8), P(SAGESLA_WS_SK),
