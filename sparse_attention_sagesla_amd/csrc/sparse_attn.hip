@@ -151,11 +151,15 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
   // The partial last block: keys at or past nlast take no part. Their scores are set to
   // 0 before the maximum, and their FP8 weights to zero after the exponentials.
   if (partial) {
+    // key_of_slot(g, ...) >= nlast against the lane's bound, formed here: hoisted out of
+    // the loop, the 32 comparisons would hold 64 scalar registers for the whole kernel
+    int thr = nlast - 4 * g;
+    asm volatile("" : "+v"(thr));
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
       for (int v = 0; v < 16; v++)
-        if (key_of_slot(g, tt, v) >= nlast) S[tt][v] = 0;
+        if (key_of_slot(0, tt, v) >= thr) S[tt][v] = 0;
   }
   int mx = 0;
 #pragma unroll
@@ -170,7 +174,10 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
   // float(S_max) = F_max - 1.5*2^23 exactly; the reference is its product with a rounded
   // up to an integer, never below the previous one
   const float mold = st.m;
-  const float mn = fmaxf(mold, __builtin_ceilf((__int_as_float(mx) - kMagicF) * a));
+  // (a plain v_max_f32: both operands are canonical, so fmaxf's quieting of mold, a loop
+  // value the compiler cannot prove canonical, would only cost an instruction)
+  float mn;
+  asm("v_max_f32 %0, %1, %2" : "=v"(mn) : "v"(mold), "v"(__builtin_ceilf((__int_as_float(mx) - kMagicF) * a)));
   const bool moved = __builtin_amdgcn_ballot_w64(mn > mold) != 0;
   st.m = mn;
   // exponentials and FP8 packing, 4 scores per group. For the row maximum the fused
@@ -199,6 +206,8 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
 #undef SAGESLA_EXP
   slot<12, PV>(pp, st, pprev, lsel, Sn, q, magic);
   if (partial) {
+    int thr = nlast - 4 * g;
+    asm volatile("" : "+v"(thr));
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
@@ -206,7 +215,7 @@ __device__ __forceinline__ v8i block_step(v16i (&S)[2], RowAcc& st, float a, flo
         uint32_t keep = 0u;
 #pragma unroll
         for (int e = 0; e < 4; e++)
-          if (key_of_slot(g, tt, 4 * v4 + e) < nlast) keep |= 0xFFu << (8 * e);
+          if (key_of_slot(0, tt, 4 * v4 + e) < thr) keep |= 0xFFu << (8 * e);
         pb[4 * tt + v4] &= (int)keep;
       }
   }
