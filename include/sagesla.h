@@ -135,10 +135,11 @@ sagesla_status sagesla_workspace_layout(int B, int H, int N, int d, int block, d
  * Full forward: out = SageSLA(q, k, v) (+ linear branch through proj when proj != NULL
  * and ksel < Nb). workspace: device memory of at least sagesla_workspace_size bytes;
  * its contents on return are the SAGESLA_WS_* intermediates of this call.
- * Streams: the whole call is ordered on `stream`. Inside it, the key-block selection runs
- * on a second stream the library owns per device (default priority, created by the first
- * call on that device outside a graph capture, kept until the process ends), forked from
- * `stream` after the head statistics and joined back before the linear complement. The
+ * Streams: the whole call is ordered on `stream`. Inside it, the key-block selection (and,
+ * with the linear branch, the union of the kept lists) runs on a second stream the library
+ * owns per device (default priority, created by the first call on that device outside a
+ * graph capture, kept until the process ends), forked from `stream` after the head
+ * statistics and joined back before the masked complement product. The
  * call may be captured into a HIP graph (a first call on a device that is itself being
  * captured runs on `stream` alone), and calls from several host threads are safe.
  * sagesla_fwd_prepared and sagesla_fwd_tensors do the same; sagesla_fwd_noalloc runs on

@@ -142,10 +142,10 @@ sagesla_status check_device() {
 
 sagesla_status from_hip(hipError_t e) { return e == hipSuccess ? SAGESLA_OK : SAGESLA_ERR_HIP; }
 
-// A second stream per device on which the forward runs the key-block selection beside the
-// K/V quantization and the linear-state totals: both need only the pooling and the head
-// statistics, and the selection is bound by fp64 and LDS work where the quantization is
-// bound by HBM. The stream and its two events are created on first use (not while the
+// A second stream per device on which the forward runs the key-block selection (and the
+// union of the kept lists) beside the K/V quantization and the linear-state totals: both
+// need only the pooling and the head statistics, and the selection is bound by fp64 and
+// LDS work where the quantization is bound by HBM. The stream and its two events are created on first use (not while the
 // caller's stream is being captured) and kept until the process ends; the stream has the
 // default priority. fork_mu is held from the fork to the join, so that concurrent callers
 // never interleave their uses of the two events.
