@@ -176,8 +176,6 @@ static SideStream* side_stream(hipStream_t caller) {
   return &ss;
 }
 
-
-
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // keys: the score-key region of the adaptive forward
