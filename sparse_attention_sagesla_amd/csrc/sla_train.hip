@@ -741,13 +741,14 @@ __device__ __forceinline__ v8bf lds_col8(const uint16_t (*tile)[kSp], int base, 
 
 // Per (head, query block), lanes = query rows (2 waves x 32). Adds dq_l into dq and writes
 // phi(q), du, O_l (bf16, row-major) and ds (fp32) for the state gradients and dW.
-__global__ __launch_bounds__(128) void sla_lin_bwd_q_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ dout,
-                                                            const uint16_t* __restrict__ hc,
-                                                            const uint16_t* __restrict__ proj, int BH, int N, int Nb,
-                                                            int per_xcd, float* __restrict__ dq,
-                                                            uint16_t* __restrict__ phq_o, uint16_t* __restrict__ du_o,
-                                                            float* __restrict__ ds_o, uint16_t* __restrict__ ol_o) {
+// Two waves per SIMD (here and in sla_lin_bwd_k_kernel): left alone, the compiler adds
+// accumulation registers beyond 256 per lane and the kernels run one wave per SIMD, 1.0 ms
+// more for the two together at the Wan2.1-14B 720p shape.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sla_lin_bwd_q_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, const uint16_t* __restrict__ hc,
+    const uint16_t* __restrict__ proj, int BH, int N, int Nb, int per_xcd, float* __restrict__ dq,
+    uint16_t* __restrict__ phq_o, uint16_t* __restrict__ du_o, float* __restrict__ ds_o,
+    uint16_t* __restrict__ ol_o) {
   __shared__ __attribute__((aligned(16))) uint16_t sS[129][kSp];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
@@ -1019,10 +1020,9 @@ __global__ __launch_bounds__(256) void sla_union_t_kernel(const uint32_t* __rest
 }
 
 // Per (head, key block), lanes = keys (2 waves x 32): adds dk_l and dv_l from R_j = [dH_j ; dz_j].
-__global__ __launch_bounds__(128) void sla_lin_bwd_k_kernel(const uint16_t* __restrict__ k,
-                                                            const uint16_t* __restrict__ v,
-                                                            const uint16_t* __restrict__ rj, int BH, int N, int Nb,
-                                                            int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) void sla_lin_bwd_k_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const uint16_t* __restrict__ rj, int BH, int N,
+    int Nb, int per_xcd, float* __restrict__ dk, float* __restrict__ dv) {
   __shared__ __attribute__((aligned(16))) uint16_t sR[129][kSp];
   const int tile = xcd_tile(blockIdx.x, per_xcd);
   if (tile >= BH * Nb) return;
