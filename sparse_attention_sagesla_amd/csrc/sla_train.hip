@@ -925,16 +925,21 @@ __global__ __launch_bounds__(256) void sla_lin_dhc_kernel(const uint16_t* __rest
         }
         acc[4] = mfma(pack8(dv8), b, acc[4]);
       }
-    // D[c][a]: lane = a (32w + r), registers = c rows 32ct + 8(v/4) + 4g + v%4
+    // D[c][a]: lane = a (32w + r), registers = c rows 32ct + 8(v/4) + 4g + v%4: four
+    // consecutive c per 8-byte store
     uint16_t* R = rs + ((size_t)bh * Nb + i) * kStateElems;
     const int a = 32 * w + r;
 #pragma unroll
     for (int ct = 0; ct < 4; ct++)
 #pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int c = 32 * ct + 8 * (v >> 2) + 4 * g + (v & 3);
-        R[a * kD + c] = f32_to_bf16(acc[ct][v]);
-        cs[ct][v] += acc[ct][v];
+      for (int v4 = 0; v4 < 4; v4++) {
+        const int c = 32 * ct + 8 * v4 + 4 * g;
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(acc[ct][4 * v4]) | ((uint32_t)f32_to_bf16(acc[ct][4 * v4 + 1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(acc[ct][4 * v4 + 2]) | ((uint32_t)f32_to_bf16(acc[ct][4 * v4 + 3]) << 16);
+        *(uint2*)(R + a * kD + c) = pk;
+#pragma unroll
+        for (int e = 0; e < 4; e++) cs[ct][4 * v4 + e] += acc[ct][4 * v4 + e];
       }
     if (g == 0) R[kD * kD + a] = f32_to_bf16(acc[4][0]);
     cs[4][0] += acc[4][0];
@@ -944,7 +949,9 @@ __global__ __launch_bounds__(256) void sla_lin_dhc_kernel(const uint16_t* __rest
 #pragma unroll
   for (int ct = 0; ct < 4; ct++)
 #pragma unroll
-    for (int v = 0; v < 16; v++) P[a * kD + 32 * ct + 8 * (v >> 2) + 4 * g + (v & 3)] = cs[ct][v];
+    for (int v4 = 0; v4 < 4; v4++)
+      *(float4*)(P + a * kD + 32 * ct + 8 * v4 + 4 * g) =
+          make_float4(cs[ct][4 * v4], cs[ct][4 * v4 + 1], cs[ct][4 * v4 + 2], cs[ct][4 * v4 + 3]);
   if (g == 0) P[kD * kD + a] = cs[4][0];
 }
 
