@@ -1126,7 +1126,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 // dW partial sums: workgroup p adds O_l^T dO over its share of the (head, block) pairs;
 // wave w owns rows c = 32w .. +31 of dW. Then one pass adds the partials.
-constexpr int kDwParts = 512;
+constexpr int kDwParts = 1024;
 
 __global__ __launch_bounds__(256) void sla_dw_partial_kernel(const uint16_t* __restrict__ olt,
                                                              const uint16_t* __restrict__ dot_, int nblocks,
